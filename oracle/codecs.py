@@ -1,0 +1,103 @@
+"""Exact decoding (and, for the cache-store helpers, encoding) of the stored formats.
+
+TEST INFRASTRUCTURE (see the package header).
+
+Formats:
+* bf16: the upper 16 bits of an IEEE binary32; decoding shifts the bits up by 16.
+* fp8-e4m3, OCP "fn" variant: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+  exponent field 0 encodes subnormals m * 2^-9; S.1111.111 is NaN; there is no infinity;
+  the largest finite magnitude is 448.
+* Per-token fp8 quantization of indexer keys (the quantized indexer path of "Day0
+  Adaptation and Performance Optimization for Novel Long-Sequence Reasoning Models",
+  section 3, with the per-token fp32 scale of this project's quantized workloads): the scale
+  is the token's largest magnitude divided by 448 in fp32 (an all-zero token gets 1), the
+  code is the fp32 quotient value/scale rounded to the nearest e4m3 value, ties to the even
+  code, magnitudes above 448 saturating to 448.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bits -> float64 (exact)."""
+    u32 = bits.astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u32.view(np.float32).astype(np.float64)
+
+
+def fp8_e4m3_table() -> np.ndarray:
+    """float64 value of each of the 256 e4m3fn codes, built from the format definition."""
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sign = -1.0 if (c >> 7) & 1 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * m * 2.0 ** -9
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_FP8_TABLE = fp8_e4m3_table()
+
+
+def decode_fp8_e4m3(codes: np.ndarray) -> np.ndarray:
+    """uint8 e4m3fn codes -> float64 (exact)."""
+    return _FP8_TABLE[codes.astype(np.intp)]
+
+
+def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored tensor -> float64, dtype in {f32, bf16, fp8} (fp8 without its scale)."""
+    if dtype == "f32":
+        return arr.astype(np.float64)
+    if dtype == "bf16":
+        return decode_bf16(arr)
+    if dtype == "fp8":
+        return decode_fp8_e4m3(arr)
+    raise ValueError(dtype)
+
+
+def encode_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest, ties to even (NaN -> quiet NaN)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) & np.uint64(0xFFFF)
+    out = r.astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    out[nan] = np.uint16(0x7FC0) | (((u[nan] >> np.uint64(16)) & np.uint64(0x8000)).astype(np.uint16))
+    return out
+
+
+_POS_CODES = np.arange(0, 127, dtype=np.int64)          # +0 ... +448 (0x7E)
+_POS_VALS = _FP8_TABLE[:127]                            # strictly increasing
+
+
+def encode_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """float64/float32 -> e4m3fn codes: nearest value, ties to the even code, saturating
+    magnitudes above 448 to 448; NaN -> 0x7F; the sign of zero is kept."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.searchsorted(_POS_VALS, a, side="left")     # first value >= a
+    hi = np.clip(hi, 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_hi = _POS_VALS[hi] - a
+    d_lo = a - _POS_VALS[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
+    code = np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo])
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_fp8_per_token(x: np.ndarray):
+    """float32 [n, D] -> (uint8 codes [n, D], float32 scales [n])."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    scale = np.divide(amax, np.float32(448.0), dtype=np.float32)
+    scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
+    quot = np.divide(x, scale[:, None], dtype=np.float32)
+    return encode_fp8_e4m3(quot), scale
