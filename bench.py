@@ -1,0 +1,282 @@
+"""Throughput of the DSA hot path (lightning indexer + Top-K + Sparse Flash Attention) on one
+MI355X.
+
+One step = dsa_indexer_topk then dsa_sparse_attn over one batch of decode queries, both on
+the current stream, inputs resident in HBM.  Default workload: quantized decode at 128K
+context (batch 8, per-sequence context uniform in [64K, 128K], fp8-e4m3 index keys with
+per-token scales, bf16 queries, indexer 64 heads x 128, Top-K 2048, SFA 128 heads over the
+576/512 latent cache in 64-token pages scattered by a random block table).
+
+The working set of one step (~125 MB) fits the 256 MB Infinity Cache, so the timed loop
+rotates over `--copies` independent device copies of all pools, tables and queries: a copy
+is reused only after ~1 GB of other copies has been touched.
+
+Prints one JSON line (see the keys below), including the roofline of the dominant kernel
+(the indexer, HBM-bound: algorithmic bytes per launch / its mean launch time from HIP events
+recorded around it inside the timed region) and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 4]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/sec (indexer+TopK+SFA) at 128K ctx; % peak HBM BW / MFMA"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "indexer_counters.json")
+
+
+def indexer_bytes(spec, V):
+    """Algorithmic bytes one indexer launch must move: every visible key (+ its fp8 scale),
+    one block-table entry per 64-token page, the queries and head weights, the index list."""
+    ek = ELEM[spec.k_dtype]
+    sk = 4 if spec.k_dtype == "fp8" else 0
+    eq = ELEM[spec.q_dtype]
+    b = 0
+    for v in V:
+        v = int(v)
+        b += v * (spec.idx_dim * ek + sk)
+        if spec.block_size:
+            b += 4 * math.ceil(v / spec.block_size)
+        b += spec.idx_heads * (spec.idx_dim * eq + 4)
+        b += 4 * spec.top_k
+    return b
+
+
+def sfa_bytes(spec, V):
+    """Algorithmic bytes of one SFA launch: the index list, the selected latent rows, the
+    queries and the outputs."""
+    e = ELEM[spec.kv_dtype]
+    b = 0
+    for v in V:
+        k_eff = min(spec.top_k, int(v))
+        b += 4 * spec.top_k + k_eff * spec.d_qk * e
+        b += spec.sfa_heads * (spec.d_qk * e + spec.d_v * e)
+    return b
+
+
+def sfa_flops(spec, V):
+    return sum(2 * spec.sfa_heads * min(spec.top_k, int(v)) * (spec.d_qk + spec.d_v) for v in V)
+
+
+def indexer_flops(spec, V):
+    return sum(2 * spec.idx_heads * spec.idx_dim * int(v) for v in V)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("indexer.hip", "dsa_common.hpp", "dsa_internal.hpp"):
+        with open(os.path.join(ROOT, "sparse_indexed_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per indexer launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    if c.get("source_digest") != source_digest() or c.get("workload") is None:
+        return None, c.get("workload")
+    return c.get("hbm_bytes_per_launch"), c.get("workload")
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """The oracle (NumPy float64, never tuned) on whole queries of the same workload until
+    about budget_s of CPU time has passed; queries/s."""
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = cores
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            threads = max(int(i.get("num_threads", 1)) for i in info)
+    except Exception:
+        pass
+    T = inp.spec.num_queries
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        t = done % T
+        r = oracle.indexer_topk_query(inp, t)
+        oracle.sfa_query(inp, t, r.idx)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s and done >= 1:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} whole queries (indexer + Top-K + SFA) of the same workload, "
+                      f"{el:.1f} s wall, NumPy float64 with {threads} BLAS threads on "
+                      f"{cores} available cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4, help="workload number (1-5)")
+    ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sharding across GPUs is described in DESIGN.md, not implemented).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_indexed_attention_amd as dsa
+    from synth import make_inputs, workload
+    from synth.device import to_device
+
+    dsa.load()
+    torch.cuda.set_device(0)
+    spec = workload(args.config)
+    seed = args.seed or args.config
+    print(f"bench: generating {spec.name} (seed {seed})", file=sys.stderr, flush=True)
+    inp = make_inputs(spec, seed=seed)
+    V = [int(v) for v in inp.q_visible]
+    T = spec.num_queries
+
+    step_bytes_idx = indexer_bytes(spec, V)
+    step_bytes_sfa = sfa_bytes(spec, V)
+    per_copy = step_bytes_idx + step_bytes_sfa
+    copies = args.copies or max(3, min(12, math.ceil(1.0e9 / per_copy) + 1))
+    if spec.name.startswith("prefill"):
+        copies = args.copies or 1
+    base = to_device(inp, "cuda")
+    devs = [base]
+    for _ in range(copies - 1):
+        c = to_device(inp, "cuda") if False else None
+        import copy as _copy
+        c = _copy.copy(base)
+        for f in ("q_idx", "w", "k_pool", "k_scale", "q_sfa", "kv_pool", "block_table", "q_seq",
+                  "q_visible"):
+            v = getattr(base, f)
+            setattr(c, f, None if v is None else v.clone())
+        devs.append(c)
+    layouts = [dsa.make_layout(d.block_table, d.block_size, pool_rows=d.pool_rows)
+               if d.block_table is not None else
+               dsa.make_layout(None, 0, seq_stride=d.seq_stride, num_seqs=spec.num_seqs,
+                               pool_rows=d.pool_rows) for d in devs]
+    K = spec.top_k
+    ws_i = dsa.zeroed_workspace(dsa.indexer_workspace_bytes(T, base.max_visible, K), "cuda")
+    ws_s = dsa.zeroed_workspace(dsa.sfa_workspace_bytes(T, spec.sfa_heads, K, spec.d_v), "cuda")
+    outs = []
+    for d in devs:
+        idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        o = torch.empty((T, spec.sfa_heads, spec.d_v), dtype=d.q_sfa.dtype, device="cuda")
+        outs.append((idx, o))
+
+    def step(i, ev=None):
+        d, lay = devs[i % copies], layouts[i % copies]
+        idx, o = outs[i % copies]
+        if ev is not None:
+            ev[0].record()
+        dsa.indexer_topk(d.q_idx, d.w, d.k_pool, d.k_scale, lay, d.q_seq, d.q_visible,
+                         d.max_visible, K, out_idx=idx, want_score=False, workspace=ws_i)
+        if ev is not None:
+            ev[1].record()
+        dsa.sparse_attn(d.q_sfa, d.kv_pool, idx, lay, d.q_seq, spec.softmax_scale, spec.d_v,
+                        out=o, want_lse=False, workspace=ws_s)
+        if ev is not None:
+            ev[2].record()
+
+    print(f"bench: {copies} rotating copies, warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    idx_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    sfa_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = wall * 1e3 / args.steps
+    qps = T * args.steps / wall
+    idx_mean = float(np.mean(idx_ms))
+    sfa_mean = float(np.mean(sfa_ms))
+    achieved = step_bytes_idx / (idx_mean * 1e-3) / 1e9
+    traffic, prof_wl = counter_traffic()
+    print(f"bench: step {step_ms * 1e3:.1f} us (indexer {idx_mean * 1e3:.1f} us median "
+          f"{np.median(idx_ms) * 1e3:.1f}, SFA {sfa_mean * 1e3:.1f} us); indexer {achieved:.0f} GB/s; "
+          f"SFA {step_bytes_sfa / (sfa_mean * 1e-3) / 1e9:.0f} GB/s, "
+          f"{sfa_flops(spec, V) / (sfa_mean * 1e-3) / 1e12:.1f} TFLOP/s; whole step "
+          f"{(step_bytes_idx + step_bytes_sfa) / (step_ms * 1e-3) / 1e9:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": qps,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name,
+            "queries_per_step": T,
+            "context": {"min": min(V), "max": max(V), "mean": float(np.mean(V))},
+            "top_k": K,
+            "indexer": f"{spec.idx_heads}x{spec.idx_dim} q {spec.q_dtype} keys {spec.k_dtype}",
+            "sfa": f"{spec.sfa_heads} heads {spec.d_qk}/{spec.d_v} {spec.kv_dtype}",
+            "block_size": spec.block_size,
+            "rotating_copies": copies,
+            "step_algorithmic_bytes": step_bytes_idx + step_bytes_sfa,
+            "step_hbm_frac": (step_bytes_idx + step_bytes_sfa) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "sfa_mean_us": sfa_mean * 1e3,
+            "indexer_mean_us": idx_mean * 1e3,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "indexer_topk_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+// C ABI of the DSA hot path: host-side validation, launch planning and dispatch.
+// Nothing here reads device memory or synchronizes; errors are returned before any launch.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.hpp"
+
+namespace {
+
+using namespace dsa;
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return l;
+}
+
+dsa_status check_layout(const dsa_layout* L, const dsa_queries* Q, bool need_visible) {
+  if (!L || !Q) return DSA_ERR_NULL;
+  if (!Q->q_seq || (need_visible && !Q->q_visible)) return DSA_ERR_NULL;
+  if (Q->num_queries < 1 || Q->num_queries > 65535) return DSA_ERR_SHAPE;
+  if (L->num_seqs < 1) return DSA_ERR_SHAPE;
+  if (need_visible && (Q->max_visible < 1 || Q->max_visible > DSA_MAX_CONTEXT))
+    return DSA_ERR_SHAPE;
+  if (misaligned(L->block_table) || misaligned(Q->q_seq) || misaligned(Q->q_visible))
+    return DSA_ERR_ALIGN;
+  if (L->block_table) {
+    if (!is_pow2(L->block_size) || L->block_size > 65536) return DSA_ERR_SHAPE;
+    if (L->max_blocks_per_seq < 1) return DSA_ERR_SHAPE;
+    if (need_visible &&
+        (int64_t)L->max_blocks_per_seq * L->block_size < (int64_t)Q->max_visible)
+      return DSA_ERR_SHAPE;
+  } else {
+    if (L->seq_stride < 1) return DSA_ERR_SHAPE;
+    if (need_visible && L->seq_stride < Q->max_visible) return DSA_ERR_SHAPE;
+    if (L->pool_rows < (int64_t)(L->num_seqs - 1) * L->seq_stride + (need_visible ? Q->max_visible : 1))
+      return DSA_ERR_SHAPE;
+  }
+  return DSA_OK;
+}
+
+Layout make_layout(const dsa_layout* L) {
+  Layout d{};
+  d.bt = L->block_table;
+  d.bt_stride = L->max_blocks_per_seq;
+  d.bs_log2 = L->block_table ? log2i(L->block_size) : 0;
+  d.seq_stride = L->seq_stride;
+  return d;
+}
+
+bool indexer_fast(dsa_dtype q_dtype, dsa_dtype k_dtype, int32_t H, int32_t D) {
+  return q_dtype == DSA_BF16 && (k_dtype == DSA_BF16 || k_dtype == DSA_FP8_E4M3) && H == 64 &&
+         D == 128;
+}
+
+bool sfa_fast(dsa_dtype dtype, int32_t H, int32_t dqk, int32_t dv) {
+  return dtype == DSA_BF16 && dqk == kSfaDqk && dv == kSfaDv && H % 16 == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_indexer_topk_workspace_size(int32_t num_queries, int32_t max_visible, int32_t top_k) {
+  if (num_queries < 1 || max_visible < 1 || max_visible > DSA_MAX_CONTEXT || top_k < 1) return 0;
+  return plan_indexer(num_queries, max_visible, top_k).bytes;
+}
+
+dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_w,
+                            const void* k_pool, dsa_dtype k_dtype, const float* k_scale,
+                            int32_t n_heads, int32_t head_dim, const dsa_layout* layout,
+                            const dsa_queries* queries, int32_t top_k, int32_t* out_idx,
+                            float* out_score, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!q || !head_w || !k_pool || !out_idx) return DSA_ERR_NULL;
+  if (k_dtype == DSA_FP8_E4M3 && !k_scale) return DSA_ERR_NULL;
+  if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (k_dtype != DSA_F32 && k_dtype != DSA_BF16 && k_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  if (n_heads < 1 || head_dim < 8 || head_dim % 8 != 0) return DSA_ERR_SHAPE;
+  if ((int64_t)n_heads * head_dim > kGenericMaxHD || n_heads > kGenericMaxHeads)
+    return DSA_ERR_UNSUPPORTED;
+  if (top_k < 1) return DSA_ERR_SHAPE;
+  if (top_k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  dsa_status st = check_layout(layout, queries, true);
+  if (st != DSA_OK) return st;
+  if (misaligned(q) || misaligned(head_w) || misaligned(k_pool) || misaligned(k_scale) ||
+      misaligned(out_idx) || misaligned(out_score) || misaligned(workspace))
+    return DSA_ERR_ALIGN;
+  const int32_t T = queries->num_queries;
+  const IndexerPlan pl = plan_indexer(T, queries->max_visible, top_k);
+  if (!workspace || workspace_bytes < pl.bytes) return DSA_ERR_WORKSPACE;
+
+  IndexerParams p{};
+  p.q = q;
+  p.w = head_w;
+  p.k_pool = k_pool;
+  p.k_scale = k_dtype == DSA_FP8_E4M3 ? k_scale : nullptr;
+  p.L = make_layout(layout);
+  p.q_seq = queries->q_seq;
+  p.q_vis = queries->q_visible;
+  p.T = T;
+  p.H = n_heads;
+  p.D = head_dim;
+  p.K = top_k;
+  p.max_visible = queries->max_visible;
+  p.q_dtype = q_dtype;
+  p.k_dtype = k_dtype;
+  p.split = pl.split;
+  p.nsplit_max = pl.nsplit_max;
+  p.cap = pl.cap;
+  p.out_idx = out_idx;
+  p.out_score = out_score;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  p.counters = reinterpret_cast<uint32_t*>(ws + pl.off_counters);
+  p.hdr = reinterpret_cast<uint32_t*>(ws + pl.off_hdr);
+  p.cand_key = reinterpret_cast<uint32_t*>(ws + pl.off_ckey);
+  p.cand_pos = reinterpret_cast<int32_t*>(ws + pl.off_cpos);
+  p.flat_key = reinterpret_cast<uint32_t*>(ws + pl.off_fkey);
+  p.flat_pos = reinterpret_cast<int32_t*>(ws + pl.off_fpos);
+  const hipError_t e = launch_indexer(p, indexer_fast(q_dtype, k_dtype, n_heads, head_dim),
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+size_t dsa_sparse_attn_workspace_size(int32_t num_queries, int32_t n_heads, int32_t top_k,
+                                      int32_t d_v) {
+  if (num_queries < 1 || n_heads < 1 || top_k < 1 || d_v < 1) return 0;
+  // sized for the fast path, which needs at least as much as the reference path
+  return plan_sfa(num_queries, n_heads, top_k, d_v, n_heads % 16 == 0).bytes;
+}
+
+dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool, int32_t n_heads,
+                           int32_t d_qk, int32_t d_v, float softmax_scale,
+                           const dsa_layout* layout, const dsa_queries* queries,
+                           const int32_t* idx, int32_t top_k, void* out, float* out_lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kv_pool || !idx || !out) return DSA_ERR_NULL;
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (n_heads < 1 || n_heads > 1024) return DSA_ERR_SHAPE;
+  if (d_qk < 64 || d_qk % 64 != 0 || d_v < 64 || d_v % 64 != 0 || d_v > d_qk) return DSA_ERR_SHAPE;
+  if (d_qk > 1024) return DSA_ERR_UNSUPPORTED;
+  if (top_k < 1) return DSA_ERR_SHAPE;
+  if (top_k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (!(softmax_scale == softmax_scale)) return DSA_ERR_SHAPE;
+  dsa_status st = check_layout(layout, queries, false);
+  if (st != DSA_OK) return st;
+  if (misaligned(q) || misaligned(kv_pool) || misaligned(idx) || misaligned(out) ||
+      misaligned(out_lse) || misaligned(workspace))
+    return DSA_ERR_ALIGN;
+  const int32_t T = queries->num_queries;
+  const bool fast = sfa_fast(dtype, n_heads, d_qk, d_v);
+  const SfaPlan pl = plan_sfa(T, n_heads, top_k, d_v, fast);
+  if (!workspace || workspace_bytes < pl.bytes) return DSA_ERR_WORKSPACE;
+
+  SfaParams p{};
+  p.q = q;
+  p.kv = kv_pool;
+  p.L = make_layout(layout);
+  p.q_seq = queries->q_seq;
+  p.idx = idx;
+  p.T = T;
+  p.H = n_heads;
+  p.dqk = d_qk;
+  p.dv = d_v;
+  p.K = top_k;
+  p.scale = softmax_scale;
+  p.dtype = dtype;
+  p.heads_per_wg = pl.heads_per_wg;
+  p.n_hg = pl.n_hg;
+  p.rows_per_split = pl.rows_per_split;
+  p.nsplit = pl.nsplit;
+  p.out = out;
+  p.lse = out_lse;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  p.counters = reinterpret_cast<uint32_t*>(ws + pl.off_counters);
+  p.part_o = reinterpret_cast<float*>(ws + pl.off_part);
+  p.part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
+  const hipError_t e = launch_sfa(p, fast, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+dsa_status dsa_store_index_keys(const float* k_new, int32_t n_tokens, int32_t head_dim,
+                                const int64_t* slot, void* k_pool, dsa_dtype k_dtype,
+                                float* k_scale, void* stream) {
+  if (!k_new || !slot || !k_pool) return DSA_ERR_NULL;
+  if (k_dtype == DSA_FP8_E4M3 && !k_scale) return DSA_ERR_NULL;
+  if (k_dtype != DSA_F32 && k_dtype != DSA_BF16 && k_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  if (n_tokens < 1 || n_tokens > (1 << 30) || head_dim < 1) return DSA_ERR_SHAPE;
+  if (misaligned(k_new) || misaligned(slot) || misaligned(k_pool) || misaligned(k_scale))
+    return DSA_ERR_ALIGN;
+  const hipError_t e = launch_store_index_keys(k_new, n_tokens, head_dim, slot, k_pool, k_dtype,
+                                               k_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+dsa_status dsa_store_kv(const void* kv_new, dsa_dtype src_dtype, int32_t n_tokens, int32_t d_qk,
+                        const int64_t* slot, void* kv_pool, dsa_dtype pool_dtype, void* stream) {
+  if (!kv_new || !slot || !kv_pool) return DSA_ERR_NULL;
+  if ((src_dtype != DSA_F32 && src_dtype != DSA_BF16) ||
+      (pool_dtype != DSA_F32 && pool_dtype != DSA_BF16))
+    return DSA_ERR_DTYPE;
+  if (n_tokens < 1 || n_tokens > (1 << 30) || d_qk < 1) return DSA_ERR_SHAPE;
+  if (misaligned(kv_new) || misaligned(slot) || misaligned(kv_pool)) return DSA_ERR_ALIGN;
+  const hipError_t e = launch_store_kv(kv_new, src_dtype, n_tokens, d_qk, slot, kv_pool,
+                                       pool_dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size is out of range or inconsistent";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE: dtype not accepted for this argument";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape or size not built";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: device pointer not 16-byte aligned";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+}  // extern "C"

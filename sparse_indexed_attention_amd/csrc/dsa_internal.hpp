@@ -1,0 +1,90 @@
+// Host/device shared declarations: kernel parameter blocks, launch plans and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dsa_common.hpp"
+
+namespace dsa {
+
+// ------------------------------------------------------------------ indexer + Top-K
+constexpr int kIdxThreads = 256;
+constexpr int kSplitMax = 4096;        // context positions scored by one workgroup
+constexpr int kNSplitMax = 1024;       // context splits per query
+constexpr int kGenericMaxHD = 8192;    // n_heads * head_dim on the reference path
+constexpr int kGenericMaxHeads = 256;
+
+enum { kDtF32 = 0, kDtBF16 = 1, kDtFP8 = 2 };
+
+struct IndexerPlan {
+  int32_t split;        // positions per context split (multiple of 64)
+  int32_t nsplit_max;   // splits of the longest visible prefix
+  int32_t cap;          // candidate slots per split = min(split, top_k)
+  size_t off_counters, off_hdr, off_ckey, off_cpos, off_fkey, off_fpos, bytes;
+};
+
+struct IndexerParams {
+  const void* q;
+  const float* w;
+  const void* k_pool;
+  const float* k_scale;
+  Layout L;
+  const int32_t* q_seq;
+  const int32_t* q_vis;
+  int32_t T, H, D, K, max_visible;
+  int32_t q_dtype, k_dtype;
+  int32_t split, nsplit_max, cap;
+  int32_t* out_idx;
+  float* out_score;
+  uint32_t* counters;   // [T]            arrivals per query (self-resetting)
+  uint32_t* hdr;        // [T][nsplit][2] emitted count, threshold key
+  uint32_t* cand_key;   // [T][nsplit][cap]
+  int32_t* cand_pos;    // [T][nsplit][cap]
+  uint32_t* flat_key;   // [T][nsplit*cap]
+  int32_t* flat_pos;    // [T][nsplit*cap]
+};
+
+IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k);
+hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream);
+
+// ------------------------------------------------------------------ sparse attention
+constexpr int kSfaDqk = 576;
+constexpr int kSfaDv = 512;
+
+struct SfaPlan {
+  int32_t heads_per_wg;   // heads handled by one workgroup (fast path)
+  int32_t n_hg;           // head groups
+  int32_t rows_per_split; // selected rows per split (multiple of 32)
+  int32_t nsplit;         // splits of top_k
+  size_t off_counters, off_part, off_ml, bytes;
+};
+
+struct SfaParams {
+  const void* q;          // [T, H, d_qk]
+  const void* kv;         // [rows, d_qk]
+  Layout L;
+  const int32_t* q_seq;
+  const int32_t* idx;     // [T, K]
+  int32_t T, H, dqk, dv, K;
+  float scale;
+  int32_t dtype;
+  int32_t heads_per_wg, n_hg, rows_per_split, nsplit;
+  void* out;              // [T, H, d_v]
+  float* lse;             // [T, H] or nullptr
+  uint32_t* counters;     // [T][n_hg]
+  float* part_o;          // [T][n_hg][nsplit][heads_per_wg][d_v]
+  float* part_ml;         // [T][n_hg][nsplit][heads_per_wg][2]
+};
+
+SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path);
+hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream);
+
+// ------------------------------------------------------------------ cache writers
+hipError_t launch_store_index_keys(const float* k_new, int32_t n, int32_t D, const int64_t* slot,
+                                   void* k_pool, int32_t k_dtype, float* k_scale, hipStream_t s);
+hipError_t launch_store_kv(const void* kv_new, int32_t src_dtype, int32_t n, int32_t dqk,
+                           const int64_t* slot, void* kv_pool, int32_t pool_dtype, hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,192 @@
+"""GPU parity of dsa_indexer_topk against the oracle, through the C ABI.
+
+Tolerance (per query): the returned set has exactly K_eff distinct positions in [0, V) and
+differs from the oracle's only at positions whose fp32 score is within 1e-6 relative of the
+oracle's K-th score.  Strict suites (integer-exact scores, planted ties between
+bit-identical keys, the fp8 code table) require identical sets and exact scores."""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_inputs, scaled_spec, workload
+from synth.device import to_device
+from tests.gpu_util import log, run_indexer, score_error
+from tests.helpers import plant_ties, rows_of, set_integer_exact
+
+pytestmark = pytest.mark.gpu
+
+
+def check(inp, idx, score, strict=False, queries=None, score_tol=2e-6):
+    refs = oracle.indexer_topk(inp, queries)
+    res = oracle.check_topk(idx, refs, strict=strict)
+    errs = [score_error(score[r.t], idx[r.t], r) for r in refs]
+    log(f"  {inp.spec.name}: {len(refs)} queries, in-band diffs {res.n_in_band_diff}, "
+        f"max score err / kth {max(errs):.2e}")
+    assert res.ok, "\n".join(res.msgs[:10])
+    assert max(errs) <= score_tol
+    return refs
+
+
+CASES = {
+    # reference path: fp32 q/k, 8 heads x 64, contiguous, K=256 (the tiny workload, full size)
+    "tiny_fp32": lambda: workload(1),
+    "tiny_fp32_paged": lambda: scaled_spec(workload(1), seq_lens=[4096, 1500, 33], block_size=16,
+                                           permute=True, extra_blocks=2),
+    # MFMA path, bf16 keys: lengths around K and the 64-token pages, several splits
+    "bf16_mixed": lambda: scaled_spec(workload(2), seq_lens=[5000, 777, 9000, 64, 1, 130, 2047,
+                                                             2048, 2049, 63, 65]),
+    "bf16_k100": lambda: scaled_spec(workload(2), seq_lens=[5000, 9000, 130, 17000], top_k=100),
+    "bf16_bs128": lambda: scaled_spec(workload(2), seq_lens=[12345, 3000], block_size=128),
+    # MFMA path, fp8 keys with per-token scales
+    "fp8_mixed": lambda: scaled_spec(workload(4), seq_lens=[20000, 3333, 2049, 65, 1]),
+    "fp8_k256": lambda: scaled_spec(workload(4), seq_lens=[30000, 70000], top_k=256),
+    # reference path with mixed formats
+    "ref_bf16q_fp8k": lambda: scaled_spec(workload(4), seq_lens=[3000, 5000], idx_heads=16,
+                                          idx_dim=64, top_k=300),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_indexer_matches_oracle(dsa, case):
+    spec = CASES[case]()
+    inp = make_inputs(spec, seed=zlib.crc32(case.encode()) % 1000, with_sfa=False)
+    log(f"case {case}: T={spec.num_queries} maxV={spec.max_visible} K={spec.top_k}")
+    idx, score = run_indexer(dsa, inp)
+    check(inp, idx, score, score_tol=2e-6 if spec.idx_heads == 64 else 1e-6)
+
+
+@pytest.mark.parametrize("k_dtype", ["bf16", "fp8"])
+def test_integer_exact_suite_is_bit_exact(dsa, k_dtype):
+    spec = scaled_spec(workload(4), seq_lens=[6000, 1500, 64, 65, 20000], k_dtype=k_dtype,
+                       top_k=512)
+    inp = make_inputs(spec, seed=21, with_sfa=False)
+    set_integer_exact(inp, np.random.default_rng(3))
+    idx, score = run_indexer(dsa, inp)
+    refs = check(inp, idx, score, strict=True, score_tol=0.0)
+    for r in refs:
+        assert np.array_equal(score[r.t][:r.k_eff], r.S32[idx[r.t][:r.k_eff]])
+
+
+def test_fp8_code_table_through_the_fast_path(dsa):
+    """Each key holds one fp8 code in dim 77 (scale 1); head 0 of the query is +-e_77 and the
+    only weighted head, so every score is ReLU(+-code value): all 254 finite codes come
+    back exactly through the MFMA path's fp8 widening."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    V = codes.size
+    spec = scaled_spec(workload(4), seq_lens=[V], q_seq=[0, 0], q_visible=[V, V], top_k=V)
+    inp = make_inputs(spec, seed=2, with_sfa=False)
+    rows = rows_of(inp, 0, np.arange(V))
+    inp.k_pool[rows] = 0
+    inp.k_pool[rows, 77] = codes
+    inp.k_scale[rows] = 1.0
+    inp.q_idx[...] = 0
+    inp.q_idx[0, 0, 77] = 0x3F80          # +1.0 (bf16 bits)
+    inp.q_idx[1, 0, 77] = 0xBF80          # -1.0
+    inp.w[...] = 0
+    inp.w[:, 0] = 1.0
+    idx, score = run_indexer(dsa, inp)
+    vals = oracle.decode_fp8_e4m3(codes)
+    for t, sign in ((0, 1.0), (1, -1.0)):
+        got = np.zeros(V)
+        got[idx[t]] = score[t]
+        assert np.array_equal(got, np.maximum(sign * vals, 0.0)), t
+    check(inp, idx, score, strict=True, score_tol=0.0)
+
+
+def test_planted_ties_select_lowest_position(dsa):
+    spec = scaled_spec(workload(5), seq_lens=[200000], top_k=2048)
+    inp = make_inputs(spec, seed=55, with_sfa=False)
+    groups = plant_ties(inp, 0, np.random.default_rng(7))
+    idx, score = run_indexer(dsa, inp)
+    refs = check(inp, idx, score)
+    sel = set(idx[0][:refs[0].k_eff].tolist())
+    assert set(groups["interior"].tolist()) <= sel
+    assert not (set(groups["exterior"].tolist()) & sel)
+    bnd = groups["boundary"]
+    assert [p in sel for p in bnd.tolist()] == [True] + [False] * (len(bnd) - 1)
+    assert len(set(score[0][np.isin(idx[0], groups["interior"])].tolist())) == 1
+
+
+def test_concentrated_top_positions_take_the_fallback(dsa):
+    """All of the top positions sit in one stretch of the context, far more than any split's
+    share, so split thresholds cut too high and the merge must re-score those splits."""
+    spec = scaled_spec(workload(2), seq_lens=[40000, 30000], top_k=1500)
+    inp = make_inputs(spec, seed=77, with_sfa=False)
+    for b, (lo, hi) in enumerate([(8000, 10000), (29000, 30000)]):
+        rows = rows_of(inp, b, np.arange(lo, hi))
+        k = oracle.decode_bf16(inp.k_pool[rows]) * 4.0          # exact in bf16
+        inp.k_pool[rows] = oracle.encode_bf16_rne(k.astype(np.float32))
+    idx, score = run_indexer(dsa, inp)
+    check(inp, idx, score)
+
+
+def test_layout_invariance_and_determinism(dsa):
+    spec = scaled_spec(workload(4), seq_lens=[30000, 9000])
+    paged = make_inputs(spec, seed=5, with_sfa=False)
+    contig_spec = scaled_spec(spec, block_size=0, permute=False, extra_blocks=0)
+    contig = make_inputs(contig_spec, seed=5, with_sfa=False)
+    stride = contig.seq_stride
+    for b, n in enumerate(spec.seq_lens):
+        r = rows_of(paged, b, np.arange(n))
+        contig.k_pool[b * stride:b * stride + n] = paged.k_pool[r]
+        contig.k_scale[b * stride:b * stride + n] = paged.k_scale[r]
+    contig.q_idx[...] = paged.q_idx
+    contig.w[...] = paged.w
+    i1, s1 = run_indexer(dsa, paged)
+    i2, s2 = run_indexer(dsa, paged)
+    i3, s3 = run_indexer(dsa, contig)
+    assert np.array_equal(i1, i2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(i1, i3) and np.array_equal(s1.view(np.uint32), s3.view(np.uint32))
+
+
+def test_workspace_reuse_across_sizes(dsa):
+    """One zero-initialised workspace serves a large call and then smaller ones."""
+    big = scaled_spec(workload(2), seq_lens=[40000, 40000, 3000])
+    small = scaled_spec(workload(2), seq_lens=[9000])
+    inp_b = make_inputs(big, seed=1, with_sfa=False)
+    inp_s = make_inputs(small, seed=2, with_sfa=False)
+    ws = dsa.zeroed_workspace(dsa.indexer_workspace_bytes(3, 40000, 2048), "cuda")
+    for inp in (inp_b, inp_s, inp_b):
+        idx, score = run_indexer(dsa, inp, workspace=ws)
+        check(inp, idx, score)
+
+
+# ---- full-size workloads (all queries, or a sample the oracle can score) ---------------------
+@pytest.mark.slow
+def test_full_decode_bf16_32k(dsa):
+    inp = make_inputs(workload(2), seed=2, with_sfa=False)
+    idx, score = run_indexer(dsa, inp)
+    check(inp, idx, score)
+
+
+@pytest.mark.slow
+def test_full_decode_fp8_128k(dsa):
+    inp = make_inputs(workload(4), seed=4, with_sfa=False)
+    idx, score = run_indexer(dsa, inp)
+    check(inp, idx, score)
+
+
+@pytest.mark.slow
+def test_full_decode_fp8_1m_with_planted_ties(dsa):
+    inp = make_inputs(workload(5), seed=5, with_sfa=False)
+    groups = plant_ties(inp, 0, np.random.default_rng(5))
+    idx, score = run_indexer(dsa, inp)
+    check(inp, idx, score)
+    sel = set(idx[0][:2048].tolist())
+    assert set(groups["interior"].tolist()) <= sel
+    assert not (set(groups["exterior"].tolist()) & sel)
+    bnd = groups["boundary"]
+    assert [p in sel for p in bnd.tolist()] == [True] + [False] * (len(bnd) - 1)
+
+
+@pytest.mark.slow
+def test_full_chunked_prefill_sampled(dsa):
+    inp = make_inputs(workload(3), seed=3, with_sfa=False)
+    idx, score = run_indexer(dsa, inp)
+    sample = [0, 1, 777, 2048, 4094, 4095]
+    check(inp, idx, score, queries=sample)
+    # causal: no query selects a position it cannot see
+    V = inp.q_visible
+    assert np.all((idx < V[:, None]) | (idx == -1))
