@@ -20,6 +20,7 @@ recorded around it inside the timed region) and the CPU oracle timed on a bounde
 from __future__ import annotations
 
 import argparse
+import copy
 import hashlib
 import json
 import math
@@ -171,9 +172,7 @@ def main():
     base = to_device(inp, "cuda")
     devs = [base]
     for _ in range(copies - 1):
-        c = to_device(inp, "cuda") if False else None
-        import copy as _copy
-        c = _copy.copy(base)
+        c = copy.copy(base)
         for f in ("q_idx", "w", "k_pool", "k_scale", "q_sfa", "kv_pool", "block_table", "q_seq",
                   "q_visible"):
             v = getattr(base, f)

@@ -111,7 +111,8 @@ typedef struct {
  *   k_scale:[pool_rows] fp32, required for FP8_E4M3, ignored otherwise
  *   1 <= n_heads * head_dim <= 8192, head_dim % 8 == 0, 1 <= top_k <= DSA_MAX_TOPK.
  * The fast path (MFMA scoring) runs for q BF16, keys BF16 or FP8_E4M3, n_heads 64, head_dim
- * 128.  Every other accepted combination runs a reference path that scores in fp64.
+ * 128 and a contiguous layout or block_size >= 32.  Every other accepted combination runs a
+ * reference path that scores in fp64.
  *
  * workspace: dsa_indexer_topk_workspace_size(...) bytes.  It MUST be zero-filled before its
  * first use; every call leaves it zero-filled again where that matters, so one buffer can be

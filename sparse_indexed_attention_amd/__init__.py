@@ -48,11 +48,13 @@ _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libdsa.so (raises if it has not been built)."""
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libdsa.so (raises if it has not been built).  DSA_LIB_PATH overrides the
+    in-tree location."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("DSA_LIB_PATH") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            f"`python -m sparse_indexed_attention_amd.build`")

@@ -55,9 +55,10 @@ Layout make_layout(const dsa_layout* L) {
   return d;
 }
 
-bool indexer_fast(dsa_dtype q_dtype, dsa_dtype k_dtype, int32_t H, int32_t D) {
+bool indexer_fast(dsa_dtype q_dtype, dsa_dtype k_dtype, int32_t H, int32_t D,
+                  const dsa_layout* L) {
   return q_dtype == DSA_BF16 && (k_dtype == DSA_BF16 || k_dtype == DSA_FP8_E4M3) && H == 64 &&
-         D == 128;
+         D == 128 && (!L->block_table || L->block_size >= kMinFastBlock);
 }
 
 bool sfa_fast(dsa_dtype dtype, int32_t H, int32_t dqk, int32_t dv) {
@@ -123,8 +124,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
   p.cand_key = reinterpret_cast<uint32_t*>(ws + pl.off_ckey);
   p.cand_pos = reinterpret_cast<int32_t*>(ws + pl.off_cpos);
   p.flat_key = reinterpret_cast<uint32_t*>(ws + pl.off_fkey);
-  p.flat_pos = reinterpret_cast<int32_t*>(ws + pl.off_fpos);
-  const hipError_t e = launch_indexer(p, indexer_fast(q_dtype, k_dtype, n_heads, head_dim),
+  const hipError_t e = launch_indexer(p, indexer_fast(q_dtype, k_dtype, n_heads, head_dim, layout),
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

@@ -11,8 +11,10 @@ namespace dsa {
 
 // ------------------------------------------------------------------ indexer + Top-K
 constexpr int kIdxThreads = 256;
-constexpr int kSplitMax = 4096;        // context positions scored by one workgroup
-constexpr int kNSplitMax = 1024;       // context splits per query
+constexpr int kSplitMax = 2048;        // context positions scored by one workgroup
+constexpr int kNSplitMax = 2048;       // context splits per query
+constexpr int kMaxTopK = 2048;         // largest top_k
+constexpr int kMinFastBlock = 32;      // smallest page size of the MFMA path (one page per 32-position group)
 constexpr int kGenericMaxHD = 8192;    // n_heads * head_dim on the reference path
 constexpr int kGenericMaxHeads = 256;
 
@@ -22,7 +24,7 @@ struct IndexerPlan {
   int32_t split;        // positions per context split (multiple of 64)
   int32_t nsplit_max;   // splits of the longest visible prefix
   int32_t cap;          // candidate slots per split = min(split, top_k)
-  size_t off_counters, off_hdr, off_ckey, off_cpos, off_fkey, off_fpos, bytes;
+  size_t off_counters, off_hdr, off_ckey, off_cpos, off_fkey, bytes;
 };
 
 struct IndexerParams {
@@ -42,8 +44,7 @@ struct IndexerParams {
   uint32_t* hdr;        // [T][nsplit][2] emitted count, threshold key
   uint32_t* cand_key;   // [T][nsplit][cap]
   int32_t* cand_pos;    // [T][nsplit][cap]
-  uint32_t* flat_key;   // [T][nsplit*cap]
-  int32_t* flat_pos;    // [T][nsplit*cap]
+  uint32_t* flat_key;   // [T][nsplit*cap]  merge scratch when the candidates exceed LDS
 };
 
 IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k);

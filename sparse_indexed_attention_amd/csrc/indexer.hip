@@ -6,29 +6,39 @@
 // Scoring, head-weighted aggregation and Top-K run in one kernel that reads the paged key
 // cache directly and writes only the index list: the fused index operator of "Large Model
 // Inference Acceleration: Day-0 Adaptation..." (section 1.1) and of "Day0 Adaptation and
-// Sparse Attention Optimization for Long-Sequence LLM Inference" (section 4).  The
-// per-head scores never leave the registers and the per-position scores stay in LDS.
+// Sparse Attention Optimization for Long-Sequence LLM Inference" (section 4).  The per-head
+// scores never leave the registers and the per-position scores stay in LDS.
 //
-// Work decomposition (MI355X: 256 CUs, wave64, 160 KB LDS per CU):
-//   * one workgroup per (query, context split of `split` positions);
-//   * scoring: each wave takes groups of 32 positions; one v_mfma_f32_32x32x16_bf16 chain
-//     per 32-head half computes x[head, position] for the group (keys as the B operand,
-//     straight from HBM in MFMA lane layout; fp8 keys are widened to bf16 exactly), then each
-//     lane applies ReLU and the head weights to the 16 accumulator rows it holds and one
-//     cross-lane add finishes the head sum.  The fp8 per-token scale multiplies the head sum
-//     (ReLU(c x) = c ReLU(x) for c > 0).  Every position goes through the same instruction
-//     sequence, so bit-identical keys get bit-identical scores wherever they sit;
-//   * each split picks a threshold key with radix histograms over its LDS scores so that a
-//     little more than its expected share of the Top-K survives, and writes those
-//     candidates (order-preserving key, position) to the workspace;
-//   * the last split of a query to arrive (atomic counter) gathers the candidates, finds the
-//     exact K_eff-th key by radix select, and checks that every split's threshold lies at or
-//     below it - then the candidates provably contain the exact answer.  A split whose
-//     threshold was too high is re-scored by the merging workgroup and contributes its exact
-//     local Top-K instead (rare for any input whose top positions are not concentrated in a
+// Work decomposition (MI355X: 256 CUs in 8 XCDs, wave64, 160 KB LDS per CU):
+//   * one workgroup of 4 waves per (query, context split of `split` positions);
+//   * scoring: each wave takes a contiguous run of 32-position groups.  Key bytes travel
+//     HBM -> LDS with fully coalesced direct-to-LDS loads into a per-wave ring of groups.  Per
+//     group, one v_mfma_f32_32x32x16_bf16 chain per 32-head half computes x[head, position]
+//     (keys as the B operand, read back from LDS in MFMA lane layout; fp8 keys widened to
+//     bf16 exactly), then each lane applies ReLU and the head weights to the 16 accumulator
+//     rows it holds and one cross-lane add finishes the head sum.  The fp8 per-token scale
+//     multiplies the head sum (ReLU(c x) = c ReLU(x) for c > 0).  Every position goes
+//     through the same instruction sequence, so bit-identical keys get bit-identical scores
+//     wherever they sit;
+//   * each split picks a threshold key by radix selection over its LDS scores so that a
+//     little more than its expected share of the Top-K survives, and writes those candidates
+//     (order-preserving key, position) to the workspace in position order;
+//   * the last split of a query to arrive (atomic counter) gathers the candidate keys into
+//     LDS, finds the exact K_eff-th key by radix selection, and checks that every split's
+//     threshold lies at or below it - then the candidates provably contain the exact answer.
+//     A split whose threshold was too high is re-scored by the merging workgroup and
+//     contributes its exact local Top-K instead (rare unless the top positions crowd into a
 //     few splits; always correct).
+//   * Cross-workgroup data (candidates, split headers) is written and read with agent-scope
+//     accesses, which are coherent across the XCDs' separate L2 caches without writing back
+//     or invalidating those caches; each writer waits for its stores to complete before it
+//     increments the arrival counter.
+// Code that runs once per workgroup is kept in loops rather than unrolled: it executes cold
+// from the instruction cache, so its size, not its instruction count, sets its time.
 // A query whose prefix fits one split does the exact selection in place.
 // A reference path (any supported dtypes and head geometry) scores each position in fp64.
+
+#include <cstdlib>
 
 #include "dsa_internal.hpp"
 
@@ -36,15 +46,45 @@ namespace dsa {
 namespace {
 
 constexpr int NT = kIdxThreads;
+constexpr int NWAVE = NT / 64;
+constexpr int kBins = 2048;               // radix bins per pass
 
-struct Smem {
-  uint32_t keys[kSplitMax];
-  int hist[256];
-  int res[4];
-  int scan[NT / 64 + 2];
-  int seg_off[kNSplitMax + 1];
-  uint32_t seg_tau[kNSplitMax];
-  int bcast[4];
+// LDS ring of the MFMA scorer: D slots per wave (D a power of two), each holding one
+// 32-position group of keys (+ its fp8 scales).
+template <int MODE> struct Ring { static constexpr int D = 1, SLOT = 0; };
+template <> struct Ring<1> { static constexpr int D = 2, SLOT = 8192; };          // bf16 keys
+template <> struct Ring<2> { static constexpr int D = 4, SLOT = 4096 + 256; };    // fp8 keys + scales
+
+// Bytes of the kernel's shared region: the scorer's ring while scoring, then the selection
+// arrays.
+template <int MODE>
+constexpr int region_bytes() {
+  return MODE == 0 ? 65536 : Ring<MODE>::D * NWAVE * Ring<MODE>::SLOT;
+}
+// Merge layout of the region: split offsets, split thresholds, then the flat candidate keys.
+constexpr int kSegOffBytes = (kNSplitMax + 1) * 4 + 12;
+constexpr int kFlatOffset = kSegOffBytes + kNSplitMax * 4;
+template <int MODE>
+constexpr int flat_capacity() {
+  return ((region_bytes<MODE>() - kFlatOffset) / 4 - 64) / 64 * 64;
+}
+
+// Pointers to the kernel's LDS arrays.
+struct Lds {
+  uint32_t* keys;     // [kSplitMax] order-preserving score keys of the split
+  const float* w;     // [NWAVE][64] head weights, one copy per wave (MFMA paths)
+  uint8_t* region;    // region_bytes<MODE>()
+  int* hist;          // [kBins]
+  int* seg_off;       // [kNSplitMax + 1]
+  uint32_t* seg_tau;  // [kNSplitMax]
+  uint32_t* flat;     // [flat_capacity]
+  int* res;           // [4]
+  int* scan;          // [2 * NWAVE + 2]
+  int* wcnt;          // [2 * NWAVE]
+  int* bcast;         // [4]
+  uint32_t* range;    // [2 * NWAVE] per-wave smallest and largest score key of the split
+  int* psum;          // [NT] partial histogram sums
+  uint32_t* small;    // [64] keys of one histogram bin
 };
 
 struct GenericSmem {
@@ -52,21 +92,144 @@ struct GenericSmem {
   float w[kGenericMaxHeads];
 };
 
+// cross-workgroup stores and loads (see the header comment)
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+// LDS byte address of a pointer into LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct-to-LDS load: each active lane l reads SIZE bytes (16 or 4) at gbase + voff and they
+// land at LDS byte address lds + SIZE * l; gbase and lds are wave-uniform.  AGENT makes it an
+// agent-scope (cross-XCD coherent) read, like ld_agent.  Issued as inline asm, so the
+// compiler does not see these LDS writes (its own wait insertion would otherwise drain every
+// outstanding load before each LDS read); the callers wait for them with vmcnt, and the asm's
+// memory clobber keeps the compiler from moving LDS accesses across it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int SIZE, bool AGENT = false>
+__device__ __forceinline__ void load_to_lds(const void* gptr, uint32_t voff, uint32_t lds_in) {
+  static_assert(SIZE == 16 || SIZE == 4, "load size");
+  // the operands are wave-uniform; make them scalar for the instruction's SGPR fields
+  const uint64_t ga = (uint64_t)(uintptr_t)gptr;
+  const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)ga);
+  const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
+  const void* gbase = (const void*)(uintptr_t)(((uint64_t)ghi << 32) | glo);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
+  else if constexpr (AGENT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 sc1"
+                 :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// ---------------------------------------------------------------------------------------
+// Wave-level cross-lane operations on DPP (row shifts within 16-lane rows, then row
+// broadcasts across them): a few VALU cycles per step instead of an LDS round trip.
+// ---------------------------------------------------------------------------------------
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t id, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ int wave_scan_add(int v) {
+  return (int)wave_incl_scan((uint32_t)v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  v = wave_incl_scan(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = wave_incl_scan(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // ---------------------------------------------------------------------------------------
 // Scoring
 // ---------------------------------------------------------------------------------------
+
+// max(x, 0) for any non-NaN float as one integer max on its bits: every negative float
+// (and -0) has a negative int32 pattern and maps to +0; non-negative floats are unchanged.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
 
 // MFMA scorer: q bf16 [64 heads x 128 dims], keys bf16 or fp8 (128 per token).
 // Lane layout of v_mfma_f32_32x32x16_bf16: lane l supplies row/column (l & 31) and the
 // 8-element k-slice 8*(l >> 5) .. +7; accumulator element r of lane l is
 // D[8*(r/4) + 4*(l>>5) + (r%4)][l & 31].  The 128 key dims are assigned to k-slices so that
-// lane half h reads dims [64h, 64h+64) of its key row contiguously; the query uses the same
-// assignment, so every MFMA step still pairs equal dims.
-template <bool FP8>
+// lane half h takes dims [64h, 64h+64) of its key row; the query uses the same assignment,
+// so every MFMA step still pairs equal dims.
+// Key rows of a group land in the ring with coalesced direct-to-LDS loads (each load
+// instruction moves 1 KB: whole 128-byte lines per 8 or 16 lanes); each row's 16-byte chunks
+// are XOR-swizzled by the row index so that the MFMA-layout reads back from LDS hit distinct
+// banks.  A group lies in one page (pages hold >= 32 tokens; splits start at multiples of
+// 64), whose block id is one wave-uniform scalar load.  Group indices past the wave's run
+// are clamped onto its last group (harmless re-reads) so every step issues the same loads
+// and the hardware waits stay exact.
+template <bool FP8, bool PAGED, int MODE>
 __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int seq, int start,
-                                           int len, uint32_t* lkeys) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                           int len, const Lds& L, uint32_t& kr_lo, uint32_t& kr_hi) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
+  constexpr int ROWB = FP8 ? 128 : 256;       // bytes per key row
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  constexpr int GB = 32 * ROWB;               // key bytes per group
+  constexpr int NI = GB / 1024;               // direct-to-LDS loads per group (keys)
+  constexpr int D = Ring<MODE>::D;            // ring depth: D-1 groups in flight
+  constexpr int SLOT = Ring<MODE>::SLOT;
+  constexpr int LPG = NI + (FP8 ? 1 : 0);     // loads per group
+  constexpr int RPI = 1024 / ROWB;            // rows per load instruction
+  constexpr int LPR = 64 / RPI;               // lanes per row in a load instruction
+  static_assert(GB + (FP8 ? 256 : 0) <= SLOT, "slot size");
+  static_assert((D & (D - 1)) == 0, "ring depth is a power of two");
+
+  const int ngroups = (len + 31) >> 5;
+  const int per = (ngroups + NWAVE - 1) / NWAVE;
+  const int g0 = min(ngroups, wave * per), g1 = min(ngroups, g0 + per);
+  if (g0 >= g1) return;
+  static_assert(kSplitMax / 32 / NWAVE <= 64, "one lane per group of a wave's run");
+  // One round trip brings the query (registers), this wave's copy of the head weights (LDS)
+  // and the pages of its groups (lane l: the block id of group g0 + l).
   const uint16_t* qb = (const uint16_t*)p.q + (size_t)t * (64 * 128);
   bf16x8 a0[8], a1[8];
 #pragma unroll
@@ -74,74 +237,113 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
     a0[s] = *(const bf16x8*)(qb + col * 128 + half * 64 + 8 * s);
     a1[s] = *(const bf16x8*)(qb + (32 + col) * 128 + half * 64 + 8 * s);
   }
-  float w0[16], w1[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = 8 * (r >> 2) + 4 * half + (r & 3);
-    w0[r] = p.w[t * 64 + i];
-    w1[r] = p.w[t * 64 + 32 + i];
-  }
-  constexpr int NV = FP8 ? 4 : 8;             // 16-byte loads per lane per group
-  constexpr int ROWB = FP8 ? 128 : 256;       // bytes per key row
-  const uint8_t* kbase = (const uint8_t*)p.k_pool + half * (ROWB / 2);
-  const int ngroups = (len + 31) >> 5;
+  const float* lw = L.w + wave * 64;
+  load_to_lds<4>(p.w + (size_t)t * 64, 4u * lane, lds_addr(lw));
+  int gblk = 0;
+  if constexpr (PAGED)
+    gblk = p.L.bt[(int64_t)seq * p.L.bt_stride + ((start + 32 * min(g0 + lane, g1 - 1)) >> p.L.bs_log2)];
+  uint32_t& kmin = kr_lo;
+  uint32_t& kmax = kr_hi;
+  const int bsl = PAGED ? p.L.bs_log2 : 0;
+  const int64_t cbase = PAGED ? 0 : (int64_t)seq * p.L.seq_stride;
+  const uint8_t* kbytes = (const uint8_t*)p.k_pool;
+  const int cpos = lane % LPR;                // chunk position this lane fills in its row
+  // slot k of this wave's ring
+  uint8_t* const ring0 = L.region + wave * SLOT;
+  auto slot_of = [&](int k) { return ring0 + k * (NWAVE * SLOT); };
 
-  auto load = [&](int g, u32x4* raw, float& sc) {
-    const int off = g * 32 + col;
-    if (off < len) {
-      const int64_t row = pool_row(p.L, seq, start + off);
-      const u32x4* src = (const u32x4*)(kbase + row * ROWB);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) raw[i] = __builtin_nontemporal_load(src + i);
-      sc = FP8 ? p.k_scale[row] : 1.f;
-    } else {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
-      sc = 0.f;
+  // Group g covers positions start + 32g + [0, 32) (the last group of a split stops at len;
+  // its rows past the end re-read its last row).  All of them lie in one page, so the
+  // group's first pool row is wave-uniform and the lanes add 32-bit offsets to it.
+  auto issue = [&](int g, uint8_t* sb) {
+    g = min(g, g1 - 1);
+    const int gpos = start + 32 * g;
+    const int last = len - 1 - 32 * g;        // last valid row of the group (>= 0)
+    int64_t row0;
+    if constexpr (PAGED) {
+      const int blk = __builtin_amdgcn_readlane(gblk, g - g0);
+      row0 = ((int64_t)blk << bsl) | (gpos & ((1 << bsl) - 1));
     }
+    else row0 = cbase + gpos;
+    const uint8_t* gbase = kbytes + row0 * ROWB;
+    const uint32_t lb = lds_addr(sb);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = RPI * i + lane / LPR;
+      const uint32_t off = (uint32_t)(min(r, last) * ROWB + 16 * (cpos ^ (r & (CPR - 1))));
+      load_to_lds<16>(gbase, off, lb + 1024 * i);
+    }
+    if constexpr (FP8) load_to_lds<4>(p.k_scale + row0, 4u * (uint32_t)min(col, last), lb + GB);
   };
-
-  u32x4 cur[NV], nxt[NV];
-  float csc = 0.f, nsc = 0.f;
-  int g = wave;
-  if (g < ngroups) load(g, cur, csc);
-  for (; g < ngroups; g += 4) {
-    const bool more = g + 4 < ngroups;
-    if (more) load(g + 4, nxt, nsc);
-    f32x16 acc0 = {}, acc1 = {};
+  // Group g's products: both 32-head chains of MFMAs over the key rows in slot sb.
+  auto products = [&](const uint8_t* sb, f32x16& acc0, f32x16& acc1) {
+    const uint8_t* rb = sb + col * ROWB;      // this lane's row
+    acc0 = f32x16{};
+    acc1 = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      bf16x8 b;
+      bf16x8 kb;
       if constexpr (FP8) {
-        const u32x4 v = cur[s >> 1];
+        const u32x4 v = *(const u32x4*)(rb + 16 * ((4 * half + (s >> 1)) ^ (col & (CPR - 1))));
         const uint32_t lo = (s & 1) ? v.z : v.x;
         const uint32_t hi = (s & 1) ? v.w : v.y;
         const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
         const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
         const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
         const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-        b = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        kb = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       } else {
-        b = __builtin_bit_cast(bf16x8, cur[s]);
+        kb = *(const bf16x8*)(rb + 16 * ((8 * half + s) ^ (col & (CPR - 1))));
       }
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], b, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], kb, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], kb, acc1, 0, 0, 0);
     }
-    float part = 0.f;
+  };
+  // Group g's scores from its products: ReLU, head weights, head sum, fp8 token scale.
+  auto finish = [&](int g, const f32x16& acc0, const f32x16& acc1, float scale) {
+    // head weights of accumulator rows 8*(r/4) + 4*half + (r%4): four consecutive floats;
+    // four independent partial sums keep the dependent adds short
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part = fmaf(w0[r], fmaxf(acc0[r], 0.f), part);
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 w0 = *(const f32x4*)(lw + 8 * rg + 4 * half);
+      const f32x4 w1 = *(const f32x4*)(lw + 32 + 8 * rg + 4 * half);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part = fmaf(w1[r], fmaxf(acc1[r], 0.f), part);
-    float tot = part + __shfl_xor(part, 32, 64);
-    if constexpr (FP8) tot *= csc;
+      for (int u = 0; u < 4; ++u) {
+        part[u] = fmaf(w0[u], relu(acc0[4 * rg + u]), part[u]);
+        part[u] = fmaf(w1[u], relu(acc1[4 * rg + u]), part[u]);
+      }
+    }
+    const float psum = (part[0] + part[1]) + (part[2] + part[3]);
+    float tot = psum + __shfl_xor(psum, 32, 64);
+    if constexpr (FP8) tot *= scale;
     const int off = g * 32 + col;
-    if (half == 0 && off < len) lkeys[off] = float_to_key(tot);
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
-      csc = nsc;
+    if (half == 0 && off < len) {
+      const uint32_t key = float_to_key(tot);
+      L.keys[off] = key;
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
     }
+  };
+
+  // The query must be in registers before the ring starts: left pending, the compiler's wait
+  // for it would sit inside the loop and drain the ring on every step.
+  wait_vmcnt<0>();
+  for (int k = 0; k < D - 1; ++k) issue(g0 + k, slot_of(k));
+#pragma unroll 1
+  for (int g = g0; g < g1; ++g) {
+    const int k = (g - g0) & (D - 1);
+    // refill the slot consumed in the previous step (its LDS reads have completed)
+    issue(g + D - 1, slot_of((k + D - 1) & (D - 1)));
+    wait_vmcnt<LPG * (D - 1)>();              // group g has landed in LDS
+    const uint8_t* sb = slot_of(k);
+    f32x16 acc0, acc1;
+    products(sb, acc0, acc1);
+    // both chains are issued before any accumulator is read, so they interleave
+    __builtin_amdgcn_sched_barrier(0);
+    finish(g, acc0, acc1, FP8 ? *(const float*)(sb + GB + 4 * col) : 1.f);
   }
+  wait_vmcnt<0>();                            // no load may still target the ring afterwards
 }
 
 __device__ __forceinline__ float load_elem(const void* base, int dt, int64_t i) {
@@ -152,8 +354,9 @@ __device__ __forceinline__ float load_elem(const void* base, int dt, int64_t i) 
 
 // Reference scorer: one thread per position, fp64 accumulation (products of the stored
 // operands are exact in fp64), rounded once to fp32.
-__device__ void score_generic(const IndexerParams& p, int seq, int start, int len,
-                              uint32_t* lkeys, const GenericSmem& gs) {
+__device__ __forceinline__ void score_generic(const IndexerParams& p, int seq, int start, int len,
+                                              uint32_t* lkeys, const GenericSmem& gs,
+                                              uint32_t& kmin, uint32_t& kmax) {
   const int H = p.H, D = p.D;
   for (int i = threadIdx.x; i < len; i += NT) {
     const int64_t row = pool_row(p.L, seq, start + i);
@@ -165,187 +368,658 @@ __device__ void score_generic(const IndexerParams& p, int seq, int start, int le
         x = fma((double)gs.q[h * D + d], (double)load_elem(p.k_pool, p.k_dtype, row * D + d) * ks, x);
       S = fma((double)gs.w[h], fmax(x, 0.0), S);
     }
-    lkeys[i] = float_to_key((float)S);
+    const uint32_t key = float_to_key((float)S);
+    lkeys[i] = key;
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
   }
 }
 
+// Score positions [start, start+len) into L.keys; returns the smallest and largest key.
+// Ends with a workgroup barrier.
 template <int MODE>
 __device__ __forceinline__ void score_split(const IndexerParams& p, int t, int seq, int start,
-                                            int len, uint32_t* lkeys, const GenericSmem* gs) {
-  if constexpr (MODE == 1) score_mfma<false>(p, t, seq, start, len, lkeys);
-  else if constexpr (MODE == 2) score_mfma<true>(p, t, seq, start, len, lkeys);
-  else score_generic(p, seq, start, len, lkeys, *gs);
-}
-
-// ---------------------------------------------------------------------------------------
-// Radix selection over order-preserving keys
-// ---------------------------------------------------------------------------------------
-
-// Histogram of digit (key >> shift) & 255 over keys with (key & mask) == prefix.  The first
-// digit of a set of scores is nearly constant, so that pass aggregates equal digits across
-// the wave before touching LDS (one atomic per distinct digit instead of 64 on one word).
-template <class Get>
-__device__ void build_hist(Get get, int n, uint32_t prefix, uint32_t mask, int shift, int* hist,
-                           bool aggregate) {
-  for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
-  __syncthreads();
-  if (aggregate) {
-    const int lane = threadIdx.x & 63;
-    const int iters = (n + NT - 1) / NT;
-    for (int it = 0; it < iters; ++it) {
-      const int i = it * NT + threadIdx.x;
-      bool m = false;
-      int bin = 0;
-      if (i < n) {
-        const uint32_t k = get(i);
-        m = (k & mask) == prefix;
-        bin = (int)((k >> shift) & 255u);
-      }
-      uint64_t todo = __ballot(m);
-      while (todo) {
-        const int leader = __builtin_ctzll(todo);
-        const int lb = __shfl(bin, leader, 64);
-        const uint64_t grp = __ballot(m && bin == lb) & todo;
-        if (lane == leader) atomicAdd(&hist[lb], __popcll(grp));
-        todo &= ~grp;
-      }
-    }
+                                            int len, const Lds& L, const GenericSmem* gs,
+                                            uint32_t& lo, uint32_t& hi) {
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  if constexpr (MODE == 0) {
+    score_generic(p, seq, start, len, L.keys, *gs, kmin, kmax);
   } else {
-    for (int i = threadIdx.x; i < n; i += NT) {
-      const uint32_t k = get(i);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
-    }
+    // wave-uniform values kept in scalar registers
+    t = __builtin_amdgcn_readfirstlane(t);
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    start = __builtin_amdgcn_readfirstlane(start);
+    len = __builtin_amdgcn_readfirstlane(len);
+    if (p.L.bt) score_mfma<MODE == 2, true, MODE>(p, t, seq, start, len, L, kmin, kmax);
+    else score_mfma<MODE == 2, false, MODE>(p, t, seq, start, len, L, kmin, kmax);
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if ((threadIdx.x & 63) == 0) {
+    L.range[threadIdx.x >> 6] = kmin;
+    L.range[NWAVE + (threadIdx.x >> 6)] = kmax;
   }
   __syncthreads();
+  lo = 0xffffffffu;
+  hi = 0u;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    lo = min(lo, L.range[w]);
+    hi = max(hi, L.range[NWAVE + w]);
+  }
 }
 
-// Bin d holding the r-th largest (1-based) counted key: above(d) < r <= above(d) + hist[d],
-// above(d) = number of counted keys in bins > d.  res = {d, above(d), hist[d]}.
-__device__ void radix_find(const int* hist, int r, int* res) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int c[4], loc = 0;
+// ---------------------------------------------------------------------------------------
+// Radix selection over order-preserving keys, with digits fitted to the keys' range.
+// A pass counts the keys in [base, base + width] by the digit (key - base) >> sh, where sh
+// is the smallest shift that maps the whole range onto kBins bins.  Fitting the range
+// spreads a set of near-equal top scores over many bins instead of the few bins that the
+// keys' leading bits would give them, so the LDS histogram atomics rarely collide.  Once the
+// bin holding the wanted rank is known, its few keys are gathered and ranked directly.
+// The keys are keys[0, n), in LDS or global memory.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int range_shift(uint32_t width) {
+  const int bits = width ? 32 - __clz((int)width) : 0;
+  return max(0, bits - 11);
+}
+
+// Smallest and largest key over the workgroup.
+__device__ __forceinline__ void key_range(const uint32_t* keys, int n, const Lds& L,
+                                          uint32_t& lo, uint32_t& hi) {
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = keys[min(i0 + u * NT, n - 1)];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      c[u] = hist[255 - 4 * lane - u];
-      loc += c[u];
-    }
-    int above = wave_inclusive_scan(loc) - loc;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (above < r && r <= above + c[u]) {
-        res[0] = 255 - 4 * lane - u;
-        res[1] = above;
-        res[2] = c[u];
-      }
-      above += c[u];
+      mn = min(mn, k[u]);
+      mx = max(mx, k[u]);
     }
   }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    L.range[wave] = mn;
+    L.range[NWAVE + wave] = mx;
+  }
   __syncthreads();
+  lo = 0xffffffffu;
+  hi = 0u;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    lo = min(lo, L.range[w]);
+    hi = max(hi, L.range[NWAVE + w]);
+  }
 }
 
-// The k-th largest key (1 <= k <= n) and the number of keys strictly above it.
-template <class Get>
-__device__ void radix_kth(Get get, int n, int k, Smem& sm, uint32_t& T, int& gt) {
-  uint32_t prefix = 0, mask = 0;
+// Bin of rank r (1-based, counted from the largest key) in a histogram over [base, base+width]
+// with shift sh: fills the histogram, then finds bin d with above(d) < r <= above(d) +
+// hist[d], where above(d) counts the keys in bins above d.  Every wave finds the same
+// result, so no barrier is needed to share it.
+struct BinPick { int d, above, c; };
+__device__ __forceinline__ BinPick find_in_hist(int r, const Lds& L);
+__device__ __forceinline__ BinPick rank_bin(const uint32_t* keys, int n, uint32_t base,
+                                            uint32_t width, int sh, int r, const Lds& L) {
+  int* hist = L.hist;
+  __syncthreads();   // earlier readers of the histogram are done
+  for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+    uint32_t o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = keys[min(i0 + u * NT, n - 1)] - base;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * NT < n && o[u] <= width) atomicAdd(&hist[o[u] >> sh], 1);
+  }
+  __syncthreads();
+  return find_in_hist(r, L);
+}
+
+// Bin of rank r in the filled histogram L.hist (see rank_bin).  Starts and ends with
+// workgroup-wide steps only where noted: one barrier after the partial sums.
+__device__ __forceinline__ BinPick find_in_hist(int r, const Lds& L) {
+  const int* hist = L.hist;
+  int* psum = L.psum;
+  {
+    // thread i: the sum of bins [8i, 8i + 8)
+    const int4 v0 = *(const int4*)(hist + 8 * threadIdx.x);
+    const int4 v1 = *(const int4*)(hist + 8 * threadIdx.x + 4);
+    psum[threadIdx.x] = v0.x + v0.y + v0.z + v0.w + v1.x + v1.y + v1.z + v1.w;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  // level 1: lane l holds 32-bin group 63 - l (descending)
+  const int4 q = *(const int4*)(psum + 4 * (63 - lane));
+  const int c1 = q.x + q.y + q.z + q.w;
+  const int s1 = wave_scan_add(c1);
+  const uint64_t b1 = __ballot(s1 >= r);
+  const int l1 = b1 ? __builtin_ctzll(b1) : 63;
+  const int grp = 63 - l1;
+  const int above1 = __builtin_amdgcn_readlane(s1 - c1, l1);
+  // level 2: lane l < 32 holds bin 32*grp + 31 - l
+  const int c2 = lane < 32 ? hist[32 * grp + 31 - lane] : 0;
+  const int s2 = wave_scan_add(c2);
+  const uint64_t b2 = __ballot(s2 >= r - above1);
+  const int l2 = b2 ? __builtin_ctzll(b2) : 31;
+  BinPick bp;
+  bp.d = 32 * grp + 31 - l2;
+  bp.above = above1 + __builtin_amdgcn_readlane(s2 - c2, l2);
+  bp.c = __builtin_amdgcn_readlane(c2, l2);
+  return bp;
+}
+
+// The k-th largest key T (1 <= k <= n), the number of keys above it (gt) and the number at
+// or above it (ge); every key lies in [lo, hi].
+struct Kth { uint32_t T; int gt, ge; };
+__device__ __forceinline__ Kth radix_kth(const uint32_t* keys, int n, int k, uint32_t lo,
+                                         uint32_t hi, const Lds& L) {
+  uint32_t base = lo, width = hi - lo;
   int above = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    build_hist(get, n, prefix, mask, shift, sm.hist, pass == 0);
-    radix_find(sm.hist, k - above, sm.res);
-    const int d = sm.res[0], a = sm.res[1];
-    above += a;
-    prefix |= (uint32_t)d << shift;
-    mask |= 0xffu << shift;
+  for (;;) {
+    const int sh = range_shift(width);
+    const BinPick bp = rank_bin(keys, n, base, width, sh, k - above, L);
+    base += (uint32_t)bp.d << sh;
+    if (sh == 0) return Kth{base, above + bp.above, above + bp.above + bp.c};
+    width = (1u << sh) - 1u;
+    if (bp.c <= 64) {
+      // gather the c keys of the bin and rank them within one wave
+      uint32_t* small = L.small;
+      if (threadIdx.x == 0) L.bcast[3] = 0;
+      __syncthreads();
+      for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kk[u] = keys[min(i0 + u * NT, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool in = i0 + u * NT < n && kk[u] - base <= width;
+          const uint64_t bl = __ballot(in);
+          if (bl) {
+            int at = 0;
+            if ((threadIdx.x & 63) == 0) at = atomicAdd(&L.bcast[3], __popcll(bl));
+            at = __builtin_amdgcn_readfirstlane(at);
+            if (in) small[at + __popcll(bl & ((1ull << (threadIdx.x & 63)) - 1ull))] = kk[u];
+          }
+        }
+      }
+      __syncthreads();
+      const int lane = threadIdx.x & 63, c = bp.c, r = k - above - bp.above;
+      const uint32_t v = lane < c ? small[lane] : 0u;
+      int gt = 0, ge = 0;
+      for (int j = 0; j < c; ++j) {
+        const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+        gt += w > v;
+        ge += w >= v;
+      }
+      const uint64_t hit = __ballot(lane < c && gt < r && r <= ge);
+      const int l = __builtin_ctzll(hit);
+      const int a = above + bp.above;
+      return Kth{(uint32_t)__builtin_amdgcn_readlane((int)v, l),
+                 a + __builtin_amdgcn_readlane(gt, l), a + __builtin_amdgcn_readlane(ge, l)};
+    }
+    above += bp.above;
   }
-  T = prefix;
-  gt = above;
 }
 
 // A threshold key tau such that the count of keys >= tau is at least m when possible and
-// at most `hard`, preferably at most `soft`.  Returns tau and that count.
-__device__ void local_threshold(const uint32_t* keys, int n, int m, int soft, int hard, Smem& sm,
-                                uint32_t& tau, int& count) {
-  auto get = [&](int i) { return keys[i]; };
-  uint32_t prefix = 0, mask = 0;
-  int above = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    build_hist(get, n, prefix, mask, shift, sm.hist, pass == 0);
-    radix_find(sm.hist, m - above, sm.res);
-    const int d = sm.res[0], a = sm.res[1], c = sm.res[2];
-    const int tot = above + a + c;
-    const uint32_t edge = prefix | ((uint32_t)d << shift);
-    if (tot <= soft || (pass == 3 && tot <= hard)) {
-      tau = edge;
-      count = tot;
-      return;
+// at most `hard`, preferably at most `soft`; every key lies in [lo, hi].  Returns tau and
+// that count.
+__device__ __forceinline__ void local_threshold(const uint32_t* keys, int n, int m, int soft,
+                                                int hard, uint32_t lo, uint32_t hi, const Lds& L,
+                                                uint32_t& tau, int& count) {
+  const int sh = range_shift(hi - lo);
+  const BinPick bp = rank_bin(keys, n, lo, hi - lo, sh, m, L);
+  const int tot = bp.above + bp.c;
+  if (tot <= soft) {
+    tau = lo + ((uint32_t)bp.d << sh);
+    count = tot;
+    return;
+  }
+  // the bin at the cut is crowded: cut at the exact m-th key instead
+  __syncthreads();
+  const Kth kt = radix_kth(keys, n, m, lo, hi, L);
+  if (kt.ge <= hard) {
+    tau = kt.T;
+    count = kt.ge;
+  } else {
+    tau = kt.T + 1u;   // too many keys equal the m-th: keep only those above it
+    count = kt.gt;
+  }
+}
+
+// Stable selection of keys[0, n) in index order, one contiguous run per wave with ballot
+// compaction: key i is taken if key > T, or key == T and fewer than `need` earlier keys equal
+// to T were taken.  out(slot, i, key) for each taken key.  Each pass reads four 64-key
+// chunks at once.
+template <class Out>
+__device__ __forceinline__ void emit_sel(const uint32_t* keys, int n, uint32_t T, int need,
+                                         Out out, const Lds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = ((n + NWAVE * 64 - 1) / (NWAVE * 64)) * 64;
+  const int lo = min(n, wave * chunk), hi = min(n, lo + chunk);
+  int gt = 0, eq = 0;
+  for (int i0 = lo; i0 < hi; i0 += 256) {
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = keys[min(i0 + 64 * u + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = i0 + 64 * u + lane < hi;
+      gt += __popcll(__ballot(in && k[u] > T));
+      eq += __popcll(__ballot(in && k[u] == T));
     }
-    above += a;
-    prefix = edge;
-    mask |= 0xffu << shift;
   }
-  // One value v = prefix holds too many equal keys: keep only the keys above it.
-  tau = prefix + 1u;
-  count = above;
+  if (lane == 0) {
+    L.wcnt[wave] = gt;
+    L.wcnt[NWAVE + wave] = eq;
+  }
+  __syncthreads();
+  int eq_base = 0, slot = 0;
+  for (int w = 0; w < wave; ++w) {
+    const int e = L.wcnt[NWAVE + w];
+    slot += L.wcnt[w] + max(0, min(e, need - eq_base));
+    eq_base += e;
+  }
+  __syncthreads();
+  for (int i0 = lo; i0 < hi; i0 += 256) {
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = keys[min(i0 + 64 * u + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 64 * u + lane;
+      const bool in = i < hi;
+      const bool is_eq = in && k[u] == T;
+      const uint64_t eqb = __ballot(is_eq);
+      const int eq_rank = eq_base + __popcll(eqb & ((1ull << lane) - 1ull));
+      const bool take = (in && k[u] > T) || (is_eq && eq_rank < need);
+      const uint64_t tb = __ballot(take);
+      if (take) out(slot + __popcll(tb & ((1ull << lane) - 1ull)), i, k[u]);
+      slot += __popcll(tb);
+      eq_base += __popcll(eqb);
+    }
+  }
 }
 
-// Stable selection in index order: element i is taken if key > T, or key == T and fewer than
-// `need` earlier elements equal to T were taken.  out(slot, i, key) for each taken element.
-template <class Get, class Out>
-__device__ void emit(Get get, int n, uint32_t T, int need, Out out, Smem& sm) {
-  const int E = (n + NT - 1) / NT;
-  const int lo = min(n, (int)threadIdx.x * E), hi = min(n, lo + E);
+// ---------------------------------------------------------------------------------------
+// Selection over keys held in registers: thread i holds the contiguous block of keys
+// [E*i, E*i + E) of an LDS array (missing keys read as 0, below every real key), so every
+// pass after the one LDS read works from registers, and a stable selection in index order
+// needs only two workgroup scans.
+// ---------------------------------------------------------------------------------------
+// Exclusive scan of one int per thread over the workgroup (DPP within each wave); buf
+// alternates between two halves of L.scan so that back-to-back scans need one barrier each.
+__device__ __forceinline__ int wg_scan(int v, int buf, const Lds& L, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_scan_add(v);
+  int* sc = L.scan + buf * NWAVE;
+  if (lane == 63) sc[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    const int c = sc[w];
+    before += w < wave ? c : 0;
+    total += c;
+  }
+  return before + incl - v;
+}
+
+template <int E>
+struct KeyBlock {
+  static_assert(E % 4 == 0, "whole 16-byte reads");
+  uint32_t k[E];
+  int base, cnt;
+  // keys[] must be 16-byte aligned and readable up to index E * NT.
+  __device__ __forceinline__ void load(const uint32_t* keys, int n) {
+    base = threadIdx.x * E;
+    cnt = max(0, min(E, n - base));
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const u32x4 v = *(const u32x4*)(keys + base + e);
+      k[e] = v.x;
+      k[e + 1] = v.y;
+      k[e + 2] = v.z;
+      k[e + 3] = v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) k[e] = e < cnt ? k[e] : 0u;
+  }
+};
+
+// Smallest and largest key of the block set (at least one key).
+template <int E>
+__device__ __forceinline__ void block_range(const KeyBlock<E>& b, const Lds& L, uint32_t& lo,
+                                            uint32_t& hi) {
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    mn = min(mn, e < b.cnt ? b.k[e] : 0xffffffffu);
+    mx = max(mx, b.k[e]);
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    L.range[wave] = mn;
+    L.range[NWAVE + wave] = mx;
+  }
+  __syncthreads();
+  lo = 0xffffffffu;
+  hi = 0u;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    lo = min(lo, L.range[w]);
+    hi = max(hi, L.range[NWAVE + w]);
+  }
+}
+
+// rank_bin over the block's keys; base must be above 0 (missing keys are 0).
+template <int E>
+__device__ __forceinline__ BinPick block_rank_bin(const KeyBlock<E>& b, uint32_t base,
+                                                  uint32_t width, int sh, int r, const Lds& L) {
+  int* hist = L.hist;
+  __syncthreads();   // earlier readers of the histogram are done
+  for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t o = b.k[e] - base;
+    if (o <= width) atomicAdd(&hist[o >> sh], 1);
+  }
+  __syncthreads();
+  return find_in_hist(r, L);
+}
+
+// The k-th largest key of the block set, with the counts above and at-or-above it.
+template <int E>
+__device__ __forceinline__ Kth block_kth(const KeyBlock<E>& b, int k, uint32_t lo, uint32_t hi,
+                                         const Lds& L) {
+  uint32_t base = lo, width = hi - lo;
+  int above = 0;
+  for (;;) {
+    const int sh = range_shift(width);
+    const BinPick bp = block_rank_bin(b, base, width, sh, k - above, L);
+    base += (uint32_t)bp.d << sh;
+    if (sh == 0) return Kth{base, above + bp.above, above + bp.above + bp.c};
+    width = (1u << sh) - 1u;
+    if (bp.c <= 64) {
+      // gather the c keys of the bin and rank them within one wave
+      const int lane = threadIdx.x & 63;
+      if (threadIdx.x == 0) L.bcast[3] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool in = b.k[e] - base <= width;
+        const uint64_t bl = __ballot(in);
+        if (bl) {
+          int at = 0;
+          if (lane == 0) at = atomicAdd(&L.bcast[3], __popcll(bl));
+          at = __builtin_amdgcn_readfirstlane(at);
+          if (in) L.small[at + __popcll(bl & ((1ull << lane) - 1ull))] = b.k[e];
+        }
+      }
+      __syncthreads();
+      const int c = bp.c, r = k - above - bp.above;
+      const uint32_t v = lane < c ? L.small[lane] : 0u;
+      int gt = 0, ge = 0;
+      for (int j = 0; j < c; ++j) {
+        const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+        gt += w > v;
+        ge += w >= v;
+      }
+      const uint64_t hit = __ballot(lane < c && gt < r && r <= ge);
+      const int l = __builtin_ctzll(hit);
+      const int a = above + bp.above;
+      return Kth{(uint32_t)__builtin_amdgcn_readlane((int)v, l),
+                 a + __builtin_amdgcn_readlane(gt, l), a + __builtin_amdgcn_readlane(ge, l)};
+    }
+    above += bp.above;
+  }
+}
+
+// Stable selection in index order: key i is taken if key > T, or key == T and fewer than
+// `need` earlier keys equal to T were taken.  out(slot, i, key) for each taken key.
+template <int E, class Out>
+__device__ __forceinline__ void block_emit(const KeyBlock<E>& b, uint32_t T, int need, Out out,
+                                           const Lds& L) {
   int eq = 0;
-  for (int i = lo; i < hi; ++i) eq += get(i) == T;
-  int tot;
-  const int eq_base = wg_exclusive_scan<NT>(eq, sm.scan, &tot);
+#pragma unroll
+  for (int e = 0; e < E; ++e) eq += b.k[e] == T;
+  int total;
+  const int eq_base = wg_scan(eq, 0, L, total);
   int sel = 0, r = eq_base;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t k = get(i);
-    if (k > T) ++sel;
-    else if (k == T) { sel += r < need; ++r; }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (b.k[e] > T) ++sel;
+    else if (b.k[e] == T) { sel += r < need; ++r; }
   }
-  int slot = wg_exclusive_scan<NT>(sel, sm.scan, &tot);
+  int slot = wg_scan(sel, 1, L, total);
   r = eq_base;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t k = get(i);
-    bool take = false;
-    if (k > T) take = true;
-    else if (k == T) { take = r < need; ++r; }
-    if (take) out(slot++, i, k);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    bool take = b.k[e] > T;
+    if (b.k[e] == T) { take = r < need; ++r; }
+    if (take) out(slot++, b.base + e, b.k[e]);
   }
 }
 
-__device__ void pad_output(const IndexerParams& p, int t, int from) {
+__device__ __forceinline__ void pad_output(const IndexerParams& p, int t, int from) {
   for (int s = from + (int)threadIdx.x; s < p.K; s += NT) {
     p.out_idx[(size_t)t * p.K + s] = -1;
     if (p.out_score) p.out_score[(size_t)t * p.K + s] = 0.f;
   }
 }
 
-// Exact local Top-kk of the split scores in LDS, written to the candidate slots of split j.
-__device__ void split_exact_candidates(const IndexerParams& p, int t, int j, int start, int len,
-                                       int kk, Smem& sm) {
-  auto lget = [&](int i) { return sm.keys[i]; };
-  uint32_t T;
-  int gt;
-  radix_kth(lget, len, kk, sm, T, gt);
-  const size_t cb = ((size_t)t * p.nsplit_max + j) * p.cap;
-  emit(lget, len, T, kk - gt,
-       [&](int slot, int i, uint32_t k) {
-         p.cand_key[cb + slot] = k;
-         p.cand_pos[cb + slot] = start + i;
-       },
-       sm);
+// ---------------------------------------------------------------------------------------
+// Merge of a query's split candidates (run by the last split to arrive)
+// ---------------------------------------------------------------------------------------
+
+// Split headers -> LDS (emitted counts as offsets, thresholds); returns the candidate total.
+__device__ __forceinline__ int load_headers(const IndexerParams& p, int t, int nsplit, const Lds& L) {
+  constexpr int PER = kNSplitMax / NT;
+  const uint32_t* hdr = p.hdr + (size_t)t * p.nsplit_max * 2;
+  int c[PER], loc = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int jj = threadIdx.x * PER + u;
+    c[u] = 0;
+    if (jj < nsplit) {
+      c[u] = (int)ld_agent(hdr + 2 * jj);
+      L.seg_tau[jj] = ld_agent(hdr + 2 * jj + 1);
+    }
+    loc += c[u];
+  }
+  int N;
+  int base = wg_exclusive_scan<NT>(loc, L.scan, &N);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int jj = threadIdx.x * PER + u;
+    if (jj < nsplit) L.seg_off[jj] = base;
+    base += c[u];
+  }
+  if (threadIdx.x == 0) L.seg_off[nsplit] = N;
+  __syncthreads();
+  return N;
+}
+
+// last split whose candidates start at or before flat index i
+__device__ __forceinline__ int split_of(const Lds& L, int nsplit, int i) {
+  int a = 0, b = nsplit - 1;
+  while (a < b) {
+    const int mid = (a + b + 1) >> 1;
+    if (L.seg_off[mid] <= i) a = mid; else b = mid - 1;
+  }
+  return a;
+}
+
+// Exact selection over the flat candidate keys fk[0, N) and the output.  pos_of(i) gives
+// the position of flat candidate i.  Returns false (and writes nothing) when a split's
+// threshold lies above the K_eff-th key T.
+template <class PosOf>
+__device__ __forceinline__ bool select_output(const IndexerParams& p, int t, int K_eff,
+                                              int nsplit, int N, const uint32_t* fk, PosOf pos_of,
+                                              const Lds& L, uint32_t& T, int& gt, bool& enough) {
+  enough = N >= K_eff;
+  T = 0u;
+  gt = 0;
+  if (enough) {
+    uint32_t lo, hi;
+    key_range(fk, N, L, lo, hi);
+    const Kth kt = radix_kth(fk, N, K_eff, lo, hi, L);
+    T = kt.T;
+    gt = kt.gt;
+  }
+  int bad = 0;
+  for (int jj = threadIdx.x; jj < nsplit; jj += NT)
+    bad |= enough ? (L.seg_tau[jj] > T) : (L.seg_tau[jj] != 0u);
+  if (__syncthreads_or(bad)) return false;
+  // flat index of each output slot -> hist (free after the selection)
+  int* sel = L.hist;
+  emit_sel(fk, N, T, K_eff - gt, [&](int slot, int i, uint32_t) { if (slot < K_eff) sel[slot] = i; }, L);
+  __syncthreads();
+  // positions and scores of the selection, all loads in flight together
+  constexpr int U = kMaxTopK / NT;
+  int32_t pos[U];
+  uint32_t key[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = sel[min((int)threadIdx.x + u * NT, K_eff - 1)];
+    pos[u] = pos_of(i);
+    key[u] = fk[i];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int s = threadIdx.x + u * NT;
+    if (s < K_eff) {
+      p.out_idx[(size_t)t * p.K + s] = pos[u];
+      if (p.out_score) p.out_score[(size_t)t * p.K + s] = key_to_float(key[u]);
+    }
+  }
+  pad_output(p, t, K_eff);
+  if (threadIdx.x == 0) st_agent(&p.counters[t], 0u);
+  return true;
+}
+
+// Gathers the N candidates into flat arrays in split order (= position order) and selects.
+// When keys and positions fit in LDS they come with direct-to-LDS loads (one memory round
+// trip); otherwise the keys go through the workspace and the positions are fetched for the
+// selected candidates only.  T, gt and enough are kept for the re-scoring of failing splits.
+template <int MODE>
+__device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, int nsplit, int N,
+                                      const Lds& L, uint32_t& T, int& gt, bool& enough) {
+  const size_t qbase = (size_t)t * p.nsplit_max * p.cap;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int HALF = flat_capacity<MODE>() / 2;
+  if (N <= HALF) {
+    uint32_t* fk = L.flat;
+    int32_t* fp = (int32_t*)(L.flat + HALF);
+    const uint32_t kb = lds_addr(fk), pb = lds_addr(fp);
+#pragma unroll 1
+    for (int j = wave; j < nsplit; j += NWAVE) {
+      const int o = L.seg_off[j], cnt = L.seg_off[j + 1] - o;
+      const size_t src = qbase + (size_t)j * p.cap;
+#pragma unroll 1
+      for (int c = 0; c < cnt; c += 64) {
+        if (lane < cnt - c) {
+          load_to_lds<4, true>(p.cand_key + src + c, 4u * lane, kb + 4u * (o + c));
+          load_to_lds<4, true>(p.cand_pos + src + c, 4u * lane, pb + 4u * (o + c));
+        }
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    KeyBlock<(HALF + NT - 1) / NT / 4 * 4 + 4> fb;
+    fb.load(fk, N);
+    enough = N >= K_eff;
+    T = 0u;
+    gt = 0;
+    if (enough) {
+      uint32_t lo, hi;
+      block_range(fb, L, lo, hi);
+      const Kth kt = block_kth(fb, K_eff, lo, hi, L);
+      T = kt.T;
+      gt = kt.gt;
+    }
+    int bad = 0;
+    for (int jj = threadIdx.x; jj < nsplit; jj += NT)
+      bad |= enough ? (L.seg_tau[jj] > T) : (L.seg_tau[jj] != 0u);
+    if (__syncthreads_or(bad)) return false;
+    block_emit(fb, T, K_eff - gt,
+               [&](int slot, int i, uint32_t k) {
+                 if (slot < K_eff) {
+                   p.out_idx[(size_t)t * p.K + slot] = fp[i];
+                   if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(k);
+                 }
+               },
+               L);
+    pad_output(p, t, K_eff);
+    if (threadIdx.x == 0) st_agent(&p.counters[t], 0u);
+    return true;
+  }
+  uint32_t* g = p.flat_key + qbase;
+  constexpr int B = 8;
+#pragma unroll 1
+  for (int i0 = threadIdx.x; i0 < N; i0 += B * NT) {
+    uint32_t v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = min(i0 + u * NT, N - 1);
+      const int jj = split_of(L, nsplit, i);
+      v[u] = ld_agent(p.cand_key + qbase + (size_t)jj * p.cap + (i - L.seg_off[jj]));
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (i0 + u * NT < N) g[i0 + u * NT] = v[u];
+  }
+  __threadfence();
+  __syncthreads();
+  return select_output(p, t, K_eff, nsplit, N, g,
+                       [&](int i) {
+                         const int jj = split_of(L, nsplit, i);
+                         return ld_agent(p.cand_pos + qbase + (size_t)jj * p.cap + (i - L.seg_off[jj]));
+                       },
+                       L, T, gt, enough);
 }
 
 // ---------------------------------------------------------------------------------------
-// Kernel
+// Kernel.  The scorer has one call site: the loop first scores this workgroup's own split;
+// only the merging workgroup of a query whose split thresholds failed to certify comes back
+// to it, to re-score each failing split and take its exact local Top-K.
 // ---------------------------------------------------------------------------------------
 template <int MODE>
-__global__ __launch_bounds__(NT) void indexer_topk_kernel(IndexerParams p) {
-  __shared__ Smem sm;
+__global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
+  constexpr int RB = region_bytes<MODE>();
+  static_assert(RB >= kBins * 4 && flat_capacity<MODE>() >= 4096, "shared region");
+  __shared__ __attribute__((aligned(16))) uint8_t s_region[RB];
+  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSplitMax];
+  __shared__ __attribute__((aligned(16))) float s_w[NWAVE * 64];
+  __shared__ int s_res[4], s_scan[2 * NWAVE + 2], s_wcnt[2 * NWAVE], s_bcast[4];
+  __shared__ uint32_t s_range[2 * NWAVE];
+  __shared__ __attribute__((aligned(16))) int s_psum[NT];
+  __shared__ uint32_t s_small[64];
+  Lds L;
+  L.keys = s_keys;
+  L.w = s_w;
+  L.region = s_region;
+  L.hist = (int*)s_region;                         // while selecting a split's candidates
+  L.seg_off = (int*)s_region;                      // while merging (hist then moves to s_keys)
+  L.seg_tau = (uint32_t*)(s_region + kSegOffBytes);
+  L.flat = (uint32_t*)(s_region + kFlatOffset);
+  L.res = s_res;
+  L.scan = s_scan;
+  L.wcnt = s_wcnt;
+  L.bcast = s_bcast;
+  L.range = s_range;
+  L.psum = s_psum;
+  L.small = s_small;
+  Lds Lm = L;
+  Lm.hist = (int*)s_keys;
+
   const int t = blockIdx.y, j = blockIdx.x;
   const int V = min(p.q_vis[t], p.max_visible);
   if (V <= 0) {
@@ -356,7 +1030,6 @@ __global__ __launch_bounds__(NT) void indexer_topk_kernel(IndexerParams p) {
   if (j >= nsplit) return;
   const int seq = p.q_seq[t];
   const int K_eff = min(p.K, V);
-  const int start = j * p.split, len = min(p.split, V - start);
 
   const GenericSmem* gsp = nullptr;
   if constexpr (MODE == 0) {
@@ -365,158 +1038,120 @@ __global__ __launch_bounds__(NT) void indexer_topk_kernel(IndexerParams p) {
     for (int i = threadIdx.x; i < HD; i += NT)
       gs.q[i] = load_elem(p.q, p.q_dtype, (int64_t)t * HD + i);
     for (int i = threadIdx.x; i < p.H; i += NT) gs.w[i] = p.w[(size_t)t * p.H + i];
-    __syncthreads();
     gsp = &gs;
   }
-
-  score_split<MODE>(p, t, seq, start, len, sm.keys, gsp);
   __syncthreads();
-  auto lget = [&](int i) { return sm.keys[i]; };
 
-  if (nsplit == 1) {
-    uint32_t T;
-    int gt;
-    radix_kth(lget, len, K_eff, sm, T, gt);
-    emit(lget, len, T, K_eff - gt,
-         [&](int slot, int i, uint32_t k) {
-           p.out_idx[(size_t)t * p.K + slot] = start + i;
-           if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(k);
-         },
-         sm);
-    pad_output(p, t, K_eff);
-    return;
-  }
+  int cur = j;            // split to score
+  bool refill = false;    // re-scoring failing splits for this query's merge
+  uint32_t T = 0u;
+  int gt = 0, N = 0;
+  bool enough = false;
+  for (;;) {
+    const int start = cur * p.split, len = min(p.split, V - start);
+    uint32_t klo, khi;
+    score_split<MODE>(p, t, seq, start, len, L, gsp, klo, khi);
 
-  // ---- candidates of this split --------------------------------------------------------
-  {
-    const float e = (float)K_eff * (float)len / (float)V;
-    int m = (int)ceilf(e + 4.f * sqrtf(e) + 4.f);
-    const int hard = min(len, p.cap);
-    m = min(m, hard);
-    const int soft = min(hard, 2 * m);
-    uint32_t tau = 0u;
-    int cnt = len;
-    if (m < len) local_threshold(sm.keys, len, m, soft, hard, sm, tau, cnt);
-    else tau = 0u;       // everything fits: all keys are >= 0
-    const size_t cb = ((size_t)t * p.nsplit_max + j) * p.cap;
-    emit(lget, len, tau, 0x7fffffff,
-         [&](int slot, int i, uint32_t k) {
-           if (slot < p.cap) {
-             p.cand_key[cb + slot] = k;
-             p.cand_pos[cb + slot] = start + i;
-           }
-         },
-         sm);
-    if (threadIdx.x == 0) {
-      uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + j) * 2;
-      h[0] = (uint32_t)min(cnt, p.cap);
-      h[1] = tau;
-    }
-  }
-
-  // ---- arrival: the last split of this query merges --------------------------------------
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    sm.bcast[0] = atomicAdd(&p.counters[t], 1u) == (uint32_t)(nsplit - 1);
-  __syncthreads();
-  if (!sm.bcast[0]) return;
-  __threadfence();
-
-  const uint32_t* hdr = p.hdr + (size_t)t * p.nsplit_max * 2;
-  const size_t qbase = (size_t)t * p.nsplit_max * p.cap;
-  uint32_t* fk = p.flat_key + qbase;
-  int32_t* fpos = p.flat_pos + qbase;
-
-  for (int round = 0; round < 2; ++round) {
-    // split headers -> LDS, candidate offsets
-    int c[4], loc = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int jj = threadIdx.x * 4 + u;
-      c[u] = 0;
-      if (jj < nsplit) {
-        c[u] = (int)__builtin_nontemporal_load(hdr + 2 * jj);
-        sm.seg_tau[jj] = __builtin_nontemporal_load(hdr + 2 * jj + 1);
+    if (!refill) {
+      if (nsplit == 1) {
+        const Kth kt = radix_kth(L.keys, len, K_eff, klo, khi, L);
+        emit_sel(L.keys, len, kt.T, K_eff - kt.gt,
+                 [&](int slot, int i, uint32_t k) {
+                   if (slot < K_eff) {
+                     p.out_idx[(size_t)t * p.K + slot] = start + i;
+                     if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(k);
+                   }
+                 },
+                 L);
+        pad_output(p, t, K_eff);
+        return;
       }
-      loc += c[u];
-    }
-    int N;
-    int base = wg_exclusive_scan<NT>(loc, sm.scan, &N);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int jj = threadIdx.x * 4 + u;
-      if (jj < nsplit) sm.seg_off[jj] = base;
-      base += c[u];
-    }
-    if (threadIdx.x == 0) sm.seg_off[nsplit] = N;
-    __syncthreads();
-
-    // gather the candidates into one flat array (split order = position order)
-    {
-      const int E = (N + NT - 1) / NT;
-      const int lo = min(N, (int)threadIdx.x * E), hi = min(N, lo + E);
-      if (lo < hi) {
-        int a = 0, b = nsplit - 1;      // last split with seg_off <= lo
-        while (a < b) {
-          const int mid = (a + b + 1) >> 1;
-          if (sm.seg_off[mid] <= lo) a = mid; else b = mid - 1;
+      // candidates of this split: every key at or above a threshold chosen so that a little
+      // more than the split's expected share e of the Top-K survives
+      {
+        const float e = (float)K_eff * (float)len / (float)V;
+        int m = (int)ceilf(e + 4.f * sqrtf(e) + 4.f);
+        const int hard = min(len, p.cap);
+        m = min(m, hard);
+        const int soft = min(hard, 2 * m);
+        KeyBlock<kSplitMax / NT> kb;
+        kb.load(L.keys, len);
+        uint32_t tau = 0u;
+        int cnt = len;
+        if (m < len) {
+          const int sh = range_shift(khi - klo);
+          const BinPick bp = block_rank_bin(kb, klo, khi - klo, sh, m, L);
+          tau = klo + ((uint32_t)bp.d << sh);
+          cnt = bp.above + bp.c;
+          if (cnt > soft) {
+            // the bin at the cut is crowded: cut at the exact m-th key instead
+            const Kth kt = block_kth(kb, m, klo, khi, L);
+            tau = kt.ge <= hard ? kt.T : kt.T + 1u;   // too many equal keys: only those above
+            cnt = kt.ge <= hard ? kt.ge : kt.gt;
+          }
         }
-        int jj = a;
-        for (int i = lo; i < hi; ++i) {
-          while (i >= sm.seg_off[jj + 1]) ++jj;
-          const size_t src = qbase + (size_t)jj * p.cap + (i - sm.seg_off[jj]);
-          fk[i] = __builtin_nontemporal_load(p.cand_key + src);
-          fpos[i] = __builtin_nontemporal_load(p.cand_pos + src);
+        const size_t cb = ((size_t)t * p.nsplit_max + cur) * p.cap;
+        block_emit(kb, tau, 0x7fffffff,
+                   [&](int slot, int i, uint32_t k) {
+                     if (slot < p.cap) {
+                       st_agent(p.cand_key + cb + slot, k);
+                       st_agent(p.cand_pos + cb + slot, start + i);
+                     }
+                   },
+                   L);
+        if (threadIdx.x == 0) {
+          uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * 2;
+          st_agent(h, (uint32_t)min(cnt, p.cap));
+          st_agent(h + 1, tau);
         }
       }
+      // arrival: the last split of this query to arrive merges
+      wait_all_memory();
+      __syncthreads();
+      if (threadIdx.x == 0)
+        L.bcast[0] = __hip_atomic_fetch_add(&p.counters[t], 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1);
+      __syncthreads();
+      if (!L.bcast[0]) return;
+      N = load_headers(p, t, nsplit, Lm);
+      if (merge<MODE>(p, t, K_eff, nsplit, N, Lm, T, gt, enough)) return;
+      refill = true;
+      cur = -1;
+    } else {
+      // exact local Top-min(len, K_eff) of a failing split replaces its candidates
+      const int kk = min(len, K_eff);
+      const Kth kt = radix_kth(L.keys, len, kk, klo, khi, L);
+      const size_t cb = ((size_t)t * p.nsplit_max + cur) * p.cap;
+      emit_sel(L.keys, len, kt.T, kk - kt.gt,
+               [&](int slot, int i, uint32_t k) {
+                 if (slot < p.cap) {
+                   st_agent(p.cand_key + cb + slot, k);
+                   st_agent(p.cand_pos + cb + slot, start + i);
+                 }
+               },
+               L);
+      if (threadIdx.x == 0) {
+        uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * 2;
+        st_agent(h, (uint32_t)kk);
+        st_agent(h + 1, 0u);
+      }
     }
-    __threadfence();
+    // Next failing split, judged against the threshold the merge found.  The headers are
+    // read again from the workspace: their LDS copy shares memory with the scorer's ring.
+    int nxt = -1;
+    for (int jj = cur + 1; jj < nsplit && nxt < 0; ++jj) {
+      const uint32_t tau = ld_agent(p.hdr + ((size_t)t * p.nsplit_max + jj) * 2 + 1);
+      if (enough ? (tau > T) : (tau != 0u)) nxt = jj;
+    }
+    nxt = __builtin_amdgcn_readfirstlane(nxt);   // same value in every lane
+    wait_all_memory();
     __syncthreads();
-
-    auto fget = [&](int i) { return __builtin_nontemporal_load(fk + i); };
-    const bool enough = N >= K_eff;
-    uint32_t T = 0u;
-    int gt = 0;
-    if (enough) radix_kth(fget, N, K_eff, sm, T, gt);
-    int bad = 0;
-    for (int jj = threadIdx.x; jj < nsplit; jj += NT)
-      bad |= enough ? (sm.seg_tau[jj] > T) : (sm.seg_tau[jj] != 0u);
-    bad = __syncthreads_or(bad);
-
-    if (!bad || round == 1) {
-      emit(fget, N, T, K_eff - gt,
-           [&](int slot, int i, uint32_t k) {
-             if (slot < K_eff) {
-               p.out_idx[(size_t)t * p.K + slot] = __builtin_nontemporal_load(fpos + i);
-               if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(k);
-             }
-           },
-           sm);
-      pad_output(p, t, K_eff);
-      if (threadIdx.x == 0) p.counters[t] = 0u;
+    if (nxt < 0) {
+      N = load_headers(p, t, nsplit, Lm);
+      merge<MODE>(p, t, K_eff, nsplit, N, Lm, T, gt, enough);   // certified by construction
       return;
     }
-
-    // Fallback: splits whose threshold cut above the K_eff-th key contribute their exact
-    // local Top-K instead.
-    for (int jj = 0; jj < nsplit; ++jj) {
-      const bool fail = enough ? (sm.seg_tau[jj] > T) : (sm.seg_tau[jj] != 0u);
-      if (!fail) continue;
-      const int s0 = jj * p.split, l0 = min(p.split, V - s0);
-      __syncthreads();
-      score_split<MODE>(p, t, seq, s0, l0, sm.keys, gsp);
-      __syncthreads();
-      const int kk = min(l0, K_eff);
-      split_exact_candidates(p, t, jj, s0, l0, kk, sm);
-      if (threadIdx.x == 0) {
-        uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + jj) * 2;
-        h[0] = (uint32_t)kk;
-        h[1] = 0u;
-      }
-    }
-    __threadfence();
-    __syncthreads();
+    cur = nxt;
   }
 }
 
@@ -524,13 +1159,12 @@ __global__ __launch_bounds__(NT) void indexer_topk_kernel(IndexerParams p) {
 
 IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
   IndexerPlan pl{};
-  const int64_t target_wg = 1024;
+  int64_t target_wg = 512;
+  if (const char* e = getenv("DSA_INDEXER_TARGET_WG")) target_wg = atoll(e) > 0 ? atoll(e) : 512;
   int64_t split = ((int64_t)T * max_visible + target_wg - 1) / target_wg;
   split = (split + 63) / 64 * 64;
   if (split < 512) split = 512;
   if (split > kSplitMax) split = kSplitMax;
-  // long prefixes need larger splits to stay within kNSplitMax
-  while ((max_visible + split - 1) / split > kNSplitMax && split < kSplitMax) split += 64;
   pl.split = (int32_t)split;
   pl.nsplit_max = (int32_t)((max_visible + split - 1) / split);
   pl.cap = (int32_t)(split < top_k ? split : top_k);
@@ -542,7 +1176,6 @@ IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
   pl.off_ckey = off;     off = al(off + slots * 4);
   pl.off_cpos = off;     off = al(off + slots * 4);
   pl.off_fkey = off;     off = al(off + slots * 4);
-  pl.off_fpos = off;     off = al(off + slots * 4);
   pl.bytes = off;
   return pl;
 }

@@ -39,6 +39,9 @@ CASES = {
                                                              2048, 2049, 63, 65]),
     "bf16_k100": lambda: scaled_spec(workload(2), seq_lens=[5000, 9000, 130, 17000], top_k=100),
     "bf16_bs128": lambda: scaled_spec(workload(2), seq_lens=[12345, 3000], block_size=128),
+    # smallest page size of the MFMA path: every 32-position group is one whole page
+    "bf16_bs32": lambda: scaled_spec(workload(2), seq_lens=[4100, 2000, 31], block_size=32),
+    "fp8_bs32": lambda: scaled_spec(workload(4), seq_lens=[9000, 33], block_size=32),
     # MFMA path, fp8 keys with per-token scales
     "fp8_mixed": lambda: scaled_spec(workload(4), seq_lens=[20000, 3333, 2049, 65, 1]),
     "fp8_k256": lambda: scaled_spec(workload(4), seq_lens=[30000, 70000], top_k=256),
