@@ -140,7 +140,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
  *
  * dtype applies to q, kv_pool and out: BF16 (fp32 accumulation, MFMA) or F32 (reference
  * mode, fp32 throughout).  d_qk % 64 == 0, d_v % 64 == 0, d_v <= d_qk <= 1024,
- * 1 <= n_heads <= 1024; the BF16 path needs n_heads % 16 == 0, d_qk = 576 and d_v = 512 (the
+ * 1 <= n_heads <= 1024; the BF16 path needs n_heads % 32 == 0, d_qk = 576 and d_v = 512 (the
  * MLA latent geometry), other shapes run the reference path.  idx entries must be -1 or
  * positions whose rows exist; they need not be sorted.
  * workspace: dsa_sparse_attn_workspace_size(...) bytes, zero-filled before first use, left

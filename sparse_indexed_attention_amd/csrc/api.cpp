@@ -62,7 +62,7 @@ bool indexer_fast(dsa_dtype q_dtype, dsa_dtype k_dtype, int32_t H, int32_t D,
 }
 
 bool sfa_fast(dsa_dtype dtype, int32_t H, int32_t dqk, int32_t dv) {
-  return dtype == DSA_BF16 && dqk == kSfaDqk && dv == kSfaDv && H % 16 == 0;
+  return dtype == DSA_BF16 && dqk == kSfaDqk && dv == kSfaDv && H % 32 == 0;
 }
 
 }  // namespace
@@ -133,7 +133,7 @@ size_t dsa_sparse_attn_workspace_size(int32_t num_queries, int32_t n_heads, int3
                                       int32_t d_v) {
   if (num_queries < 1 || n_heads < 1 || top_k < 1 || d_v < 1) return 0;
   // sized for the fast path, which needs at least as much as the reference path
-  return plan_sfa(num_queries, n_heads, top_k, d_v, n_heads % 16 == 0).bytes;
+  return plan_sfa(num_queries, n_heads, top_k, d_v, n_heads % 32 == 0).bytes;
 }
 
 dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool, int32_t n_heads,
@@ -180,6 +180,7 @@ dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool, 
   p.lse = out_lse;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   p.counters = reinterpret_cast<uint32_t*>(ws + pl.off_counters);
+  p.flags = reinterpret_cast<uint32_t*>(ws + pl.off_flags);
   p.part_o = reinterpret_cast<float*>(ws + pl.off_part);
   p.part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
   const hipError_t e = launch_sfa(p, fast, static_cast<hipStream_t>(stream));

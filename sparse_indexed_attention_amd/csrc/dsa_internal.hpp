@@ -59,7 +59,7 @@ struct SfaPlan {
   int32_t n_hg;           // head groups
   int32_t rows_per_split; // selected rows per split (multiple of 32)
   int32_t nsplit;         // splits of top_k
-  size_t off_counters, off_part, off_ml, bytes;
+  size_t off_counters, off_flags, off_part, off_ml, bytes;
 };
 
 struct SfaParams {
@@ -75,6 +75,7 @@ struct SfaParams {
   void* out;              // [T, H, d_v]
   float* lse;             // [T, H] or nullptr
   uint32_t* counters;     // [T][n_hg]
+  uint32_t* flags;        // [T][H] heads to recompute by the reference method (self-clearing)
   float* part_o;          // [T][n_hg][nsplit][heads_per_wg][d_v]
   float* part_ml;         // [T][n_hg][nsplit][heads_per_wg][2]
 };

@@ -4,20 +4,30 @@
 // where R_j is the 576-wide latent row of the j-th selected position and its first 512
 // columns are the value.  SFA reads the main KV only at the indexer's positions ("Day0
 // Adaptation and Performance Optimization for Novel Long-Sequence Reasoning Models",
-// section 3); the rows are fetched a whole row at a time with 16-byte vector loads, the
-// block-wise vectorized sparse reads of "Day0 Adaptation and Sparse Attention Optimization
-// for Long-Sequence LLM Inference", section 4.
+// section 3); rows are fetched whole with 16-byte vector reads, the block-wise vectorized
+// sparse reads of "Day0 Adaptation and Sparse Attention Optimization for Long-Sequence LLM
+// Inference", section 4.
 //
-// Fast path (bf16 storage, d_qk = 576, d_v = 512): a workgroup owns (query, group of 16*NW
-// heads, slice of the index list).  Per tile of 32 selected rows it gathers the rows into LDS
-// twice: row-major for Q.K^T and transposed (dims x rows) for P.V, so both contractions
-// read 16-byte MFMA operands from LDS.  Each wave holds 16 heads: their queries stay in
-// registers (B operand), S^T = R . Q^T comes out of v_mfma_f32_16x16x32_bf16 with one head per
-// lane column, online softmax runs in the exp2 domain, and the probabilities in that same
-// lane layout are the A operand of the P.V MFMA (the row order of the transposed tile is
-// permuted to match).  O accumulates in fp32.  Slices of the index list are merged by a
-// log-sum-exp weighted combine kernel.
+// Fast path (bf16 storage, d_qk = 576, d_v = 512, heads a multiple of 32): a workgroup owns
+// (query, group of 32*NW heads, slice of the index list); every selected row is read once per
+// workgroup and serves all of its heads.
+//   * Gather: tiles of 32 rows land in LDS through direct-to-LDS loads, double-buffered (tile
+//     i+1 streams in while tile i is computed).  LDS rows are 73 sixteen-byte chunks (one of
+//     padding): with that odd stride both the MFMA reads of 16 rows at one column and the
+//     transposing reads of 4 rows x 2 chunks touch distinct banks.  The pool rows of the slice
+//     are resolved once, into LDS.
+//   * Each wave holds 32 heads.  S^T = R . Q^T on v_mfma_f32_32x32x16_bf16: tile rows are the
+//     A operand and the wave's queries (registers) the B operand, so a lane column is a head.
+//   * Online softmax in the exp2 domain; the output accumulators are rescaled only when a
+//     head's running maximum moves.
+//   * O += P . V on the same MFMA: the probabilities, in the S^T accumulator layout, are the
+//     A operand as they stand (the k order of the contraction is permuted to the rows each
+//     lane holds), and the V operand comes straight from the row-major tile through the
+//     transposing LDS read ds_read_b64_tr_b16, which gathers one dim of four rows into a lane.
+//   * Slices of the index list are merged by a log-sum-exp weighted combine kernel.
 // Reference path (fp32 storage or other shapes): one workgroup per (query, head), fp32.
+
+#include <cstdlib>
 
 #include "dsa_internal.hpp"
 
@@ -25,205 +35,268 @@ namespace dsa {
 namespace {
 
 constexpr int kTileRows = 32;
-constexpr int kRowBytes = kSfaDqk * 2;            // 1152
-constexpr int kKvStride = kRowBytes + 16;         // padded LDS row
-constexpr int kVtStride = kTileRows * 2 + 16;     // padded LDS dim-row of the transposed tile
+constexpr int kRowBytes = kSfaDqk * 2;                   // 1152
+constexpr int kRowChunks = kRowBytes / 16;               // 72 sixteen-byte chunks per row
+constexpr int kLdsChunks = kRowChunks + 1;               // LDS row stride, in chunks
+constexpr int kTileSlots = kTileRows * kLdsChunks;       // 2336
+constexpr int kTileBytes = kTileSlots * 16;              // 37376
+constexpr int kTileLoads = (kTileSlots + 63) / 64;       // 37 direct-to-LDS loads per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// slot of tile row r in the transposed tile: k-slice 8g..8g+7 of the P.V MFMA holds rows
-// 4g..4g+3 and 16+4g..16+4g+3, the rows one lane owns in the S^T accumulator layout.
-__device__ __forceinline__ int vt_slot(int r) {
-  return r < 16 ? 8 * (r >> 2) + (r & 3) : 8 * ((r - 16) >> 2) + 4 + ((r - 16) & 3);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Byte offset in a tile of chunk c of row r.
+__device__ __forceinline__ int tile_off(int r, int c) { return 16 * (r * kLdsChunks + c); }
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// 16 bytes per active lane from a per-lane global address into LDS at lds + 16 * lane (lds is
+// wave-uniform).  Inline asm keeps the compiler's wait insertion from draining all loads
+// before every LDS read; the caller waits with vmcnt.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load16_to_lds(const void* gaddr, uint32_t lds_in) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gaddr), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Row of the 32x32 MFMA accumulator element r held by lane half h (lane column = l & 31).
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void sfa_mfma_kernel(SfaParams p) {
+__global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   constexpr int NTS = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kTileRows * kKvStride];
-  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kSfaDv * kVtStride];
-  __shared__ int64_t rows[kTileRows];
+  constexpr int LPW = (kTileLoads + NW - 1) / NW;  // loads per wave per tile (at most)
+  constexpr int LPW_MIN = kTileLoads / NW;          // ... and at least
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kTileBytes];
+  __shared__ int32_t rows[kMaxTopK];                // pool row of each slice entry, -1 if none
+  __shared__ __attribute__((aligned(16))) float hv[NW][32];   // per-head values of a wave
 
-  const int r = blockIdx.x, hg = blockIdx.y, t = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int h0 = hg * p.heads_per_wg + wave * 16;
+  // workgroup -> (query, head group, slice); consecutive workgroups go to different XCDs, so
+  // the head groups of one (query, slice) are placed 8 apart and share an XCD's L2
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7, qq = wg >> 3;
+  const int hg = qq % p.n_hg;
+  const int cc = (qq / p.n_hg) * 8 + xcd;
+  if (cc >= p.T * p.nsplit) return;
+  const int t = cc / p.nsplit, r = cc - t * p.nsplit;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, c = lane & 31;          // lane half, lane column (= head)
+  const int h0 = hg * p.heads_per_wg + wave * 32;
   const int seq = p.q_seq[t];
-
-  // queries of this wave's 16 heads: lane holds head c16, dims 32s + 8g .. +7
-  bf16x8 qr[18];
-  {
-    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)t * p.H + h0 + c16) * kSfaDqk + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 18; ++s) qr[s] = *(const bf16x8*)(qb + 32 * s);
-  }
-  const float scale2 = p.scale * kLog2e;
-  float m2 = -INFINITY, l = 0.f;
-  f32x4 o[32];
-#pragma unroll
-  for (int n = 0; n < 32; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   const int j0 = r * p.rows_per_split;
-  const int j1 = min(p.K, j0 + p.rows_per_split);
-  const int32_t* idx = p.idx + (size_t)t * p.K;
-  const uint8_t* kv = (const uint8_t*)p.kv;
+  const int nrows = min(p.K, j0 + p.rows_per_split) - j0;
+  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
 
-  for (int tile = j0; tile < j1; tile += kTileRows) {
-    __syncthreads();
-    if (tid < kTileRows) {
-      const int jj = tile + tid;
-      const int pos = jj < j1 ? idx[jj] : -1;
-      rows[tid] = pos >= 0 ? pool_row(p.L, seq, pos) : (int64_t)-1;
+  // pool rows of the slice
+  {
+    const int32_t* idx = p.idx + (size_t)t * p.K + j0;
+    for (int i = tid; i < ntiles * kTileRows; i += NTS) {
+      const int pos = i < nrows ? idx[i] : -1;
+      rows[i] = pos >= 0 ? (int32_t)pool_row(p.L, seq, pos) : -1;
     }
-    __syncthreads();
-    for (int c = tid; c < kTileRows * 72; c += NTS) {
-      const int rr = c / 72, cc = c - rr * 72;
-      const int64_t pr = rows[rr];
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (pr >= 0) v = __builtin_nontemporal_load((const u32x4*)(kv + pr * kRowBytes) + cc);
-      *(u32x4*)(kv_lds + rr * kKvStride + cc * 16) = v;
-      if (cc < 64) {
-        const int slot = vt_slot(rr);
-        const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+  }
+  // queries of this wave's 32 heads: lane holds head c, dims 16s + 8hh .. +7
+  bf16x8 qk[36];
+  {
+    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)t * p.H + h0 + c) * kSfaDqk + 8 * hh;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint16_t h = (uint16_t)(e[u >> 1] >> (16 * (u & 1)));
-          *(uint16_t*)(vt_lds + (8 * cc + u) * kVtStride + 2 * slot) = h;
-        }
+    for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qb + 16 * s);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const uint8_t* kv = (const uint8_t*)p.kv;
+  // This wave's share of tile `tile`: loads I = wave, wave + NW, ...; lane l of load I fills
+  // chunk slot 64 I + l.  Padding slots are skipped; rows without a position get zeros.
+  auto issue = [&](int tile, int buf) {
+    uint8_t* tb = tiles[buf];
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int I = wave + NW * u;
+      if (LPW != LPW_MIN && I >= kTileLoads) break;
+      const int P = 64 * I + lane;
+      const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
+      if (P < kTileSlots && ch < kRowChunks) {
+        const int row = rows[tile * kTileRows + rr];
+        if (row >= 0) load16_to_lds(kv + (size_t)row * kRowBytes + 16 * ch, lds_u32(tb + 1024 * I));
+        else *(u32x4*)(tb + 16 * P) = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    __syncthreads();
+  };
 
-    // S^T = R . Q^T for tile rows 0..15 and 16..31
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* ra = kv_lds + c16 * kKvStride + 16 * g;
-    const uint8_t* rb = kv_lds + (16 + c16) * kKvStride + 16 * g;
+  const float scale2 = p.scale * kLog2e;
+  const int* rowsp = rows;
+
+  // S^T = R . Q^T for the tile in `tb`, scaled to the exp2 domain, -inf for empty rows: lane
+  // (hh, c) gets rows acc_row(e, hh) of head c.  Scheduling fences every few steps keep the
+  // operand reads close to their MFMAs: the register file holds the queries and the output
+  // accumulators, little else.
+  auto scores = [&](const uint8_t* tb, int tile, float (&z)[16]) {
+    f32x16 sa = {};
+    const uint8_t* ra = tb + tile_off(c, hh);
 #pragma unroll
-    for (int s = 0; s < 18; ++s) {
-      const bf16x8 a0 = *(const bf16x8*)(ra + 64 * s);
-      const bf16x8 a1 = *(const bf16x8*)(rb + 64 * s);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qr[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qr[s], s1, 0, 0, 0);
+    for (int s0 = 0; s0 < 36; s0 += 4) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] = *(const bf16x8*)(ra + 32 * (s0 + u));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], qk[s0 + u], sa, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float z[8];
+    const int* trow = rowsp + tile * kTileRows;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = rows[4 * g + i] >= 0 ? s0[i] * scale2 : -INFINITY;
-      z[4 + i] = rows[16 + 4 * g + i] >= 0 ? s1[i] * scale2 : -INFINITY;
+    for (int e = 0; e < 16; ++e) z[e] = trow[acc_row(e, hh)] >= 0 ? sa[e] * scale2 : -INFINITY;
+  };
+  // Double-buffered walk over the slice's tiles: body(tile, tb) runs once each tile is in LDS.
+  auto walk = [&](auto body) {
+    issue(0, 0);
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int buf = tile & 1;
+      if (tile + 1 < ntiles) {
+        issue(tile + 1, buf ^ 1);
+        wait_vmcnt<LPW_MIN>();                    // this wave's loads of `tile` have landed
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();                            // ... and every other wave's
+      body(tile, tiles[buf]);
+      __syncthreads();                            // the buffer is refilled two tiles later
     }
-    float mx = z[0];
+  };
+
+  // Exponent reference m2 per head: set by the head's first live tile and never moved, so the
+  // output accumulators are never rescaled.  Probabilities exp2(z - m2) may exceed 1; up to
+  // 2^64 bf16 operands and fp32 sums of 2^11 terms keep their full relative precision.  A
+  // head whose scores pass m2 + 64 is flagged, and the combine kernel recomputes it with the
+  // reference method.
+  float m2 = -INFINITY, l = 0.f;
+  f32x16 o[16];
+  bool over = false;
+  auto attend = [&](int tile, const uint8_t* tb) {
+    float z[16];
+    scores(tb, tile, z);
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, z[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m2, mx);
-    const bool live = mn != -INFINITY;
-    const float alpha = live ? exp2f(m2 - mn) : 1.f;
-    float pr8[8], ps = 0.f;
+    if (m2 == -INFINITY) m2 = mx;                // first live tile of this head (O, l are 0)
+    over |= mx > m2 + 64.f;
+    const bool live = m2 != -INFINITY;
+    float pe[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr8[i] = live ? exp2f(z[i] - mn) : 0.f;
-      ps += pr8[i];
+    for (int e = 0; e < 16; ++e) {
+      pe[e] = live ? exp2f(z[e] - m2) : 0.f;
+      l += pe[e];
     }
-    l = l * alpha + ps;
-    m2 = mn;
-    // O rows held by this lane are heads 4g..4g+3: their rescale factors live in lanes 4g+i
+    // P as the A operand of k step kk: k slot 8hh + u is row 16kk + 8(u/4) + 4hh + u%4,
+    // i.e. accumulator elements 8kk .. 8kk+7 as they stand
+    bf16x8 pa0, pa1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-      for (int n = 0; n < 32; ++n) o[n][i] *= ai;
+    for (int u = 0; u < 8; ++u) {
+      pa0[u] = (__bf16)pe[u];
+      pa1[u] = (__bf16)pe[8 + u];
     }
-    bf16x8 pa;
+    // V operand for dims 32nb .. +31, k step kk: in each 16-lane group, lane i supplies row
+    // 16kk + 8jj + 4hh + i/4, dims 32nb + 16(c/16) + 4(i%4) .. +3; the transposing read
+    // returns dim 32nb + c of four consecutive rows
+    const int vi = c & 15;
+    const int vrow = 4 * hh + (vi >> 2);
+    const int vdim = 16 * (c >> 4) + 4 * (vi & 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pa[i] = (__bf16)pr8[i];
-    const uint8_t* vb = vt_lds + c16 * kVtStride + 16 * g;
+    for (int nb = 0; nb < 16; ++nb) {
+      const int dim = 32 * nb + vdim;
+      const int cho = tile_off(0, dim >> 3) + 2 * (dim & 7);
+      bf16x8 b[2];
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      const bf16x8 b = *(const bf16x8*)(vb + 16 * n * kVtStride);
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[n], 0, 0, 0);
+      for (int kk = 0; kk < 2; ++kk) {
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(tb + tile_off(16 * kk + vrow, 0) + cho));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(tb + tile_off(16 * kk + 8 + vrow, 0) + cho));
+        b[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, b[0], o[nb], 0, 0, 0);
+      o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, b[1], o[nb], 0, 0, 0);
+      if (nb & 1) __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
 
-  // per-head totals: lanes sharing c16 hold disjoint rows of the same head
-  float lt = l + __shfl_xor(l, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  float lrow[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lrow[i] = __shfl(lt, 4 * g + i, 64);
+  for (int n = 0; n < 16; ++n) o[n] = f32x16{};
+  walk(attend);
+  if (over && hh == 0) p.flags[(size_t)t * p.H + h0 + c] = 1u;
 
+  // per-head totals: the two lane halves of a column hold disjoint rows of its head
+  const float lt = l + __shfl_xor(l, 32, 64);
   if (p.nsplit == 1) {
+    if (hh == 0) hv[wave][c] = lt > 0.f ? 1.f / lt : 0.f;
     uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + h0) * kSfaDv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float inv = lrow[i] > 0.f ? 1.f / lrow[i] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 inv = *(const f32x4*)&hv[wave][8 * j + 4 * hh];
 #pragma unroll
-      for (int n = 0; n < 32; ++n)
-        out[(4 * g + i) * kSfaDv + 16 * n + c16] = (uint16_t)f32_to_bf16_bits(o[n][i] * inv);
+      for (int i = 0; i < 4; ++i) {
+        const int hd = 8 * j + 4 * hh + i;
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb)
+          out[hd * kSfaDv + 32 * nb + c] = __builtin_bit_cast(uint16_t, (__bf16)(o[nb][4 * j + i] * inv[i]));
+      }
     }
-    if (p.lse && g == 0)
-      p.lse[(size_t)t * p.H + h0 + c16] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
+    if (p.lse && hh == 0)
+      p.lse[(size_t)t * p.H + h0 + c] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
   } else {
-    const size_t pb = (((size_t)t * p.H + h0) * p.nsplit + r);   // (t, head h0, split r)
+    // partial (unnormalised O, running max in the exp2 domain, sum) of this slice
+    const size_t pb = (((size_t)t * p.H + h0) * p.nsplit + r);   // (t, head h0, slice r)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* po = p.part_o + (pb + (size_t)(4 * g + i) * p.nsplit) * kSfaDv;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int n = 0; n < 32; ++n) po[16 * n + c16] = o[n][i];
-    }
-    if (g == 0) {
-      float* pm = p.part_ml + (pb + (size_t)c16 * p.nsplit) * 2;
+      for (int i = 0; i < 4; ++i) {
+        const int hd = 8 * j + 4 * hh + i;
+        float* po = p.part_o + (pb + (size_t)hd * p.nsplit) * kSfaDv;
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) po[32 * nb + c] = o[nb][4 * j + i];
+      }
+    if (hh == 0) {
+      float* pm = p.part_ml + (pb + (size_t)c * p.nsplit) * 2;
       pm[0] = m2;
       pm[1] = lt;
     }
   }
 }
 
-// Log-sum-exp weighted merge of the index-list slices: one workgroup per (query, 16 heads).
-__global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p) {
-  __shared__ float wts[16][64];
-  __shared__ float lse_s[16];
-  const int hb = blockIdx.x * 16, t = blockIdx.y;
-  const int ns = p.nsplit;
-  if (threadIdx.x < 16) {
-    const int h = hb + threadIdx.x;
-    const float* pm = p.part_ml + (((size_t)t * p.H + h) * ns) * 2;
-    float M = -INFINITY;
-    for (int r = 0; r < ns; ++r) M = fmaxf(M, pm[2 * r]);
-    float L = 0.f;
-    for (int r = 0; r < ns; ++r) {
-      const float w = M == -INFINITY ? 0.f : exp2f(pm[2 * r] - M) * pm[2 * r + 1];
-      L += w;
-    }
-    for (int r = 0; r < ns; ++r)
-      wts[threadIdx.x][r] = (L > 0.f) ? exp2f(pm[2 * r] - M) / L : 0.f;
-    lse_s[threadIdx.x] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 16 * kSfaDv; e += 256) {
-    const int hh = e / kSfaDv, d = e - hh * kSfaDv;
-    const float* po = p.part_o + (((size_t)t * p.H + hb + hh) * ns) * kSfaDv + d;
-    float acc = 0.f;
-    for (int r = 0; r < ns; ++r) acc += wts[hh][r] * po[(size_t)r * kSfaDv];
-    ((uint16_t*)p.out)[((size_t)t * p.H + hb + hh) * kSfaDv + d] = (uint16_t)f32_to_bf16_bits(acc);
-  }
-  if (p.lse && threadIdx.x < 16) p.lse[(size_t)t * p.H + hb + threadIdx.x] = lse_s[threadIdx.x];
-}
-
-// Reference mode: one workgroup per (query, head), fp32 everywhere.
-constexpr int kRefThreads = 256;
-__global__ __launch_bounds__(kRefThreads) void sfa_reference_kernel(SfaParams p) {
-  __shared__ float qs[1024];
-  __shared__ float z[2048];
-  __shared__ int64_t rws[2048];
-  __shared__ float red[kRefThreads / 64];
-  const int h = blockIdx.x, t = blockIdx.y;
+// Reference computation of one (query, head), fp32 throughout, by the calling workgroup of
+// NTR threads: z_j over the selected rows, the softmax, then O.  LDS: the caller's `ws`.
+struct RefSmem {
+  float qs[1024];
+  float z[kMaxTopK];
+  int64_t rws[kMaxTopK];
+  float red[16];
+};
+template <int NTR>
+__device__ void reference_head(const SfaParams& p, int t, int h, RefSmem& ws) {
   const int tid = threadIdx.x;
   const int seq = p.q_seq[t];
   const bool f32 = p.dtype == kDtF32;
-  for (int d = tid; d < p.dqk; d += kRefThreads) {
+  for (int d = tid; d < p.dqk; d += NTR) {
     const size_t qi = ((size_t)t * p.H + h) * p.dqk + d;
-    qs[d] = f32 ? ((const float*)p.q)[qi] : bf16_bits_to_f32(((const uint16_t*)p.q)[qi]);
+    ws.qs[d] = f32 ? ((const float*)p.q)[qi] : bf16_bits_to_f32(((const uint16_t*)p.q)[qi]);
   }
   __syncthreads();
   auto kvat = [&](int64_t row, int d) -> float {
@@ -231,48 +304,94 @@ __global__ __launch_bounds__(kRefThreads) void sfa_reference_kernel(SfaParams p)
     return f32 ? ((const float*)p.kv)[i] : bf16_bits_to_f32(((const uint16_t*)p.kv)[i]);
   };
   float lmax = -INFINITY;
-  for (int j = tid; j < p.K; j += kRefThreads) {
+  for (int j = tid; j < p.K; j += NTR) {
     const int pos = p.idx[(size_t)t * p.K + j];
     float zz = -INFINITY;
     int64_t row = -1;
     if (pos >= 0) {
       row = pool_row(p.L, seq, pos);
       float acc = 0.f;
-      for (int d = 0; d < p.dqk; ++d) acc = fmaf(qs[d], kvat(row, d), acc);
+      for (int d = 0; d < p.dqk; ++d) acc = fmaf(ws.qs[d], kvat(row, d), acc);
       zz = acc * p.scale;
     }
-    z[j] = zz;
-    rws[j] = row;
+    ws.z[j] = zz;
+    ws.rws[j] = row;
     lmax = fmaxf(lmax, zz);
   }
-  // block max
   for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = lmax;
+  if ((tid & 63) == 0) ws.red[tid >> 6] = lmax;
   __syncthreads();
-  float M = red[0];
-  for (int w = 1; w < kRefThreads / 64; ++w) M = fmaxf(M, red[w]);
+  float M = ws.red[0];
+  for (int w = 1; w < NTR / 64; ++w) M = fmaxf(M, ws.red[w]);
   __syncthreads();
   float ls = 0.f;
-  for (int j = tid; j < p.K; j += kRefThreads) {
-    const float e = (M == -INFINITY || rws[j] < 0) ? 0.f : expf(z[j] - M);
-    z[j] = e;
+  for (int j = tid; j < p.K; j += NTR) {
+    const float e = (M == -INFINITY || ws.rws[j] < 0) ? 0.f : expf(ws.z[j] - M);
+    ws.z[j] = e;
     ls += e;
   }
   for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = ls;
+  if ((tid & 63) == 0) ws.red[8 + (tid >> 6)] = ls;
   __syncthreads();
   float L = 0.f;
-  for (int w = 0; w < kRefThreads / 64; ++w) L += red[w];
+  for (int w = 0; w < NTR / 64; ++w) L += ws.red[8 + w];
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int d = tid; d < p.dv; d += kRefThreads) {
+  for (int d = tid; d < p.dv; d += NTR) {
     float acc = 0.f;
     for (int j = 0; j < p.K; ++j)
-      if (rws[j] >= 0) acc = fmaf(z[j], kvat(rws[j], d), acc);
+      if (ws.rws[j] >= 0) acc = fmaf(ws.z[j], kvat(ws.rws[j], d), acc);
     const size_t oi = ((size_t)t * p.H + h) * p.dv + d;
     if (f32) ((float*)p.out)[oi] = acc * inv;
     else ((uint16_t*)p.out)[oi] = (uint16_t)f32_to_bf16_bits(acc * inv);
   }
   if (p.lse && tid == 0) p.lse[(size_t)t * p.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+// Reference mode: one workgroup per (query, head).
+constexpr int kRefThreads = 256;
+__global__ __launch_bounds__(kRefThreads) void sfa_reference_kernel(SfaParams p) {
+  __shared__ RefSmem ws;
+  reference_head<kRefThreads>(p, blockIdx.y, blockIdx.x, ws);
+}
+
+// Log-sum-exp weighted merge of the index-list slices, one workgroup per (head, query), one
+// float4 of the 512 output dims per thread.  A head flagged by the MFMA kernel (scores far
+// above its exponent reference) is recomputed by the reference method instead; the flag is
+// cleared for the next call.
+constexpr int kCombineThreads = 128;
+__global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams p) {
+  __shared__ RefSmem ws;
+  const int h = blockIdx.x, t = blockIdx.y;
+  uint32_t* flag = p.flags + (size_t)t * p.H + h;
+  if (*flag) {
+    reference_head<kCombineThreads>(p, t, h, ws);
+    __syncthreads();
+    if (threadIdx.x == 0) *flag = 0u;
+    return;
+  }
+  if (p.nsplit == 1) return;
+  const int ns = p.nsplit;
+  const size_t base = ((size_t)t * p.H + h) * ns;
+  const float* pm = p.part_ml + base * 2;
+  float M = -INFINITY;
+  for (int r = 0; r < ns; ++r) M = fmaxf(M, pm[2 * r]);
+  float L = 0.f;
+  for (int r = 0; r < ns; ++r) L += M == -INFINITY ? 0.f : exp2f(pm[2 * r] - M) * pm[2 * r + 1];
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int d = 4 * threadIdx.x;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* po = p.part_o + base * kSfaDv + d;
+#pragma unroll 4
+  for (int r = 0; r < ns; ++r) {
+    const float w = M == -INFINITY ? 0.f : exp2f(pm[2 * r] - M) * inv;
+    const f32x4 v = *(const f32x4*)(po + (size_t)r * kSfaDv);
+    acc += w * v;
+  }
+  uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + h) * kSfaDv + d;
+  const uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+  const uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+  *(u32x2*)out = u32x2{lo, hi};
+  if (p.lse && threadIdx.x == 0) p.lse[(size_t)t * p.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -286,12 +405,21 @@ SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path) {
     pl.rows_per_split = K;
     pl.nsplit = 1;
   } else {
-    pl.heads_per_wg = (H % 64 == 0) ? 64 : (H % 32 == 0) ? 32 : 16;
+    // One workgroup per CU holds the output accumulators of its heads in registers.  When
+    // the (query, head group) pairs alone do not fill the chip, the index list is split into
+    // slices (at most 1024 rows each) until about one workgroup per CU runs.
+    const bool wide = (int64_t)T * (H / 128) >= 256;
+    pl.heads_per_wg = (H % 128 == 0) ? 128 : (H % 96 == 0) ? 96 : (H % 64 == 0) ? 64 : 32;
     pl.n_hg = H / pl.heads_per_wg;
-    const int64_t want = 512;
-    int64_t ns = (want + (int64_t)T * pl.n_hg - 1) / ((int64_t)T * pl.n_hg);
     const int64_t max_ns = (K + kTileRows - 1) / kTileRows;
-    if (ns < 1) ns = 1;
+    int64_t ns = 1;
+    if (!wide) {
+      const int64_t want = 256;
+      ns = (want + (int64_t)T * pl.n_hg - 1) / ((int64_t)T * pl.n_hg);
+      if (const char* e = getenv("DSA_SFA_SPLITS")) ns = atoll(e) > 0 ? atoll(e) : ns;
+      const int64_t min_ns = (K + 1023) / 1024;
+      if (ns < min_ns) ns = min_ns;
+    }
     if (ns > max_ns) ns = max_ns;
     int64_t rps = (K + ns - 1) / ns;
     rps = (rps + kTileRows - 1) / kTileRows * kTileRows;
@@ -301,6 +429,8 @@ SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path) {
   size_t off = 0;
   pl.off_counters = off;
   off = al(off + 16);
+  pl.off_flags = off;
+  off = al(off + (size_t)T * H * 4);
   pl.off_part = off;
   if (pl.nsplit > 1) off = al(off + (size_t)T * H * pl.nsplit * dv * 4);
   pl.off_ml = off;
@@ -314,15 +444,19 @@ hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream) {
     hipLaunchKernelGGL(sfa_reference_kernel, dim3(p.H, p.T), dim3(kRefThreads), 0, stream, p);
     return hipGetLastError();
   }
-  const dim3 grid(p.nsplit, p.n_hg, p.T);
+  // one workgroup per (query, slice) pair rounded up to whole groups of 8, times head groups
+  const int pairs = (p.T * p.nsplit + 7) / 8 * 8;
+  const dim3 grid(pairs * p.n_hg);
   switch (p.heads_per_wg) {
-    case 64: hipLaunchKernelGGL(sfa_mfma_kernel<4>, grid, dim3(256), 0, stream, p); break;
-    case 32: hipLaunchKernelGGL(sfa_mfma_kernel<2>, grid, dim3(128), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(sfa_mfma_kernel<4>, grid, dim3(256), 0, stream, p); break;
+    case 96: hipLaunchKernelGGL(sfa_mfma_kernel<3>, grid, dim3(192), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(sfa_mfma_kernel<2>, grid, dim3(128), 0, stream, p); break;
     default: hipLaunchKernelGGL(sfa_mfma_kernel<1>, grid, dim3(64), 0, stream, p); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(sfa_combine_kernel, dim3(p.H / 16, p.T), dim3(256), 0, stream, p);
+  if (e != hipSuccess) return e;
+  // merges the slices, and recomputes any flagged head (with one slice it only checks flags)
+  hipLaunchKernelGGL(sfa_combine_kernel, dim3(p.H, p.T), dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -54,6 +54,9 @@ CASES = {
     "bf16_h16_k1": (lambda: scaled_spec(workload(2), seq_lens=[64, 99], sfa_heads=16, top_k=1),
                     "sharp"),
     "bf16_config": (lambda: scaled_spec(workload(4), seq_lens=[9000, 4000]), "config"),
+    # enough queries that the index list is not split (one workgroup per query)
+    "bf16_h128_T260_whole": (lambda: scaled_spec(workload(2), seq_lens=[300] * 260, top_k=256),
+                             "sharp"),
     "ref_bf16_h8": (lambda: scaled_spec(workload(2), seq_lens=[900], sfa_heads=8, top_k=300),
                     "sharp"),
 }
@@ -129,3 +132,27 @@ def test_full_size_end_to_end_sampled(dsa, n):
     assert res.ok, res.msgs[:5]
     O, lse = run_sfa(dsa, inp, idx)
     check(inp, idx, O, lse, queries=sample)
+
+
+def test_far_maximum_takes_the_reference_fixup(dsa):
+    """A late-selected row whose logits exceed the first tile's maximum by far more than the
+    kernel's exponent headroom: its heads are flagged and recomputed by the reference method,
+    and the flags are cleared (a second call on the same workspace gives the same result)."""
+    spec = scaled_spec(workload(2), seq_lens=[5000, 4000])
+    inp = make_inputs(spec, seed=11, sfa_dist="sharp")
+    idx = oracle_idx(inp, seed=5)
+    r = rows_of(inp, 0, [int(idx[0, spec.top_k - 1])])[0]
+    inp.kv_pool[r] = oracle.encode_bf16_rne(oracle.decode(inp.kv_pool[r], "bf16") * 64.0)
+    ws = dsa.zeroed_workspace(dsa.sfa_workspace_bytes(spec.num_queries, spec.sfa_heads,
+                                                      spec.top_k, spec.d_v), "cuda")
+    O1, L1 = run_sfa(dsa, inp, idx, workspace=ws)
+    O2, L2 = run_sfa(dsa, inp, idx, workspace=ws)
+    # the scaled row makes |O| reach ~50, so the bound is relative: bf16 output rounding is
+    # half an ulp, 2^-9 of the value, plus the usual accumulation error
+    Oref, Lref = oracle.sfa(inp, idx, list(range(spec.num_queries)))
+    scale = np.maximum(np.abs(Oref).max(axis=-1, keepdims=True), 1.0)
+    rel = np.abs(O1 - Oref) / scale
+    log(f"  max |dO|/max|O| per head {rel.max():.2e}, max |dLSE| {np.abs(L1 - Lref).max():.2e}")
+    assert rel.max() <= 2e-2 / 4
+    assert np.all(np.abs(L1 - Lref) <= 1e-4 * np.maximum(1.0, np.abs(Lref)))
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
