@@ -179,9 +179,9 @@ dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool, 
   p.out = out;
   p.lse = out_lse;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  p.counters = reinterpret_cast<uint32_t*>(ws + pl.off_counters);
+  p.zero = ws + pl.off_zero;
   p.flags = reinterpret_cast<uint32_t*>(ws + pl.off_flags);
-  p.part_o = reinterpret_cast<float*>(ws + pl.off_part);
+  p.part_o = ws + pl.off_part;
   p.part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
   const hipError_t e = launch_sfa(p, fast, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;

@@ -59,7 +59,7 @@ struct SfaPlan {
   int32_t n_hg;           // head groups
   int32_t rows_per_split; // selected rows per split (multiple of 32)
   int32_t nsplit;         // splits of top_k
-  size_t off_counters, off_flags, off_part, off_ml, bytes;
+  size_t off_zero, off_flags, off_part, off_ml, bytes;
 };
 
 struct SfaParams {
@@ -74,10 +74,10 @@ struct SfaParams {
   int32_t heads_per_wg, n_hg, rows_per_split, nsplit;
   void* out;              // [T, H, d_v]
   float* lse;             // [T, H] or nullptr
-  uint32_t* counters;     // [T][n_hg]
-  uint32_t* flags;        // [T][H] heads to recompute by the reference method (self-clearing)
-  float* part_o;          // [T][n_hg][nsplit][heads_per_wg][d_v]
-  float* part_ml;         // [T][n_hg][nsplit][heads_per_wg][2]
+  const void* zero;       // 16 zero bytes (source of the rows of absent positions)
+  uint32_t* flags;        // [T][H/32][nsplit] bit c: head 32g + c to recompute by the reference method
+  void* part_o;           // [T][H/32][nsplit] 32 KB blocks of fp16 partial outputs
+  float* part_ml;         // [T][H][nsplit][2] exponent reference (exp2 domain), sum
 };
 
 SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path);

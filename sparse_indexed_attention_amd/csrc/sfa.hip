@@ -41,6 +41,7 @@ constexpr int kLdsChunks = kRowChunks + 1;               // LDS row stride, in c
 constexpr int kTileSlots = kTileRows * kLdsChunks;       // 2336
 constexpr int kTileBytes = kTileSlots * 16;              // 37376
 constexpr int kTileLoads = (kTileSlots + 63) / 64;       // 37 direct-to-LDS loads per tile
+constexpr int kTileBufs = 3;                             // LDS tile buffers (two tiles ahead)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -77,12 +78,23 @@ __device__ __forceinline__ void load16_to_lds(const void* gaddr, uint32_t lds_in
 // Row of the 32x32 MFMA accumulator element r held by lane half h (lane column = l & 31).
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Max / sum of a value and the one held by the lane 32 apart: v_permlane32_swap exchanges the
+// halves, one of its two results is the lane's own value and the other its partner's.
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   constexpr int NTS = NW * 64;
   constexpr int LPW = (kTileLoads + NW - 1) / NW;  // loads per wave per tile (at most)
   constexpr int LPW_MIN = kTileLoads / NW;          // ... and at least
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kTileBufs][kTileBytes];
   __shared__ int32_t rows[kMaxTopK];                // pool row of each slice entry, -1 if none
   __shared__ __attribute__((aligned(16))) float hv[NW][32];   // per-head values of a wave
 
@@ -97,13 +109,22 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = lane >> 5, c = lane & 31;          // lane half, lane column (= head)
-  const int h0 = hg * p.heads_per_wg + wave * 32;
+  const int hh = lane >> 5, c = lane & 31;          // lane half, lane column
+  const int hw = hg * NW + wave;                    // this wave's group of 32 heads
+  const int h0 = hw * 32;
   const int seq = p.q_seq[t];
   const int j0 = r * p.rows_per_split;
   const int nrows = min(p.K, j0 + p.rows_per_split) - j0;
   const int ntiles = (nrows + kTileRows - 1) / kTileRows;
 
+  // queries of this wave's 32 heads (lane holds head c, dims 16s + 8hh .. +7), loaded first:
+  // their latency overlaps that of the index and block-table reads below
+  bf16x8 qk[36];
+  {
+    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)t * p.H + h0 + c) * kSfaDqk + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qb + 16 * s);
+  }
   // pool rows of the slice
   {
     const int32_t* idx = p.idx + (size_t)t * p.K + j0;
@@ -112,19 +133,16 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
       rows[i] = pos >= 0 ? (int32_t)pool_row(p.L, seq, pos) : -1;
     }
   }
-  // queries of this wave's 32 heads: lane holds head c, dims 16s + 8hh .. +7
-  bf16x8 qk[36];
-  {
-    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)t * p.H + h0 + c) * kSfaDqk + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qb + 16 * s);
-  }
   wait_vmcnt<0>();
   __syncthreads();
 
   const uint8_t* kv = (const uint8_t*)p.kv;
+  const uint8_t* zero = (const uint8_t*)p.zero;
   // This wave's share of tile `tile`: loads I = wave, wave + NW, ...; lane l of load I fills
-  // chunk slot 64 I + l.  Padding slots are skipped; rows without a position get zeros.
+  // chunk slot 64 I + l.  Rows without a position are filled from a zeroed global chunk, so
+  // every load instruction has active lanes (a padding slot is at most one lane of 64) and
+  // each wave issues the same number of loads for every tile: the vmcnt waits below count
+  // on that.
   auto issue = [&](int tile, int buf) {
     uint8_t* tb = tiles[buf];
 #pragma unroll
@@ -135,49 +153,43 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
       const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
       if (P < kTileSlots && ch < kRowChunks) {
         const int row = rows[tile * kTileRows + rr];
-        if (row >= 0) load16_to_lds(kv + (size_t)row * kRowBytes + 16 * ch, lds_u32(tb + 1024 * I));
-        else *(u32x4*)(tb + 16 * P) = u32x4{0u, 0u, 0u, 0u};
+        load16_to_lds(row >= 0 ? kv + (size_t)row * kRowBytes + 16 * ch : zero, lds_u32(tb + 1024 * I));
       }
     }
   };
 
   const float scale2 = p.scale * kLog2e;
-  const int* rowsp = rows;
 
   // S^T = R . Q^T for the tile in `tb`, scaled to the exp2 domain, -inf for empty rows: lane
-  // (hh, c) gets rows acc_row(e, hh) of head c.  Scheduling fences every few steps keep the
-  // operand reads close to their MFMAs: the register file holds the queries and the output
-  // accumulators, little else.
-  auto scores = [&](const uint8_t* tb, int tile, float (&z)[16]) {
+  // (hh, c) gets rows acc_row(e, hh) of head c.  The operand reads of the next four k steps
+  // are issued before the MFMAs of the current four (scheduling fences keep that order); the
+  // register file holds the queries and the output accumulators, so there is room for little
+  // more.
+  auto scores = [&](const uint8_t* tb, uint32_t valid, float (&z)[16]) {
     f32x16 sa = {};
     const uint8_t* ra = tb + tile_off(c, hh);
+    bf16x8 a[2][4];
 #pragma unroll
-    for (int s0 = 0; s0 < 36; s0 += 4) {
-      bf16x8 a[4];
+    for (int u = 0; u < 4; ++u) a[0][u] = *(const bf16x8*)(ra + 32 * u);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] = *(const bf16x8*)(ra + 32 * (s0 + u));
+    for (int g = 0; g < 9; ++g) {
+      if (g + 1 < 9) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], qk[s0 + u], sa, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) a[(g + 1) & 1][u] = *(const bf16x8*)(ra + 32 * (4 * (g + 1) + u));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[g & 1][u], qk[4 * g + u], sa, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int* trow = rowsp + tile * kTileRows;
+    if (valid == 0xffffffffu) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) z[e] = trow[acc_row(e, hh)] >= 0 ? sa[e] * scale2 : -INFINITY;
-  };
-  // Double-buffered walk over the slice's tiles: body(tile, tb) runs once each tile is in LDS.
-  auto walk = [&](auto body) {
-    issue(0, 0);
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int buf = tile & 1;
-      if (tile + 1 < ntiles) {
-        issue(tile + 1, buf ^ 1);
-        wait_vmcnt<LPW_MIN>();                    // this wave's loads of `tile` have landed
-      } else {
-        wait_vmcnt<0>();
-      }
-      __syncthreads();                            // ... and every other wave's
-      body(tile, tiles[buf]);
-      __syncthreads();                            // the buffer is refilled two tiles later
+      for (int e = 0; e < 16; ++e) z[e] = sa[e] * scale2;
+    } else {
+      const uint32_t mh = valid >> (4 * hh);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        z[e] = (mh >> (8 * (e >> 2) + (e & 3))) & 1u ? sa[e] * scale2 : -INFINITY;
     }
   };
 
@@ -189,64 +201,87 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   float m2 = -INFINITY, l = 0.f;
   f32x16 o[16];
   bool over = false;
+  // V operand for dims 32nb .. +31, k step kk: in each 16-lane group, lane i supplies row
+  // 16kk + 8jj + 4hh + i/4, dims 32nb + 16(c/16) + 4(i%4) .. +3; the transposing read returns
+  // dim 32nb + c of four consecutive rows
+  const int vi = c & 15;
+  const int vrow = 4 * hh + (vi >> 2);
+  const int vdim = 16 * (c >> 4) + 4 * (vi & 3);
   auto attend = [&](int tile, const uint8_t* tb) {
+    const uint32_t valid = (uint32_t)__ballot(rows[tile * kTileRows + c] >= 0);
     float z[16];
-    scores(tb, tile, z);
+    scores(tb, valid, z);
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, z[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xhalf_max(mx);
     if (m2 == -INFINITY) m2 = mx;                // first live tile of this head (O, l are 0)
     over |= mx > m2 + 64.f;
     const bool live = m2 != -INFINITY;
     float pe[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      pe[e] = live ? exp2f(z[e] - m2) : 0.f;
+      pe[e] = live ? __builtin_amdgcn_exp2f(z[e] - m2) : 0.f;
       l += pe[e];
     }
     // P as the A operand of k step kk: k slot 8hh + u is row 16kk + 8(u/4) + 4hh + u%4,
     // i.e. accumulator elements 8kk .. 8kk+7 as they stand
-    bf16x8 pa0, pa1;
+    bf16x8 pa[2];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      pa0[u] = (__bf16)pe[u];
-      pa1[u] = (__bf16)pe[8 + u];
+      pa[0][u] = (__bf16)pe[u];
+      pa[1][u] = (__bf16)pe[8 + u];
     }
-    // V operand for dims 32nb .. +31, k step kk: in each 16-lane group, lane i supplies row
-    // 16kk + 8jj + 4hh + i/4, dims 32nb + 16(c/16) + 4(i%4) .. +3; the transposing read
-    // returns dim 32nb + c of four consecutive rows
-    const int vi = c & 15;
-    const int vrow = 4 * hh + (vi >> 2);
-    const int vdim = 16 * (c >> 4) + 4 * (vi & 3);
-#pragma unroll
-    for (int nb = 0; nb < 16; ++nb) {
+    auto vread = [&](int nb, s16x4 (&v)[4]) {
       const int dim = 32 * nb + vdim;
       const int cho = tile_off(0, dim >> 3) + 2 * (dim & 7);
-      bf16x8 b[2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(tb + tile_off(8 * q + vrow, 0) + cho));
+    };
+    s16x4 vb[2][4];
+    vread(0, vb[0]);
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) {
+      if (nb + 1 < 16) vread(nb + 1, vb[(nb + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const s16x4* v = vb[nb & 1];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(tb + tile_off(16 * kk + vrow, 0) + cho));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(tb + tile_off(16 * kk + 8 + vrow, 0) + cho));
-        b[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[2 * kk], v[2 * kk + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], b, o[nb], 0, 0, 0);
       }
-      o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, b[0], o[nb], 0, 0, 0);
-      o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, b[1], o[nb], 0, 0, 0);
-      if (nb & 1) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
 #pragma unroll
   for (int n = 0; n < 16; ++n) o[n] = f32x16{};
-  walk(attend);
-  if (over && hh == 0) p.flags[(size_t)t * p.H + h0 + c] = 1u;
+  // Tiles stream through kTileBufs LDS buffers, kTileBufs - 1 of them ahead of the one being
+  // computed.
+  static_assert(kTileBufs == 3, "prologue below issues three tiles");
+  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+  if (ntiles > 2) issue(2, 2);
+  int buf = 0;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int ahead = min(ntiles - 1 - tile, kTileBufs - 1);   // later tiles in flight
+    if (ahead >= 2) wait_vmcnt<(2 * LPW_MIN < 63 ? 2 * LPW_MIN : 63)>();   // capped: waits longer
+    else if (ahead == 1) wait_vmcnt<LPW_MIN>();
+    else wait_vmcnt<0>();                        // this wave's loads of `tile` have landed
+    __syncthreads();                             // ... and every other wave's
+    attend(tile, tiles[buf]);
+    __syncthreads();                             // the buffer is free again
+    if (tile + kTileBufs < ntiles) issue(tile + kTileBufs, buf);
+    buf = buf == kTileBufs - 1 ? 0 : buf + 1;
+  }
 
   // per-head totals: the two lane halves of a column hold disjoint rows of its head
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = xhalf_sum(l);
+  if (hh == 0) hv[wave][c] = lt > 0.f ? 1.f / lt : 0.f;
+  const uint32_t flagword = (uint32_t)__ballot(over);   // bit c: head h0 + c
   if (p.nsplit == 1) {
-    if (hh == 0) hv[wave][c] = lt > 0.f ? 1.f / lt : 0.f;
     uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + h0) * kSfaDv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -262,23 +297,34 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     if (p.lse && hh == 0)
       p.lse[(size_t)t * p.H + h0 + c] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
   } else {
-    // partial (unnormalised O, running max in the exp2 domain, sum) of this slice
-    const size_t pb = (((size_t)t * p.H + h0) * p.nsplit + r);   // (t, head h0, slice r)
+    // Partial of this slice: O / l in fp16, stored as the accumulators lie in the registers.
+    // Record (j, np) of lane (hh, c) holds heads 8j + 4hh + i (i < 4) at dims 32(2np + s) + c
+    // (s < 2), value 4s + i.  A wave's 32 heads form one 32 KB block per (query, slice).
+    uint8_t* po = (uint8_t*)p.part_o + ((((size_t)t * (p.H / 32) + hw) * p.nsplit + r) * 32) * 1024 + 16 * lane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 inv = *(const f32x4*)&hv[wave][8 * j + 4 * hh];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hd = 8 * j + 4 * hh + i;
-        float* po = p.part_o + (pb + (size_t)hd * p.nsplit) * kSfaDv;
+      for (int np = 0; np < 8; ++np) {
+        uint32_t w[4];
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb) po[32 * nb + c] = o[nb][4 * j + i];
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const _Float16 a = (_Float16)(o[2 * np + s][4 * j + i] * inv[i]);
+            const _Float16 b = (_Float16)(o[2 * np + s][4 * j + i + 1] * inv[i + 1]);
+            w[2 * s + i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+          }
+        *(u32x4*)(po + (size_t)(8 * j + np) * 1024) = u32x4{w[0], w[1], w[2], w[3]};
       }
+    }
     if (hh == 0) {
-      float* pm = p.part_ml + (pb + (size_t)c * p.nsplit) * 2;
+      float* pm = p.part_ml + (((size_t)t * p.H + h0 + c) * p.nsplit + r) * 2;
       pm[0] = m2;
       pm[1] = lt;
     }
   }
+  if (lane == 0) p.flags[((size_t)t * (p.H / 32) + hw) * p.nsplit + r] = flagword;
 }
 
 // Reference computation of one (query, head), fp32 throughout, by the calling workgroup of
@@ -354,44 +400,126 @@ __global__ __launch_bounds__(kRefThreads) void sfa_reference_kernel(SfaParams p)
   reference_head<kRefThreads>(p, blockIdx.y, blockIdx.x, ws);
 }
 
-// Log-sum-exp weighted merge of the index-list slices, one workgroup per (head, query), one
-// float4 of the 512 output dims per thread.  A head flagged by the MFMA kernel (scores far
-// above its exponent reference) is recomputed by the reference method instead; the flag is
-// cleared for the next call.
-constexpr int kCombineThreads = 128;
+// Merge of the index-list slices.  A workgroup owns (query, 8 heads, half of the 512 output
+// dims): the log-sum-exp weights of the slices, then per thread one 16-byte record of the
+// fp16 partials per slice, summed in fp32.  Heads flagged by the MFMA kernel (scores far above
+// the exponent reference) are recomputed by the reference method in the first half's
+// workgroup and skipped by the other; a head whose merged output is not finite (a partial
+// beyond the fp16 range) is recomputed by the workgroup that saw it.  With a single slice the
+// MFMA kernel wrote the output and only the flags are checked.
+constexpr int kCombineThreads = 256;
+constexpr int kMaxSlices = 64;
+static_assert(kMaxTopK / kTileRows <= kMaxSlices, "a slice holds at least one tile");
+constexpr int kCombineFirst = 32;                    // partial records loaded before the weights
+constexpr int kCombineBatch = 16;                    // ... and per batch after them
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams p) {
   __shared__ RefSmem ws;
-  const int h = blockIdx.x, t = blockIdx.y;
-  uint32_t* flag = p.flags + (size_t)t * p.H + h;
-  if (*flag) {
-    reference_head<kCombineThreads>(p, t, h, ws);
+  __shared__ __attribute__((aligned(16))) float wgt[kMaxSlices][8];
+  __shared__ uint32_t flagged, nonfinite;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_hw = p.H / 32;
+  const int half = blockIdx.x & 1, j = (blockIdx.x >> 1) & 3, hw = blockIdx.x >> 3;
+  const int t = blockIdx.y;
+  const int hb = hw * 32 + 8 * j;                     // heads hb .. hb + 7
+  const int S = p.nsplit;
+  // record np of lane ln: heads hb + 4hh + i, dims 64np + 32s + c, value 4s + i.  The first
+  // slices' records are requested before anything else, so that their latency overlaps the
+  // weight computation.
+  const int np = 4 * half + wave, hh = lane >> 5, c = lane & 31;
+  const uint8_t* src = (const uint8_t*)p.part_o +
+                       ((((size_t)t * n_hw + hw) * S * 32) + 8 * j + np) * 1024 + 16 * lane;
+  u32x4 w0[kCombineFirst];
+  if (S > 1) {
+#pragma unroll
+    for (int u = 0; u < kCombineFirst; ++u)
+      w0[u] = u < S ? *(const u32x4*)(src + (size_t)u * 32 * 1024) : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (wave == 0) {
+    uint32_t f = lane < S ? p.flags[((size_t)t * n_hw + hw) * S + lane] : 0u;
+    for (int off = 32; off >= 1; off >>= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
+    if (lane == 0) {
+      flagged = (f >> (8 * j)) & 0xffu;
+      nonfinite = 0u;
+    }
+  }
+  if (S > 1) {
+    // weights of heads `wave` and `wave + 4`, lane r holding slice r
+    const int k0 = wave, k1 = wave + 4;
+    float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+    if (lane < S) {
+      const float2 a = *(const float2*)(p.part_ml + (((size_t)t * p.H + hb + k0) * S + lane) * 2);
+      const float2 b = *(const float2*)(p.part_ml + (((size_t)t * p.H + hb + k1) * S + lane) * 2);
+      m0 = a.x, l0 = a.y, m1 = b.x, l1 = b.y;
+    }
+    const float M0 = wave_max(m0), M1 = wave_max(m1);
+    const float e0 = (M0 == -INFINITY || lane >= S) ? 0.f : exp2f(m0 - M0) * l0;
+    const float e1 = (M1 == -INFINITY || lane >= S) ? 0.f : exp2f(m1 - M1) * l1;
+    const float L0 = wave_sum(e0), L1 = wave_sum(e1);
+    if (lane < S) {
+      wgt[lane][k0] = L0 > 0.f ? e0 / L0 : 0.f;
+      wgt[lane][k1] = L1 > 0.f ? e1 / L1 : 0.f;
+    }
+    if (p.lse && half == 0 && lane == 0) {
+      p.lse[(size_t)t * p.H + hb + k0] = L0 > 0.f ? (M0 + log2f(L0)) * kLn2 : -INFINITY;
+      p.lse[(size_t)t * p.H + hb + k1] = L1 > 0.f ? (M1 + log2f(L1)) * kLn2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+  if (S > 1) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kCombineFirst; ++u) {
+      const f32x4 wr = u < S ? *(const f32x4*)&wgt[u][4 * hh] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const uint32_t bits = (w0[u][v >> 1] >> (16 * (v & 1))) & 0xffffu;
+        acc[v] += wr[v & 3] * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+      }
+    }
+    for (int r0 = kCombineFirst; r0 < S; r0 += kCombineBatch) {
+      u32x4 w[kCombineBatch];
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u)
+        w[u] = r0 + u < S ? *(const u32x4*)(src + (size_t)(r0 + u) * 32 * 1024) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) {
+        if (r0 + u >= S) break;
+        const f32x4 wr = *(const f32x4*)&wgt[r0 + u][4 * hh];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const uint32_t bits = (w[u][v >> 1] >> (16 * (v & 1))) & 0xffffu;
+          acc[v] += wr[v & 3] * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+        }
+      }
+    }
+    const uint32_t skip = flagged >> (4 * hh);
+    uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + hb + 4 * hh) * kSfaDv + 64 * np + c;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int i = v & 3, sd = v >> 2;
+      if ((skip >> i) & 1u) continue;
+      if (!__builtin_isfinite(acc[v])) atomicOr(&nonfinite, 1u << (4 * hh + i));
+      out[i * kSfaDv + 32 * sd] = (uint16_t)f32_to_bf16_bits(acc[v]);
+    }
+  }
+  __syncthreads();
+  uint32_t m = (half == 0 ? flagged : 0u) | nonfinite;
+  while (m) {
+    const int k = __builtin_ctz(m);
+    m &= m - 1;
+    reference_head<kCombineThreads>(p, t, hb + k, ws);
     __syncthreads();
-    if (threadIdx.x == 0) *flag = 0u;
-    return;
   }
-  if (p.nsplit == 1) return;
-  const int ns = p.nsplit;
-  const size_t base = ((size_t)t * p.H + h) * ns;
-  const float* pm = p.part_ml + base * 2;
-  float M = -INFINITY;
-  for (int r = 0; r < ns; ++r) M = fmaxf(M, pm[2 * r]);
-  float L = 0.f;
-  for (int r = 0; r < ns; ++r) L += M == -INFINITY ? 0.f : exp2f(pm[2 * r] - M) * pm[2 * r + 1];
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const int d = 4 * threadIdx.x;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* po = p.part_o + base * kSfaDv + d;
-#pragma unroll 4
-  for (int r = 0; r < ns; ++r) {
-    const float w = M == -INFINITY ? 0.f : exp2f(pm[2 * r] - M) * inv;
-    const f32x4 v = *(const f32x4*)(po + (size_t)r * kSfaDv);
-    acc += w * v;
-  }
-  uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + h) * kSfaDv + d;
-  const uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-  const uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-  *(u32x2*)out = u32x2{lo, hi};
-  if (p.lse && threadIdx.x == 0) p.lse[(size_t)t * p.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -427,12 +555,12 @@ SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path) {
     pl.nsplit = (int32_t)((K + rps - 1) / rps);
   }
   size_t off = 0;
-  pl.off_counters = off;
+  pl.off_zero = off;                     // never written: stays as the caller zeroed it
   off = al(off + 16);
   pl.off_flags = off;
-  off = al(off + (size_t)T * H * 4);
+  off = al(off + (size_t)T * ((H + 31) / 32) * pl.nsplit * 4);
   pl.off_part = off;
-  if (pl.nsplit > 1) off = al(off + (size_t)T * H * pl.nsplit * dv * 4);
+  if (pl.nsplit > 1) off = al(off + (size_t)T * H * pl.nsplit * dv * 2);
   pl.off_ml = off;
   if (pl.nsplit > 1) off = al(off + (size_t)T * H * pl.nsplit * 8);
   pl.bytes = off;
@@ -456,7 +584,7 @@ hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // merges the slices, and recomputes any flagged head (with one slice it only checks flags)
-  hipLaunchKernelGGL(sfa_combine_kernel, dim3(p.H, p.T), dim3(kCombineThreads), 0, stream, p);
+  hipLaunchKernelGGL(sfa_combine_kernel, dim3(p.H / 4, p.T), dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 
