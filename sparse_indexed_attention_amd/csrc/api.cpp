@@ -123,7 +123,6 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
   p.hdr = reinterpret_cast<uint32_t*>(ws + pl.off_hdr);
   p.cand_key = reinterpret_cast<uint32_t*>(ws + pl.off_ckey);
   p.cand_pos = reinterpret_cast<int32_t*>(ws + pl.off_cpos);
-  p.flat_key = reinterpret_cast<uint32_t*>(ws + pl.off_fkey);
   const hipError_t e = launch_indexer(p, indexer_fast(q_dtype, k_dtype, n_heads, head_dim, layout),
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;

@@ -24,7 +24,7 @@ struct IndexerPlan {
   int32_t split;        // positions per context split (multiple of 64)
   int32_t nsplit_max;   // splits of the longest visible prefix
   int32_t cap;          // candidate slots per split = min(split, top_k)
-  size_t off_counters, off_hdr, off_ckey, off_cpos, off_fkey, bytes;
+  size_t off_counters, off_hdr, off_ckey, off_cpos, bytes;
 };
 
 struct IndexerParams {
@@ -40,12 +40,17 @@ struct IndexerParams {
   int32_t split, nsplit_max, cap;
   int32_t* out_idx;
   float* out_score;
-  uint32_t* counters;   // [T]            arrivals per query (self-resetting)
-  uint32_t* hdr;        // [T][nsplit][2] emitted count, threshold key
-  uint32_t* cand_key;   // [T][nsplit][cap]
-  int32_t* cand_pos;    // [T][nsplit][cap]
-  uint32_t* flat_key;   // [T][nsplit*cap]  merge scratch when the candidates exceed LDS
+  uint32_t* counters;   // [T][2]         arrivals, flat-list length per query (self-resetting)
+  uint32_t* hdr;        // [T][nsplit][4] emitted count, threshold key, run offset
+  uint32_t* cand_key;   // [T][2 * nsplit * cap] (+256) flat candidate lists: keys
+  int32_t* cand_pos;    // [T][2 * nsplit * cap] (+256) ... and positions
 };
+
+// Entries of one query's flat candidate list: room for every split's run twice (a re-scored
+// split appends a new run), rounded to whole 256-byte lines.
+__host__ __device__ inline size_t indexer_flat_stride(int32_t nsplit_max, int32_t cap) {
+  return ((size_t)2 * nsplit_max * cap + 63) / 64 * 64;
+}
 
 IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k);
 hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream);

@@ -61,13 +61,16 @@ template <int MODE>
 constexpr int region_bytes() {
   return MODE == 0 ? 65536 : Ring<MODE>::D * NWAVE * Ring<MODE>::SLOT;
 }
-// Merge layout of the region: split offsets, split thresholds, then the flat candidate keys.
-constexpr int kSegOffBytes = (kNSplitMax + 1) * 4 + 12;
-constexpr int kFlatOffset = kSegOffBytes + kNSplitMax * 4;
+// Merge layout of the region: the selection (keys, flat indices, then positions), then the
+// query's flat candidate list (keys, then positions when they fit).  The position bitmap that
+// orders the output reuses the flat part once the selection is gathered.
+constexpr int kSelBytes = kMaxTopK * 8;
 template <int MODE>
-constexpr int flat_capacity() {
-  return ((region_bytes<MODE>() - kFlatOffset) / 4 - 64) / 64 * 64;
+constexpr int flat_words() {
+  return (region_bytes<MODE>() - kSelBytes) / 4;
 }
+constexpr int kWinWords = 4096;                  // bitmap window: 32 * 4096 positions
+static_assert(kWinWords % NT == 0, "bitmap words per thread");
 
 // Pointers to the kernel's LDS arrays.
 struct Lds {
@@ -75,9 +78,9 @@ struct Lds {
   const float* w;     // [NWAVE][64] head weights, one copy per wave (MFMA paths)
   uint8_t* region;    // region_bytes<MODE>()
   int* hist;          // [kBins]
-  int* seg_off;       // [kNSplitMax + 1]
-  uint32_t* seg_tau;  // [kNSplitMax]
-  uint32_t* flat;     // [flat_capacity]
+  uint32_t* sel_key;  // [kMaxTopK] merge: keys of the selection
+  int32_t* sel_pos;   // [kMaxTopK] merge: flat indices, then positions, of the selection
+  uint32_t* flat;     // [flat_words] merge: flat candidate keys (+ positions)
   int* res;           // [4]
   int* scan;          // [2 * NWAVE + 2]
   int* wcnt;          // [2 * NWAVE]
@@ -144,7 +147,10 @@ __device__ __forceinline__ void load_to_lds(const void* gptr, uint32_t voff, uin
   const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
   const void* gbase = (const void*)(uintptr_t)(((uint64_t)ghi << 32) | glo);
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
-  if constexpr (SIZE == 16)
+  if constexpr (SIZE == 16 && AGENT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 sc1"
+                 :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
+  else if constexpr (SIZE == 16)
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
   else if constexpr (AGENT)
@@ -816,174 +822,397 @@ __device__ __forceinline__ void pad_output(const IndexerParams& p, int t, int fr
 }
 
 // ---------------------------------------------------------------------------------------
-// Merge of a query's split candidates (run by the last split to arrive)
+// Merge of a query's split candidates (run by the last split to arrive).
+//
+// Each split appends its candidates (key, position), in position order, to the query's flat
+// candidate list at an offset it takes from an atomic counter, so the list is a sequence of
+// runs in arrival order.  The merge reads that list row by row (entry i at thread i % NT):
+// the K_eff-th key T by range-fitted radix passes, the lower-position tie-break among keys
+// equal to T by the same selection over the tied positions, then the selection (K_eff
+// entries) is gathered and put in position order with a bitmap over the positions.  Keys of
+// runs replaced by a re-scored split are zeroed, and key 0 lies below every real key.
 // ---------------------------------------------------------------------------------------
+struct MergeHdr {
+  int n_alloc;        // entries in the flat list
+  int n_real;         // candidates of the live runs
+  uint32_t max_tau;   // largest split threshold
+};
 
-// Split headers -> LDS (emitted counts as offsets, thresholds); returns the candidate total.
-__device__ __forceinline__ int load_headers(const IndexerParams& p, int t, int nsplit, const Lds& L) {
-  constexpr int PER = kNSplitMax / NT;
-  const uint32_t* hdr = p.hdr + (size_t)t * p.nsplit_max * 2;
-  int c[PER], loc = 0;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int jj = threadIdx.x * PER + u;
-    c[u] = 0;
-    if (jj < nsplit) {
-      c[u] = (int)ld_agent(hdr + 2 * jj);
-      L.seg_tau[jj] = ld_agent(hdr + 2 * jj + 1);
-    }
-    loc += c[u];
+__device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split headers: candidate total and largest threshold; the flat list's length.
+__device__ __forceinline__ MergeHdr load_headers(const IndexerParams& p, int t, int nsplit,
+                                                 const Lds& L) {
+  const uint32_t* hdr = p.hdr + (size_t)t * p.nsplit_max * 4;
+  int c = 0;
+  uint32_t tau = 0u;
+  for (int jj = threadIdx.x; jj < nsplit; jj += NT) {
+    c += (int)ld_agent(hdr + 4 * jj);
+    tau = max(tau, ld_agent(hdr + 4 * jj + 1));
   }
-  int N;
-  int base = wg_exclusive_scan<NT>(loc, L.scan, &N);
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int jj = threadIdx.x * PER + u;
-    if (jj < nsplit) L.seg_off[jj] = base;
-    base += c[u];
+  c = wave_scan_add(c);
+  c = __builtin_amdgcn_readlane(c, 63);
+  tau = wave_max(tau);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();   // earlier readers of L.res / L.range are done
+  if ((threadIdx.x & 63) == 0) {
+    L.res[wave] = c;
+    L.range[wave] = tau;
   }
-  if (threadIdx.x == 0) L.seg_off[nsplit] = N;
   __syncthreads();
-  return N;
-}
-
-// last split whose candidates start at or before flat index i
-__device__ __forceinline__ int split_of(const Lds& L, int nsplit, int i) {
-  int a = 0, b = nsplit - 1;
-  while (a < b) {
-    const int mid = (a + b + 1) >> 1;
-    if (L.seg_off[mid] <= i) a = mid; else b = mid - 1;
+  MergeHdr h;
+  h.n_real = 0;
+  h.max_tau = 0u;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    h.n_real += L.res[w];
+    h.max_tau = max(h.max_tau, L.range[w]);
   }
-  return a;
+  h.n_alloc = (int)ld_agent(p.counters + 2 * t + 1);
+  return h;
 }
 
-// Exact selection over the flat candidate keys fk[0, N) and the output.  pos_of(i) gives
-// the position of flat candidate i.  Returns false (and writes nothing) when a split's
-// threshold lies above the K_eff-th key T.
-template <class PosOf>
-__device__ __forceinline__ bool select_output(const IndexerParams& p, int t, int K_eff,
-                                              int nsplit, int N, const uint32_t* fk, PosOf pos_of,
-                                              const Lds& L, uint32_t& T, int& gt, bool& enough) {
-  enough = N >= K_eff;
+// Row-major selection over entries [0, n) whose keys come from key_of(i) (0: no entry).
+// Each pass reads four rows at once so that global reads overlap.
+template <class KeyOf>
+__device__ __forceinline__ void rm_range(int n, KeyOf key_of, const Lds& L, uint32_t& lo,
+                                         uint32_t& hi) {
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = i0 + u * NT < n ? key_of(i0 + u * NT) : 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      mn = min(mn, k[u] ? k[u] : 0xffffffffu);
+      mx = max(mx, k[u]);
+    }
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();   // earlier readers of L.range are done
+  if ((threadIdx.x & 63) == 0) {
+    L.range[wave] = mn;
+    L.range[NWAVE + wave] = mx;
+  }
+  __syncthreads();
+  lo = 0xffffffffu;
+  hi = 0u;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    lo = min(lo, L.range[w]);
+    hi = max(hi, L.range[NWAVE + w]);
+  }
+}
+
+template <class KeyOf>
+__device__ __forceinline__ BinPick rm_rank_bin(int n, KeyOf key_of, uint32_t base,
+                                               uint32_t width, int sh, int r, const Lds& L) {
+  int* hist = L.hist;
+  __syncthreads();   // earlier readers of the histogram are done
+  for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = i0 + u * NT < n ? key_of(i0 + u * NT) : 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t o = k[u] - base;
+      if (k[u] && o <= width) atomicAdd(&hist[o >> sh], 1);
+    }
+  }
+  __syncthreads();
+  return find_in_hist(r, L);
+}
+
+// The k-th largest key among the entries (base >= 1), as radix_kth.
+template <class KeyOf>
+__device__ __forceinline__ Kth rm_kth(int n, KeyOf key_of, int k, uint32_t lo, uint32_t hi,
+                                      const Lds& L) {
+  uint32_t base = lo, width = hi - lo;
+  int above = 0;
+  for (;;) {
+    const int sh = range_shift(width);
+    const BinPick bp = rm_rank_bin(n, key_of, base, width, sh, k - above, L);
+    base += (uint32_t)bp.d << sh;
+    if (sh == 0) return Kth{base, above + bp.above, above + bp.above + bp.c};
+    width = (1u << sh) - 1u;
+    if (bp.c <= 64) {
+      // each wave compacts the bin's keys of its rows into its own 64-entry list (L.psum,
+      // free after the bin search); then every wave ranks the concatenation
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      uint32_t* mine = (uint32_t*)L.psum + 64 * wave;
+      int cnt = 0;
+      __syncthreads();   // every wave is done with L.psum
+      for (int i0 = 64 * wave; i0 < n; i0 += 4 * NT) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * NT + lane;
+          kk[u] = i < n ? key_of(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool in = kk[u] && kk[u] - base <= width;
+          const uint64_t bl = __ballot(in);
+          if (in) mine[cnt + __popcll(bl & ((1ull << lane) - 1ull))] = kk[u];
+          cnt += __popcll(bl);
+        }
+      }
+      if (lane == 0) L.wcnt[wave] = cnt;
+      __syncthreads();
+      const int c = bp.c, r = k - above - bp.above;
+      int lw = lane, w = 0;
+#pragma unroll
+      for (int q = 0; q < NWAVE - 1; ++q)
+        if (w == q && lw >= L.wcnt[q]) { lw -= L.wcnt[q]; w = q + 1; }
+      const uint32_t v = lane < c ? ((const uint32_t*)L.psum)[64 * w + lw] : 0u;
+      int gt = 0, ge = 0;
+      for (int j = 0; j < c; ++j) {
+        const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+        gt += w > v;
+        ge += w >= v;
+      }
+      const uint64_t hit = __ballot(lane < c && gt < r && r <= ge);
+      const int l = __builtin_ctzll(hit);
+      const int a = above + bp.above;
+      return Kth{(uint32_t)__builtin_amdgcn_readlane((int)v, l),
+                 a + __builtin_amdgcn_readlane(gt, l), a + __builtin_amdgcn_readlane(ge, l)};
+    }
+    above += bp.above;
+  }
+}
+
+// Selection and output over the flat list, keys from key_of(i), positions from pos_of(i).
+// Returns false (writing nothing) when a split's threshold lies above the K_eff-th key T.
+template <class KeyOf, class PosOf>
+__device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int K_eff,
+                                             const MergeHdr& mh, KeyOf key_of, PosOf pos_of,
+                                             const Lds& L, uint32_t& T, int& gt, bool& enough) {
+  const int n = mh.n_alloc;
+  enough = mh.n_real >= K_eff;
   T = 0u;
   gt = 0;
+  int ge = 0;
   if (enough) {
     uint32_t lo, hi;
-    key_range(fk, N, L, lo, hi);
-    const Kth kt = radix_kth(fk, N, K_eff, lo, hi, L);
+    rm_range(n, key_of, L, lo, hi);
+    const Kth kt = rm_kth(n, key_of, K_eff, lo, hi, L);
     T = kt.T;
     gt = kt.gt;
+    ge = kt.ge;
   }
-  int bad = 0;
-  for (int jj = threadIdx.x; jj < nsplit; jj += NT)
-    bad |= enough ? (L.seg_tau[jj] > T) : (L.seg_tau[jj] != 0u);
-  if (__syncthreads_or(bad)) return false;
-  // flat index of each output slot -> hist (free after the selection)
-  int* sel = L.hist;
-  emit_sel(fk, N, T, K_eff - gt, [&](int slot, int i, uint32_t) { if (slot < K_eff) sel[slot] = i; }, L);
-  __syncthreads();
-  // positions and scores of the selection, all loads in flight together
-  constexpr int U = kMaxTopK / NT;
-  int32_t pos[U];
-  uint32_t key[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = sel[min((int)threadIdx.x + u * NT, K_eff - 1)];
-    pos[u] = pos_of(i);
-    key[u] = fk[i];
+  // certification: every split emitted all its keys at or above T
+  if (enough ? mh.max_tau > T : mh.max_tau != 0u) return false;
+  // among keys equal to T the lower positions win: the need-th smallest tied position
+  uint32_t pmax = 0xffffffffu;
+  const int need = K_eff - gt;
+  if (enough && ge - gt > need) {
+    auto tied = [&](int i) -> uint32_t { return key_of(i) == T ? ~(uint32_t)pos_of(i) : 0u; };
+    uint32_t lo, hi;
+    rm_range(n, tied, L, lo, hi);
+    pmax = ~rm_kth(n, tied, need, lo, hi, L).T;
   }
+  // taken: above T, or equal to it at a position no later than pmax
+  auto take = [&](uint32_t k, int32_t ps) {
+    return k > T || (k == T && k != 0u && (uint32_t)ps <= pmax);
+  };
+  // four rows of keys and positions per thread, all reads in flight together
+  auto rows4 = [&](int i0, uint32_t (&k)[4], int32_t (&ps)[4]) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int s = threadIdx.x + u * NT;
-    if (s < K_eff) {
-      p.out_idx[(size_t)t * p.K + s] = pos[u];
-      if (p.out_score) p.out_score[(size_t)t * p.K + s] = key_to_float(key[u]);
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NT;
+      k[u] = i < n ? key_of(i) : 0u;
+      ps[u] = i < n ? pos_of(i) : 0;
     }
-  }
-  pad_output(p, t, K_eff);
-  if (threadIdx.x == 0) st_agent(&p.counters[t], 0u);
-  return true;
-}
-
-// Gathers the N candidates into flat arrays in split order (= position order) and selects.
-// When keys and positions fit in LDS they come with direct-to-LDS loads (one memory round
-// trip); otherwise the keys go through the workspace and the positions are fetched for the
-// selected candidates only.  T, gt and enough are kept for the re-scoring of failing splits.
-template <int MODE>
-__device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, int nsplit, int N,
-                                      const Lds& L, uint32_t& T, int& gt, bool& enough) {
-  const size_t qbase = (size_t)t * p.nsplit_max * p.cap;
+  };
+  const int V = min(p.q_vis[t], p.max_visible);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int HALF = flat_capacity<MODE>() / 2;
-  if (N <= HALF) {
-    uint32_t* fk = L.flat;
-    int32_t* fp = (int32_t*)(L.flat + HALF);
-    const uint32_t kb = lds_addr(fk), pb = lds_addr(fp);
-#pragma unroll 1
-    for (int j = wave; j < nsplit; j += NWAVE) {
-      const int o = L.seg_off[j], cnt = L.seg_off[j + 1] - o;
-      const size_t src = qbase + (size_t)j * p.cap;
-#pragma unroll 1
-      for (int c = 0; c < cnt; c += 64) {
-        if (lane < cnt - c) {
-          load_to_lds<4, true>(p.cand_key + src + c, 4u * lane, kb + 4u * (o + c));
-          load_to_lds<4, true>(p.cand_pos + src + c, 4u * lane, pb + 4u * (o + c));
+  constexpr int WPT = kWinWords / NT;   // bitmap words per thread
+  // Output order: a bitmap over the positions, each thread owning WPT consecutive words; the
+  // slot of a selected position is the count of selected positions in earlier words plus the
+  // set bits below it in its word.
+  auto word_prefix = [&](const uint32_t* bm, uint16_t* pre, int& total) {
+    uint32_t wv[WPT];
+#pragma unroll
+    for (int u = 0; u < WPT; u += 4) {
+      const u32x4 v = *(const u32x4*)(bm + WPT * threadIdx.x + u);
+      wv[u] = v.x;
+      wv[u + 1] = v.y;
+      wv[u + 2] = v.z;
+      wv[u + 3] = v.w;
+    }
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) c += __popc(wv[u]);
+    int at = wg_scan(c, 0, L, total);
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+      pre[WPT * threadIdx.x + u] = (uint16_t)at;
+      at += __popc(wv[u]);
+    }
+  };
+  auto zero_words = [&](uint32_t* bm) {
+#pragma unroll
+    for (int u = 0; u < WPT; u += 4)
+      *(u32x4*)(bm + WPT * threadIdx.x + u) = u32x4{0u, 0u, 0u, 0u};
+  };
+  auto slot_of = [&](const uint32_t* bm, const uint16_t* pre, uint32_t o) {
+    return (int)pre[o >> 5] + __popc(bm[o >> 5] & ((1u << (o & 31)) - 1u));
+  };
+  int done = 0;
+  if (V <= 32 * kWinWords) {
+    // the whole context in one window; the flat list stays where it is, the bitmap takes the
+    // selection area and the word prefixes the histogram
+    uint32_t* bm = L.sel_key;
+    uint16_t* pre = (uint16_t*)L.hist;
+    __syncthreads();   // every wave is done with the histogram
+    zero_words(bm);
+    __syncthreads();
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+      uint32_t k[4];
+      int32_t ps[4];
+      rows4(i0, k, ps);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (take(k[u], ps[u])) atomicOr(&bm[(uint32_t)ps[u] >> 5], 1u << (ps[u] & 31));
+    }
+    __syncthreads();
+    word_prefix(bm, pre, done);
+    __syncthreads();
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+      uint32_t k[4];
+      int32_t ps[4];
+      rows4(i0, k, ps);
+      int at[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) at[u] = slot_of(bm, pre, (uint32_t)ps[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (take(k[u], ps[u]) && at[u] < K_eff) {
+          p.out_idx[(size_t)t * p.K + at[u]] = ps[u];
+          if (p.out_score) p.out_score[(size_t)t * p.K + at[u]] = key_to_float(k[u]);
         }
       }
     }
-    wait_vmcnt<0>();
+  } else {
+    // gather the selection: per-wave counts, then each wave writes its rows' selected entries
+    // (flat index and key) from its own offset; then the positions, all loads in flight
+    int cnt = 0;
+    for (int i0 = 64 * wave; i0 < n; i0 += NT) {
+      const int i = i0 + lane;
+      const uint32_t k = i < n ? key_of(i) : 0u;
+      const int32_t ps = i < n ? pos_of(i) : 0;
+      cnt += __popcll(__ballot(take(k, ps)));
+    }
+    __syncthreads();   // earlier readers of L.wcnt are done
+    if (lane == 0) L.wcnt[wave] = cnt;
     __syncthreads();
-    KeyBlock<(HALF + NT - 1) / NT / 4 * 4 + 4> fb;
-    fb.load(fk, N);
-    enough = N >= K_eff;
-    T = 0u;
-    gt = 0;
-    if (enough) {
-      uint32_t lo, hi;
-      block_range(fb, L, lo, hi);
-      const Kth kt = block_kth(fb, K_eff, lo, hi, L);
-      T = kt.T;
-      gt = kt.gt;
-    }
-    int bad = 0;
-    for (int jj = threadIdx.x; jj < nsplit; jj += NT)
-      bad |= enough ? (L.seg_tau[jj] > T) : (L.seg_tau[jj] != 0u);
-    if (__syncthreads_or(bad)) return false;
-    block_emit(fb, T, K_eff - gt,
-               [&](int slot, int i, uint32_t k) {
-                 if (slot < K_eff) {
-                   p.out_idx[(size_t)t * p.K + slot] = fp[i];
-                   if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(k);
-                 }
-               },
-               L);
-    pad_output(p, t, K_eff);
-    if (threadIdx.x == 0) st_agent(&p.counters[t], 0u);
-    return true;
-  }
-  uint32_t* g = p.flat_key + qbase;
-  constexpr int B = 8;
-#pragma unroll 1
-  for (int i0 = threadIdx.x; i0 < N; i0 += B * NT) {
-    uint32_t v[B];
+    int at = 0;
 #pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = min(i0 + u * NT, N - 1);
-      const int jj = split_of(L, nsplit, i);
-      v[u] = ld_agent(p.cand_key + qbase + (size_t)jj * p.cap + (i - L.seg_off[jj]));
+    for (int w = 0; w < NWAVE; ++w) at += w < wave ? L.wcnt[w] : 0;
+    for (int i0 = 64 * wave; i0 < n; i0 += NT) {
+      const int i = i0 + lane;
+      const uint32_t k = i < n ? key_of(i) : 0u;
+      const int32_t ps = i < n ? pos_of(i) : 0;
+      const bool tk = take(k, ps);
+      const uint64_t bl = __ballot(tk);
+      const int s = at + __popcll(bl & ((1ull << lane) - 1ull));
+      if (tk && s < kMaxTopK) {
+        L.sel_key[s] = k;
+        L.sel_pos[s] = i;
+      }
+      at += __popcll(bl);
     }
+    __syncthreads();
+    int nsel = 0;
 #pragma unroll
-    for (int u = 0; u < B; ++u)
-      if (i0 + u * NT < N) g[i0 + u * NT] = v[u];
+    for (int w = 0; w < NWAVE; ++w) nsel += L.wcnt[w];
+    nsel = min(nsel, K_eff);
+    {
+      constexpr int U = kMaxTopK / NT;
+      int32_t ps[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = threadIdx.x + u * NT;
+        ps[u] = s < nsel ? pos_of(L.sel_pos[s]) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = threadIdx.x + u * NT;
+        if (s < nsel) L.sel_pos[s] = ps[u];
+      }
+    }
+    __syncthreads();
+    // one window of positions at a time, the bitmap reusing the flat area
+    uint32_t* bm = L.flat;
+    uint16_t* pre = (uint16_t*)(L.flat + kWinWords);
+    for (int w0 = 0; w0 < V; w0 += 32 * kWinWords) {
+      zero_words(bm);
+      __syncthreads();
+      for (int s = threadIdx.x; s < nsel; s += NT) {
+        const uint32_t o = (uint32_t)(L.sel_pos[s] - w0);
+        if (o < 32u * kWinWords) atomicOr(&bm[o >> 5], 1u << (o & 31));
+      }
+      __syncthreads();
+      int total;
+      word_prefix(bm, pre, total);
+      __syncthreads();
+      for (int s = threadIdx.x; s < nsel; s += NT) {
+        const uint32_t o = (uint32_t)(L.sel_pos[s] - w0);
+        if (o < 32u * kWinWords) {
+          const int slot = done + slot_of(bm, pre, o);
+          if (slot < K_eff) {
+            p.out_idx[(size_t)t * p.K + slot] = (int)(w0 + o);
+            if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(L.sel_key[s]);
+          }
+        }
+      }
+      done += total;
+      __syncthreads();
+    }
   }
-  __threadfence();
+  pad_output(p, t, min(done, K_eff));
+  if (threadIdx.x == 0) {
+    st_agent(p.counters + 2 * t, 0u);
+    st_agent(p.counters + 2 * t + 1, 0u);
+  }
+  return true;
+}
+
+// Stages the flat list in LDS when it fits (keys; positions too when there is room) with
+// agent-scope direct-to-LDS loads, then selects.  T, gt and enough are kept for the
+// re-scoring of failing splits.
+template <int MODE>
+__device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff,
+                                      const MergeHdr& mh, const Lds& L, uint32_t& T, int& gt,
+                                      bool& enough) {
+  const size_t qflat = (size_t)t * indexer_flat_stride(p.nsplit_max, p.cap);
+  const uint32_t* gk = p.cand_key + qflat;
+  const int32_t* gp = p.cand_pos + qflat;
+  const int n = mh.n_alloc;
+  const int nr = (n + 255) / 256 * 256;             // whole 1 KB loads
+  constexpr int FW = flat_words<MODE>();
+  auto gkey = [&](int i) { return ld_agent(gk + i); };
+  auto gpos = [&](int i) { return ld_agent(gp + i); };
+  if (nr > FW) return merge_select(p, t, K_eff, mh, gkey, gpos, L, T, gt, enough);
+  const bool pos_in = 2 * nr <= FW;
+  uint32_t* fk = L.flat;
+  int32_t* fp = (int32_t*)(L.flat + nr);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int c = 256 * wave; c < n; c += 256 * NWAVE) {
+    load_to_lds<16, true>(gk + c, 16u * lane, lds_addr(fk + c));
+    if (pos_in) load_to_lds<16, true>(gp + c, 16u * lane, lds_addr(fp + c));
+  }
+  wait_vmcnt<0>();
   __syncthreads();
-  return select_output(p, t, K_eff, nsplit, N, g,
-                       [&](int i) {
-                         const int jj = split_of(L, nsplit, i);
-                         return ld_agent(p.cand_pos + qbase + (size_t)jj * p.cap + (i - L.seg_off[jj]));
-                       },
-                       L, T, gt, enough);
+  auto lkey = [&](int i) { return fk[i]; };
+  if (pos_in) return merge_select(p, t, K_eff, mh, lkey, [&](int i) { return fp[i]; }, L, T, gt, enough);
+  return merge_select(p, t, K_eff, mh, lkey, gpos, L, T, gt, enough);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -994,7 +1223,7 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
 template <int MODE>
 __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   constexpr int RB = region_bytes<MODE>();
-  static_assert(RB >= kBins * 4 && flat_capacity<MODE>() >= 4096, "shared region");
+  static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kWinWords * 3 / 2, "shared region");
   __shared__ __attribute__((aligned(16))) uint8_t s_region[RB];
   __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSplitMax];
   __shared__ __attribute__((aligned(16))) float s_w[NWAVE * 64];
@@ -1007,9 +1236,9 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   L.w = s_w;
   L.region = s_region;
   L.hist = (int*)s_region;                         // while selecting a split's candidates
-  L.seg_off = (int*)s_region;                      // while merging (hist then moves to s_keys)
-  L.seg_tau = (uint32_t*)(s_region + kSegOffBytes);
-  L.flat = (uint32_t*)(s_region + kFlatOffset);
+  L.sel_key = (uint32_t*)s_region;                 // while merging (hist then moves to s_keys)
+  L.sel_pos = (int32_t*)(s_region + kMaxTopK * 4);
+  L.flat = (uint32_t*)(s_region + kSelBytes);
   L.res = s_res;
   L.scan = s_scan;
   L.wcnt = s_wcnt;
@@ -1045,8 +1274,9 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   int cur = j;            // split to score
   bool refill = false;    // re-scoring failing splits for this query's merge
   uint32_t T = 0u;
-  int gt = 0, N = 0;
+  int gt = 0;
   bool enough = false;
+  const size_t qflat = (size_t)t * indexer_flat_stride(p.nsplit_max, p.cap);   // the query's flat list
   for (;;) {
     const int start = cur * p.split, len = min(p.split, V - start);
     uint32_t klo, khi;
@@ -1090,65 +1320,73 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
             cnt = kt.ge <= hard ? kt.ge : kt.gt;
           }
         }
-        const size_t cb = ((size_t)t * p.nsplit_max + cur) * p.cap;
+        // this split's run of the flat list
+        cnt = min(cnt, p.cap);
+        if (threadIdx.x == 0) L.bcast[1] = (int)add_agent(p.counters + 2 * t + 1, (uint32_t)cnt);
+        __syncthreads();
+        const size_t cb = qflat + (size_t)L.bcast[1];
         block_emit(kb, tau, 0x7fffffff,
                    [&](int slot, int i, uint32_t k) {
-                     if (slot < p.cap) {
+                     if (slot < cnt) {
                        st_agent(p.cand_key + cb + slot, k);
                        st_agent(p.cand_pos + cb + slot, start + i);
                      }
                    },
                    L);
         if (threadIdx.x == 0) {
-          uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * 2;
-          st_agent(h, (uint32_t)min(cnt, p.cap));
+          uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * 4;
+          st_agent(h, (uint32_t)cnt);
           st_agent(h + 1, tau);
+          st_agent(h + 2, (uint32_t)L.bcast[1]);
         }
       }
       // arrival: the last split of this query to arrive merges
       wait_all_memory();
       __syncthreads();
       if (threadIdx.x == 0)
-        L.bcast[0] = __hip_atomic_fetch_add(&p.counters[t], 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1);
+        L.bcast[0] = add_agent(p.counters + 2 * t, 1u) == (uint32_t)(nsplit - 1);
       __syncthreads();
       if (!L.bcast[0]) return;
-      N = load_headers(p, t, nsplit, Lm);
-      if (merge<MODE>(p, t, K_eff, nsplit, N, Lm, T, gt, enough)) return;
+      if (merge<MODE>(p, t, K_eff, load_headers(p, t, nsplit, Lm), Lm, T, gt, enough)) return;
       refill = true;
       cur = -1;
     } else {
-      // exact local Top-min(len, K_eff) of a failing split replaces its candidates
+      // exact local Top-min(len, K_eff) of a failing split replaces its candidates: the old
+      // run's keys are zeroed and the new run is appended to the flat list
       const int kk = min(len, K_eff);
       const Kth kt = radix_kth(L.keys, len, kk, klo, khi, L);
-      const size_t cb = ((size_t)t * p.nsplit_max + cur) * p.cap;
+      uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * 4;
+      const int old_cnt = (int)ld_agent(h), old_off = (int)ld_agent(h + 2);
+      for (int i = threadIdx.x; i < old_cnt; i += NT) st_agent(p.cand_key + qflat + old_off + i, 0u);
+      if (threadIdx.x == 0) L.bcast[1] = (int)add_agent(p.counters + 2 * t + 1, (uint32_t)kk);
+      __syncthreads();
+      const size_t cb = qflat + (size_t)L.bcast[1];
       emit_sel(L.keys, len, kt.T, kk - kt.gt,
                [&](int slot, int i, uint32_t k) {
-                 if (slot < p.cap) {
+                 if (slot < kk) {
                    st_agent(p.cand_key + cb + slot, k);
                    st_agent(p.cand_pos + cb + slot, start + i);
                  }
                },
                L);
       if (threadIdx.x == 0) {
-        uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * 2;
         st_agent(h, (uint32_t)kk);
         st_agent(h + 1, 0u);
+        st_agent(h + 2, (uint32_t)L.bcast[1]);
       }
     }
     // Next failing split, judged against the threshold the merge found.  The headers are
     // read again from the workspace: their LDS copy shares memory with the scorer's ring.
     int nxt = -1;
     for (int jj = cur + 1; jj < nsplit && nxt < 0; ++jj) {
-      const uint32_t tau = ld_agent(p.hdr + ((size_t)t * p.nsplit_max + jj) * 2 + 1);
+      const uint32_t tau = ld_agent(p.hdr + ((size_t)t * p.nsplit_max + jj) * 4 + 1);
       if (enough ? (tau > T) : (tau != 0u)) nxt = jj;
     }
     nxt = __builtin_amdgcn_readfirstlane(nxt);   // same value in every lane
     wait_all_memory();
     __syncthreads();
     if (nxt < 0) {
-      N = load_headers(p, t, nsplit, Lm);
-      merge<MODE>(p, t, K_eff, nsplit, N, Lm, T, gt, enough);   // certified by construction
+      merge<MODE>(p, t, K_eff, load_headers(p, t, nsplit, Lm), Lm, T, gt, enough);   // certified
       return;
     }
     cur = nxt;
@@ -1169,13 +1407,13 @@ IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
   pl.nsplit_max = (int32_t)((max_visible + split - 1) / split);
   pl.cap = (int32_t)(split < top_k ? split : top_k);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t slots = (size_t)T * pl.nsplit_max * pl.cap;
+  // flat candidate lists, plus one 1 KB load of slack past the last
+  const size_t slots = (size_t)T * indexer_flat_stride(pl.nsplit_max, pl.cap) + 256;
   size_t off = 0;
-  pl.off_counters = off; off = al(off + (size_t)T * 4);
-  pl.off_hdr = off;      off = al(off + (size_t)T * pl.nsplit_max * 8);
+  pl.off_counters = off; off = al(off + (size_t)T * 8);
+  pl.off_hdr = off;      off = al(off + (size_t)T * pl.nsplit_max * 16);
   pl.off_ckey = off;     off = al(off + slots * 4);
   pl.off_cpos = off;     off = al(off + slots * 4);
-  pl.off_fkey = off;     off = al(off + slots * 4);
   pl.bytes = off;
   return pl;
 }
