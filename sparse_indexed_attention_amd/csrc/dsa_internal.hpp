@@ -41,7 +41,7 @@ struct IndexerParams {
   int32_t* out_idx;
   float* out_score;
   uint32_t* counters;   // [T][2]         arrivals, flat-list length per query (self-resetting)
-  uint32_t* hdr;        // [T][nsplit][4] emitted count, threshold key, run offset
+  uint32_t* hdr;        // [T][nsplit][8] emitted count, threshold key, run offset, key range
   uint32_t* cand_key;   // [T][2 * nsplit * cap] (+256) flat candidate lists: keys
   int32_t* cand_pos;    // [T][2 * nsplit * cap] (+256) ... and positions
 };

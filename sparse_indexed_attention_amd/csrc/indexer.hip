@@ -64,7 +64,8 @@ constexpr int region_bytes() {
 // Merge layout of the region: the selection (keys, flat indices, then positions), then the
 // query's flat candidate list (keys, then positions when they fit).  The position bitmap that
 // orders the output reuses the flat part once the selection is gathered.
-constexpr int kSelBytes = kMaxTopK * 8;
+constexpr int kSelCap = kMaxTopK + 64;           // the selection and one histogram bin
+constexpr int kSelBytes = kSelCap * 8;
 template <int MODE>
 constexpr int flat_words() {
   return (region_bytes<MODE>() - kSelBytes) / 4;
@@ -78,8 +79,8 @@ struct Lds {
   const float* w;     // [NWAVE][64] head weights, one copy per wave (MFMA paths)
   uint8_t* region;    // region_bytes<MODE>()
   int* hist;          // [kBins]
-  uint32_t* sel_key;  // [kMaxTopK] merge: keys of the selection
-  int32_t* sel_pos;   // [kMaxTopK] merge: flat indices, then positions, of the selection
+  uint32_t* sel_key;  // [kSelCap] merge: keys of the selection (and a few more)
+  int32_t* sel_pos;   // [kSelCap] merge: their positions
   uint32_t* flat;     // [flat_words] merge: flat candidate keys (+ positions)
   int* res;           // [4]
   int* scan;          // [2 * NWAVE + 2]
@@ -836,78 +837,66 @@ struct MergeHdr {
   int n_alloc;        // entries in the flat list
   int n_real;         // candidates of the live runs
   uint32_t max_tau;   // largest split threshold
+  uint32_t lo, hi;    // every candidate key lies in [lo, hi]
 };
 
 __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Split headers: candidate total and largest threshold; the flat list's length.
+// Split header words: emitted count, threshold, run offset, smallest and largest emitted key.
+constexpr int kHdrWords = 8;
+
+// Split headers reduced: candidate total, largest threshold, key range; the flat list's length.
 __device__ __forceinline__ MergeHdr load_headers(const IndexerParams& p, int t, int nsplit,
                                                  const Lds& L) {
-  const uint32_t* hdr = p.hdr + (size_t)t * p.nsplit_max * 4;
+  const uint32_t* hdr = p.hdr + (size_t)t * p.nsplit_max * kHdrWords;
   int c = 0;
-  uint32_t tau = 0u;
+  uint32_t tau = 0u, lo = 0xffffffffu, hi = 0u;
   for (int jj = threadIdx.x; jj < nsplit; jj += NT) {
-    c += (int)ld_agent(hdr + 4 * jj);
-    tau = max(tau, ld_agent(hdr + 4 * jj + 1));
+    const uint32_t cnt = ld_agent(hdr + kHdrWords * jj);
+    const uint32_t tj = ld_agent(hdr + kHdrWords * jj + 1);
+    const uint32_t lj = ld_agent(hdr + kHdrWords * jj + 3);
+    const uint32_t hj = ld_agent(hdr + kHdrWords * jj + 4);
+    c += (int)cnt;
+    tau = max(tau, tj);
+    if (cnt) {
+      lo = min(lo, lj);
+      hi = max(hi, hj);
+    }
   }
   c = wave_scan_add(c);
   c = __builtin_amdgcn_readlane(c, 63);
   tau = wave_max(tau);
+  lo = wave_min(lo);
+  hi = wave_max(hi);
   const int wave = threadIdx.x >> 6;
-  __syncthreads();   // earlier readers of L.res / L.range are done
+  __syncthreads();   // earlier readers of L.res / L.range / L.wcnt are done
   if ((threadIdx.x & 63) == 0) {
     L.res[wave] = c;
-    L.range[wave] = tau;
+    L.wcnt[wave] = (int)tau;
+    L.range[wave] = lo;
+    L.range[NWAVE + wave] = hi;
   }
   __syncthreads();
   MergeHdr h;
   h.n_real = 0;
   h.max_tau = 0u;
+  h.lo = 0xffffffffu;
+  h.hi = 0u;
 #pragma unroll
   for (int w = 0; w < NWAVE; ++w) {
     h.n_real += L.res[w];
-    h.max_tau = max(h.max_tau, L.range[w]);
+    h.max_tau = max(h.max_tau, (uint32_t)L.wcnt[w]);
+    h.lo = min(h.lo, L.range[w]);
+    h.hi = max(h.hi, L.range[NWAVE + w]);
   }
   h.n_alloc = (int)ld_agent(p.counters + 2 * t + 1);
   return h;
 }
 
 // Row-major selection over entries [0, n) whose keys come from key_of(i) (0: no entry).
-// Each pass reads four rows at once so that global reads overlap.
-template <class KeyOf>
-__device__ __forceinline__ void rm_range(int n, KeyOf key_of, const Lds& L, uint32_t& lo,
-                                         uint32_t& hi) {
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
-    uint32_t k[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) k[u] = i0 + u * NT < n ? key_of(i0 + u * NT) : 0u;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      mn = min(mn, k[u] ? k[u] : 0xffffffffu);
-      mx = max(mx, k[u]);
-    }
-  }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();   // earlier readers of L.range are done
-  if ((threadIdx.x & 63) == 0) {
-    L.range[wave] = mn;
-    L.range[NWAVE + wave] = mx;
-  }
-  __syncthreads();
-  lo = 0xffffffffu;
-  hi = 0u;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) {
-    lo = min(lo, L.range[w]);
-    hi = max(hi, L.range[NWAVE + w]);
-  }
-}
-
+// Passes read four rows per thread at once so that global reads overlap.
 template <class KeyOf>
 __device__ __forceinline__ BinPick rm_rank_bin(int n, KeyOf key_of, uint32_t base,
                                                uint32_t width, int sh, int r, const Lds& L) {
@@ -929,62 +918,122 @@ __device__ __forceinline__ BinPick rm_rank_bin(int n, KeyOf key_of, uint32_t bas
   return find_in_hist(r, L);
 }
 
-// The k-th largest key among the entries (base >= 1), as radix_kth.
+// Among the c <= 64 keys of the entries that lie in [base, base + width] (base >= 1): the
+// r-th largest, with the counts above it and at or above it among them.  Each wave compacts
+// the keys of its rows into its own 64-entry list (L.psum); every wave then ranks their
+// concatenation.
+template <class KeyOf>
+__device__ __forceinline__ Kth rank_few(int n, KeyOf key_of, uint32_t base, uint32_t width,
+                                        int c, int r, const Lds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* mine = (uint32_t*)L.psum + 64 * wave;
+  int cnt = 0;
+  __syncthreads();   // every wave is done with L.psum and L.wcnt
+  for (int i0 = 64 * wave; i0 < n; i0 += 4 * NT) {
+    uint32_t kk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NT + lane;
+      kk[u] = i < n ? key_of(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = kk[u] && kk[u] - base <= width;
+      const uint64_t bl = __ballot(in);
+      if (in) mine[cnt + __popcll(bl & ((1ull << lane) - 1ull))] = kk[u];
+      cnt += __popcll(bl);
+    }
+  }
+  if (lane == 0) L.wcnt[wave] = cnt;
+  __syncthreads();
+  int lw = lane, w = 0;
+#pragma unroll
+  for (int q = 0; q < NWAVE - 1; ++q)
+    if (w == q && lw >= L.wcnt[q]) { lw -= L.wcnt[q]; w = q + 1; }
+  const uint32_t v = lane < c ? ((const uint32_t*)L.psum)[64 * w + lw] : 0u;
+  int gt = 0, ge = 0;
+  for (int j = 0; j < c; ++j) {
+    const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+    gt += x > v;
+    ge += x >= v;
+  }
+  const uint64_t hit = __ballot(lane < c && gt < r && r <= ge);
+  const int l = __builtin_ctzll(hit);
+  return Kth{(uint32_t)__builtin_amdgcn_readlane((int)v, l), __builtin_amdgcn_readlane(gt, l),
+             __builtin_amdgcn_readlane(ge, l)};
+}
+
+// Range-fitted radix passes over the entries, narrowing to the bin that holds the k-th
+// largest key until that bin is a single key value or holds at most 64 keys.  Returns the
+// bin [base, base + width], the count above it and the count in it.
+struct Narrowed { uint32_t base, width; int above, c; };
+template <class KeyOf>
+__device__ __forceinline__ Narrowed rm_narrow(int n, KeyOf key_of, int k, uint32_t lo,
+                                              uint32_t hi, const Lds& L) {
+  Narrowed nw{lo, hi - lo, 0, 0};
+  for (;;) {
+    const int sh = range_shift(nw.width);
+    const BinPick bp = rm_rank_bin(n, key_of, nw.base, nw.width, sh, k - nw.above, L);
+    nw.base += (uint32_t)bp.d << sh;
+    nw.width = sh ? (1u << sh) - 1u : 0u;
+    nw.above += bp.above;
+    nw.c = bp.c;
+    if (sh == 0 || bp.c <= 64) return nw;
+  }
+}
+
+// The k-th largest key among the entries, as radix_kth (every key in [lo, hi], lo >= 1).
 template <class KeyOf>
 __device__ __forceinline__ Kth rm_kth(int n, KeyOf key_of, int k, uint32_t lo, uint32_t hi,
                                       const Lds& L) {
-  uint32_t base = lo, width = hi - lo;
-  int above = 0;
-  for (;;) {
-    const int sh = range_shift(width);
-    const BinPick bp = rm_rank_bin(n, key_of, base, width, sh, k - above, L);
-    base += (uint32_t)bp.d << sh;
-    if (sh == 0) return Kth{base, above + bp.above, above + bp.above + bp.c};
-    width = (1u << sh) - 1u;
-    if (bp.c <= 64) {
-      // each wave compacts the bin's keys of its rows into its own 64-entry list (L.psum,
-      // free after the bin search); then every wave ranks the concatenation
-      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-      uint32_t* mine = (uint32_t*)L.psum + 64 * wave;
-      int cnt = 0;
-      __syncthreads();   // every wave is done with L.psum
-      for (int i0 = 64 * wave; i0 < n; i0 += 4 * NT) {
-        uint32_t kk[4];
+  const Narrowed nw = rm_narrow(n, key_of, k, lo, hi, L);
+  if (nw.width == 0) return Kth{nw.base, nw.above, nw.above + nw.c};
+  const Kth kt = rank_few(n, key_of, nw.base, nw.width, nw.c, k - nw.above, L);
+  return Kth{kt.T, nw.above + kt.gt, nw.above + kt.ge};
+}
+
+// Compacts the entries with pred(key) into the selection area (key, position); returns their
+// count (at most kSelCap are stored).  One LDS atomic per wave and four rows.
+template <class KeyOf, class PosOf, class Pred>
+__device__ __forceinline__ int gather_sel(int n, KeyOf key_of, PosOf pos_of, Pred pred,
+                                          const Lds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();   // earlier readers of L.bcast are done
+  if (threadIdx.x == 0) L.bcast[3] = 0;
+  __syncthreads();
+  for (int i0 = 64 * wave; i0 < n; i0 += 4 * NT) {
+    uint32_t k[4];
+    int32_t ps[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * NT + lane;
-          kk[u] = i < n ? key_of(i) : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bool in = kk[u] && kk[u] - base <= width;
-          const uint64_t bl = __ballot(in);
-          if (in) mine[cnt + __popcll(bl & ((1ull << lane) - 1ull))] = kk[u];
-          cnt += __popcll(bl);
-        }
-      }
-      if (lane == 0) L.wcnt[wave] = cnt;
-      __syncthreads();
-      const int c = bp.c, r = k - above - bp.above;
-      int lw = lane, w = 0;
-#pragma unroll
-      for (int q = 0; q < NWAVE - 1; ++q)
-        if (w == q && lw >= L.wcnt[q]) { lw -= L.wcnt[q]; w = q + 1; }
-      const uint32_t v = lane < c ? ((const uint32_t*)L.psum)[64 * w + lw] : 0u;
-      int gt = 0, ge = 0;
-      for (int j = 0; j < c; ++j) {
-        const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
-        gt += w > v;
-        ge += w >= v;
-      }
-      const uint64_t hit = __ballot(lane < c && gt < r && r <= ge);
-      const int l = __builtin_ctzll(hit);
-      const int a = above + bp.above;
-      return Kth{(uint32_t)__builtin_amdgcn_readlane((int)v, l),
-                 a + __builtin_amdgcn_readlane(gt, l), a + __builtin_amdgcn_readlane(ge, l)};
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NT + lane;
+      k[u] = i < n ? key_of(i) : 0u;
+      ps[u] = i < n ? pos_of(i) : 0;
     }
-    above += bp.above;
+    uint64_t bl[4];
+    int tot = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      bl[u] = __ballot(k[u] != 0u && pred(k[u]));
+      tot += __popcll(bl[u]);
+    }
+    if (tot) {
+      int at = 0;
+      if (lane == 0) at = atomicAdd(&L.bcast[3], tot);
+      at = __builtin_amdgcn_readfirstlane(at);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = at + __popcll(bl[u] & ((1ull << lane) - 1ull));
+        if (((bl[u] >> lane) & 1ull) && s < kSelCap) {
+          L.sel_key[s] = k[u];
+          L.sel_pos[s] = ps[u];
+        }
+        at += __popcll(bl[u]);
+      }
+    }
   }
+  __syncthreads();
+  return L.bcast[3];
 }
 
 // Selection and output over the flat list, keys from key_of(i), positions from pos_of(i).
@@ -998,45 +1047,121 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
   T = 0u;
   gt = 0;
   int ge = 0;
-  if (enough) {
-    uint32_t lo, hi;
-    rm_range(n, key_of, L, lo, hi);
-    const Kth kt = rm_kth(n, key_of, K_eff, lo, hi, L);
-    T = kt.T;
-    gt = kt.gt;
-    ge = kt.ge;
-  }
-  // certification: every split emitted all its keys at or above T
-  if (enough ? mh.max_tau > T : mh.max_tau != 0u) return false;
-  // among keys equal to T the lower positions win: the need-th smallest tied position
   uint32_t pmax = 0xffffffffu;
-  const int need = K_eff - gt;
-  if (enough && ge - gt > need) {
-    auto tied = [&](int i) -> uint32_t { return key_of(i) == T ? ~(uint32_t)pos_of(i) : 0u; };
-    uint32_t lo, hi;
-    rm_range(n, tied, L, lo, hi);
-    pmax = ~rm_kth(n, tied, need, lo, hi, L).T;
-  }
-  // taken: above T, or equal to it at a position no later than pmax
-  auto take = [&](uint32_t k, int32_t ps) {
-    return k > T || (k == T && k != 0u && (uint32_t)ps <= pmax);
-  };
-  // four rows of keys and positions per thread, all reads in flight together
-  auto rows4 = [&](int i0, uint32_t (&k)[4], int32_t (&ps)[4]) {
+  const int need_all = K_eff;
+  int ns;   // entries in the selection area: the selection and possibly a few more
+  auto sel_key = [&](int s) { return L.sel_key[s]; };
+  if (!enough) {
+    if (mh.max_tau != 0u) return false;
+    ns = gather_sel(n, key_of, pos_of, [](uint32_t) { return true; }, L);
+  } else {
+    // one radix pass usually isolates a bin of a few keys holding the K_eff-th; every key at
+    // or above that bin is gathered, and the exact K_eff-th is found among them
+    const Narrowed nw = rm_narrow(n, key_of, K_eff, mh.lo, mh.hi, L);
+    if (nw.above + nw.c <= kSelCap) {
+      ns = gather_sel(n, key_of, pos_of, [&](uint32_t k) { return k >= nw.base; }, L);
+      if (nw.width == 0) {
+        T = nw.base;
+        gt = nw.above;
+        ge = nw.above + nw.c;
+      } else {
+        const Kth kt = rank_few(ns, sel_key, nw.base, nw.width, nw.c, K_eff - nw.above, L);
+        T = kt.T;
+        gt = nw.above + kt.gt;
+        ge = nw.above + kt.ge;
+      }
+      if (mh.max_tau > T) return false;
+      const int need = K_eff - gt;
+      if (ge - gt > need) {
+        // among keys equal to T the lower positions win: the need-th smallest tied position
+        auto tied = [&](int s) -> uint32_t { return L.sel_key[s] == T ? ~(uint32_t)L.sel_pos[s] : 0u; };
+        uint32_t lo = 0xffffffffu, hi = 0u;
+        for (int s = threadIdx.x; s < ns; s += NT) {
+          const uint32_t v = tied(s);
+          if (v) { lo = min(lo, v); hi = max(hi, v); }
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0) {
+          L.range[threadIdx.x >> 6] = lo;
+          L.range[NWAVE + (threadIdx.x >> 6)] = hi;
+        }
+        __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NT;
-      k[u] = i < n ? key_of(i) : 0u;
-      ps[u] = i < n ? pos_of(i) : 0;
+        for (int w = 0; w < NWAVE; ++w) {
+          lo = min(lo, L.range[w]);
+          hi = max(hi, L.range[NWAVE + w]);
+        }
+        pmax = ~rm_kth(ns, tied, need, lo, hi, L).T;
+      }
+    } else {
+      // a crowd of equal keys: the exact selection over the whole flat list, then its entries
+      const Kth kt = rm_kth(n, key_of, K_eff, mh.lo, mh.hi, L);
+      T = kt.T;
+      gt = kt.gt;
+      ge = kt.ge;
+      if (mh.max_tau > T) return false;
+      const int need = K_eff - gt;
+      if (ge - gt > need) {
+        // ties resolved over the flat list: positions are read only for keys equal to T
+        auto tied = [&](int i) -> uint32_t { return key_of(i) == T ? ~(uint32_t)pos_of(i) : 0u; };
+        pmax = ~rm_kth(n, tied, need, 0x80000000u, 0xffffffffu, L).T;
+      }
+      // equal keys beyond the selection are not gathered: positions decide among them
+      ns = 0;
+      {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        __syncthreads();
+        if (threadIdx.x == 0) L.bcast[3] = 0;
+        __syncthreads();
+        for (int i0 = 64 * wave; i0 < n; i0 += NT) {
+          const int i = i0 + lane;
+          const uint32_t k = i < n ? key_of(i) : 0u;
+          const int32_t ps = i < n ? pos_of(i) : 0;
+          const bool tk = k != 0u && (k > T || (k == T && (uint32_t)ps <= pmax));
+          const uint64_t bl = __ballot(tk);
+          if (bl) {
+            int at = 0;
+            if (lane == 0) at = atomicAdd(&L.bcast[3], __popcll(bl));
+            at = __builtin_amdgcn_readfirstlane(at);
+            const int s = at + __popcll(bl & ((1ull << lane) - 1ull));
+            if (tk && s < kSelCap) {
+              L.sel_key[s] = k;
+              L.sel_pos[s] = ps;
+            }
+          }
+        }
+        __syncthreads();
+        ns = L.bcast[3];
+      }
     }
+  }
+  (void)need_all;
+  ns = min(ns, kSelCap);
+  // taken: above T, or equal to it at a position no later than pmax (T = 0: every entry)
+  auto take = [&](uint32_t k, int32_t ps) {
+    return k > T || (k == T && (uint32_t)ps <= pmax);
   };
+  // Output order: a bitmap over one window of positions at a time (in the flat area, free
+  // now), each thread owning WPT consecutive words; the slot of a selected position is the
+  // count of selected positions in earlier words plus the set bits below it in its word.
+  constexpr int WPT = kWinWords / NT;
+  uint32_t* bm = L.flat;
+  uint16_t* pre = (uint16_t*)(L.flat + kWinWords);
   const int V = min(p.q_vis[t], p.max_visible);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int WPT = kWinWords / NT;   // bitmap words per thread
-  // Output order: a bitmap over the positions, each thread owning WPT consecutive words; the
-  // slot of a selected position is the count of selected positions in earlier words plus the
-  // set bits below it in its word.
-  auto word_prefix = [&](const uint32_t* bm, uint16_t* pre, int& total) {
+  int done = 0;
+  for (int w0 = 0; w0 < V; w0 += 32 * kWinWords) {
+    __syncthreads();   // the flat area and the previous window are done with
+#pragma unroll
+    for (int u = 0; u < WPT; u += 4)
+      *(u32x4*)(bm + WPT * threadIdx.x + u) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (int s = threadIdx.x; s < ns; s += NT) {
+      const uint32_t o = (uint32_t)(L.sel_pos[s] - w0);
+      if (o < 32u * kWinWords && take(L.sel_key[s], L.sel_pos[s])) atomicOr(&bm[o >> 5], 1u << (o & 31));
+    }
+    __syncthreads();
     uint32_t wv[WPT];
 #pragma unroll
     for (int u = 0; u < WPT; u += 4) {
@@ -1049,132 +1174,38 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
     int c = 0;
 #pragma unroll
     for (int u = 0; u < WPT; ++u) c += __popc(wv[u]);
+    int total;
     int at = wg_scan(c, 0, L, total);
 #pragma unroll
     for (int u = 0; u < WPT; ++u) {
       pre[WPT * threadIdx.x + u] = (uint16_t)at;
       at += __popc(wv[u]);
     }
-  };
-  auto zero_words = [&](uint32_t* bm) {
-#pragma unroll
-    for (int u = 0; u < WPT; u += 4)
-      *(u32x4*)(bm + WPT * threadIdx.x + u) = u32x4{0u, 0u, 0u, 0u};
-  };
-  auto slot_of = [&](const uint32_t* bm, const uint16_t* pre, uint32_t o) {
-    return (int)pre[o >> 5] + __popc(bm[o >> 5] & ((1u << (o & 31)) - 1u));
-  };
-  int done = 0;
-  if (V <= 32 * kWinWords) {
-    // the whole context in one window; the flat list stays where it is, the bitmap takes the
-    // selection area and the word prefixes the histogram
-    uint32_t* bm = L.sel_key;
-    uint16_t* pre = (uint16_t*)L.hist;
-    __syncthreads();   // every wave is done with the histogram
-    zero_words(bm);
     __syncthreads();
-    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
-      uint32_t k[4];
-      int32_t ps[4];
-      rows4(i0, k, ps);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (take(k[u], ps[u])) atomicOr(&bm[(uint32_t)ps[u] >> 5], 1u << (ps[u] & 31));
-    }
-    __syncthreads();
-    word_prefix(bm, pre, done);
-    __syncthreads();
-    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
-      uint32_t k[4];
-      int32_t ps[4];
-      rows4(i0, k, ps);
-      int at[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) at[u] = slot_of(bm, pre, (uint32_t)ps[u]);
+    for (int s0 = threadIdx.x; s0 < ns; s0 += 4 * NT) {
+      uint32_t k[4], o[4];
+      int slot[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (take(k[u], ps[u]) && at[u] < K_eff) {
-          p.out_idx[(size_t)t * p.K + at[u]] = ps[u];
-          if (p.out_score) p.out_score[(size_t)t * p.K + at[u]] = key_to_float(k[u]);
+        const int s = min(s0 + u * NT, ns - 1);
+        k[u] = L.sel_key[s];
+        o[u] = (uint32_t)(L.sel_pos[s] - w0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t oo = min(o[u], 32u * kWinWords - 1u);
+        slot[u] = done + (int)pre[oo >> 5] + __popc(bm[oo >> 5] & ((1u << (oo & 31)) - 1u));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (s0 + u * NT < ns && o[u] < 32u * kWinWords && take(k[u], (int32_t)(o[u] + w0)) &&
+            slot[u] < K_eff) {
+          p.out_idx[(size_t)t * p.K + slot[u]] = (int)(o[u] + w0);
+          if (p.out_score) p.out_score[(size_t)t * p.K + slot[u]] = key_to_float(k[u]);
         }
       }
     }
-  } else {
-    // gather the selection: per-wave counts, then each wave writes its rows' selected entries
-    // (flat index and key) from its own offset; then the positions, all loads in flight
-    int cnt = 0;
-    for (int i0 = 64 * wave; i0 < n; i0 += NT) {
-      const int i = i0 + lane;
-      const uint32_t k = i < n ? key_of(i) : 0u;
-      const int32_t ps = i < n ? pos_of(i) : 0;
-      cnt += __popcll(__ballot(take(k, ps)));
-    }
-    __syncthreads();   // earlier readers of L.wcnt are done
-    if (lane == 0) L.wcnt[wave] = cnt;
-    __syncthreads();
-    int at = 0;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) at += w < wave ? L.wcnt[w] : 0;
-    for (int i0 = 64 * wave; i0 < n; i0 += NT) {
-      const int i = i0 + lane;
-      const uint32_t k = i < n ? key_of(i) : 0u;
-      const int32_t ps = i < n ? pos_of(i) : 0;
-      const bool tk = take(k, ps);
-      const uint64_t bl = __ballot(tk);
-      const int s = at + __popcll(bl & ((1ull << lane) - 1ull));
-      if (tk && s < kMaxTopK) {
-        L.sel_key[s] = k;
-        L.sel_pos[s] = i;
-      }
-      at += __popcll(bl);
-    }
-    __syncthreads();
-    int nsel = 0;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) nsel += L.wcnt[w];
-    nsel = min(nsel, K_eff);
-    {
-      constexpr int U = kMaxTopK / NT;
-      int32_t ps[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = threadIdx.x + u * NT;
-        ps[u] = s < nsel ? pos_of(L.sel_pos[s]) : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = threadIdx.x + u * NT;
-        if (s < nsel) L.sel_pos[s] = ps[u];
-      }
-    }
-    __syncthreads();
-    // one window of positions at a time, the bitmap reusing the flat area
-    uint32_t* bm = L.flat;
-    uint16_t* pre = (uint16_t*)(L.flat + kWinWords);
-    for (int w0 = 0; w0 < V; w0 += 32 * kWinWords) {
-      zero_words(bm);
-      __syncthreads();
-      for (int s = threadIdx.x; s < nsel; s += NT) {
-        const uint32_t o = (uint32_t)(L.sel_pos[s] - w0);
-        if (o < 32u * kWinWords) atomicOr(&bm[o >> 5], 1u << (o & 31));
-      }
-      __syncthreads();
-      int total;
-      word_prefix(bm, pre, total);
-      __syncthreads();
-      for (int s = threadIdx.x; s < nsel; s += NT) {
-        const uint32_t o = (uint32_t)(L.sel_pos[s] - w0);
-        if (o < 32u * kWinWords) {
-          const int slot = done + slot_of(bm, pre, o);
-          if (slot < K_eff) {
-            p.out_idx[(size_t)t * p.K + slot] = (int)(w0 + o);
-            if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(L.sel_key[s]);
-          }
-        }
-      }
-      done += total;
-      __syncthreads();
-    }
+    done += total;
   }
   pad_output(p, t, min(done, K_eff));
   if (threadIdx.x == 0) {
@@ -1237,7 +1268,7 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   L.region = s_region;
   L.hist = (int*)s_region;                         // while selecting a split's candidates
   L.sel_key = (uint32_t*)s_region;                 // while merging (hist then moves to s_keys)
-  L.sel_pos = (int32_t*)(s_region + kMaxTopK * 4);
+  L.sel_pos = (int32_t*)(s_region + kSelCap * 4);
   L.flat = (uint32_t*)(s_region + kSelBytes);
   L.res = s_res;
   L.scan = s_scan;
@@ -1334,10 +1365,12 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
                    },
                    L);
         if (threadIdx.x == 0) {
-          uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * 4;
+          uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * kHdrWords;
           st_agent(h, (uint32_t)cnt);
           st_agent(h + 1, tau);
           st_agent(h + 2, (uint32_t)L.bcast[1]);
+          st_agent(h + 3, max(tau, klo));
+          st_agent(h + 4, khi);
         }
       }
       // arrival: the last split of this query to arrive merges
@@ -1355,7 +1388,7 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
       // run's keys are zeroed and the new run is appended to the flat list
       const int kk = min(len, K_eff);
       const Kth kt = radix_kth(L.keys, len, kk, klo, khi, L);
-      uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * 4;
+      uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * kHdrWords;
       const int old_cnt = (int)ld_agent(h), old_off = (int)ld_agent(h + 2);
       for (int i = threadIdx.x; i < old_cnt; i += NT) st_agent(p.cand_key + qflat + old_off + i, 0u);
       if (threadIdx.x == 0) L.bcast[1] = (int)add_agent(p.counters + 2 * t + 1, (uint32_t)kk);
@@ -1373,13 +1406,15 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
         st_agent(h, (uint32_t)kk);
         st_agent(h + 1, 0u);
         st_agent(h + 2, (uint32_t)L.bcast[1]);
+        st_agent(h + 3, kt.T);
+        st_agent(h + 4, khi);
       }
     }
     // Next failing split, judged against the threshold the merge found.  The headers are
     // read again from the workspace: their LDS copy shares memory with the scorer's ring.
     int nxt = -1;
     for (int jj = cur + 1; jj < nsplit && nxt < 0; ++jj) {
-      const uint32_t tau = ld_agent(p.hdr + ((size_t)t * p.nsplit_max + jj) * 4 + 1);
+      const uint32_t tau = ld_agent(p.hdr + ((size_t)t * p.nsplit_max + jj) * kHdrWords + 1);
       if (enough ? (tau > T) : (tau != 0u)) nxt = jj;
     }
     nxt = __builtin_amdgcn_readfirstlane(nxt);   // same value in every lane
@@ -1411,7 +1446,7 @@ IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
   const size_t slots = (size_t)T * indexer_flat_stride(pl.nsplit_max, pl.cap) + 256;
   size_t off = 0;
   pl.off_counters = off; off = al(off + (size_t)T * 8);
-  pl.off_hdr = off;      off = al(off + (size_t)T * pl.nsplit_max * 16);
+  pl.off_hdr = off;      off = al(off + (size_t)T * pl.nsplit_max * 32);
   pl.off_ckey = off;     off = al(off + slots * 4);
   pl.off_cpos = off;     off = al(off + slots * 4);
   pl.bytes = off;
