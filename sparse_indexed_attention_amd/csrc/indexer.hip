@@ -62,16 +62,14 @@ constexpr int region_bytes() {
   return MODE == 0 ? 65536 : Ring<MODE>::D * NWAVE * Ring<MODE>::SLOT;
 }
 // Merge layout of the region: the selection (keys, flat indices, then positions), then the
-// query's flat candidate list (keys, then positions when they fit).  The position bitmap that
-// orders the output reuses the flat part once the selection is gathered.
+// query's flat candidate list (keys, then positions when they fit), whose space the ordering
+// of the output reuses once the selection is gathered.
 constexpr int kSelCap = kMaxTopK + 64;           // the selection and one histogram bin
 constexpr int kSelBytes = kSelCap * 8;
 template <int MODE>
 constexpr int flat_words() {
   return (region_bytes<MODE>() - kSelBytes) / 4;
 }
-constexpr int kWinWords = 4096;                  // bitmap window: 32 * 4096 positions
-static_assert(kWinWords % NT == 0, "bitmap words per thread");
 
 // Pointers to the kernel's LDS arrays.
 struct Lds {
@@ -827,11 +825,13 @@ __device__ __forceinline__ void pad_output(const IndexerParams& p, int t, int fr
 //
 // Each split appends its candidates (key, position), in position order, to the query's flat
 // candidate list at an offset it takes from an atomic counter, so the list is a sequence of
-// runs in arrival order.  The merge reads that list row by row (entry i at thread i % NT):
-// the K_eff-th key T by range-fitted radix passes, the lower-position tie-break among keys
-// equal to T by the same selection over the tied positions, then the selection (K_eff
-// entries) is gathered and put in position order with a bitmap over the positions.  Keys of
-// runs replaced by a re-scored split are zeroed, and key 0 lies below every real key.
+// runs in arrival order.  The merge finds the bin of the K_eff-th key by range-fitted radix
+// passes over that list, gathers every entry at or above the bin in flat order, and finds the
+// exact K_eff-th key T (and, among keys equal to T, the lower positions) within the gathered
+// set.  Since split r covers positions [r*split, (r+1)*split) and its run is in position
+// order, the output slot of a taken entry is the count taken in earlier splits plus its rank
+// in its run.  Keys of runs replaced by a re-scored split are zeroed, and key 0 lies below
+// every real key.
 // ---------------------------------------------------------------------------------------
 struct MergeHdr {
   int n_alloc;        // entries in the flat list
@@ -842,6 +842,15 @@ struct MergeHdr {
 
 __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// x / d for x < 2^24 with a float reciprocal and one correction step (an integer division is
+// a long instruction sequence).
+__device__ __forceinline__ uint32_t div_split(uint32_t x, uint32_t d, float inv) {
+  uint32_t q = (uint32_t)((float)x * inv);
+  q -= (uint32_t)(q * d > x);
+  q += (uint32_t)((q + 1u) * d <= x);
+  return q;
 }
 
 // Split header words: emitted count, threshold, run offset, smallest and largest emitted key.
@@ -911,7 +920,7 @@ __device__ __forceinline__ BinPick rm_rank_bin(int n, KeyOf key_of, uint32_t bas
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t o = k[u] - base;
-      if (k[u] && o <= width) atomicAdd(&hist[o >> sh], 1);
+      if ((k[u] != 0u) & (o <= width)) atomicAdd(&hist[o >> sh], 1);
     }
   }
   __syncthreads();
@@ -938,7 +947,7 @@ __device__ __forceinline__ Kth rank_few(int n, KeyOf key_of, uint32_t base, uint
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bool in = kk[u] && kk[u] - base <= width;
+      const bool in = (kk[u] != 0u) & (kk[u] - base <= width);
       const uint64_t bl = __ballot(in);
       if (in) mine[cnt + __popcll(bl & ((1ull << lane) - 1ull))] = kk[u];
       cnt += __popcll(bl);
@@ -992,48 +1001,58 @@ __device__ __forceinline__ Kth rm_kth(int n, KeyOf key_of, int k, uint32_t lo, u
   return Kth{kt.T, nw.above + kt.gt, nw.above + kt.ge};
 }
 
-// Compacts the entries with pred(key) into the selection area (key, position); returns their
-// count (at most kSelCap are stored).  One LDS atomic per wave and four rows.
+// Compacts the entries with pred(key, i) into the selection area, keeping their flat order:
+// thread i scans the contiguous block [E*i, E*i + E) of the list (E odd, so that the LDS
+// reads of a wave fall in distinct banks), counts, takes its offset from a workgroup scan,
+// then writes flat indices; the positions follow with all reads in flight.  Returns the
+// count (at most kSelCap are stored).
 template <class KeyOf, class PosOf, class Pred>
-__device__ __forceinline__ int gather_sel(int n, KeyOf key_of, PosOf pos_of, Pred pred,
-                                          const Lds& L) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();   // earlier readers of L.bcast are done
-  if (threadIdx.x == 0) L.bcast[3] = 0;
-  __syncthreads();
-  for (int i0 = 64 * wave; i0 < n; i0 += 4 * NT) {
+__device__ __forceinline__ int gather_ordered(int n, KeyOf key_of, PosOf pos_of, Pred pred,
+                                              const Lds& L) {
+  const int E = ((n + NT - 1) / NT) | 1;
+  const int b0 = min(n, E * (int)threadIdx.x), b1 = min(n, b0 + E);
+  int c = 0;
+  for (int i0 = b0; i0 < b1; i0 += 4) {
     uint32_t k[4];
-    int32_t ps[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = i0 + u < b1 ? key_of(i0 + u) : 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c += (int)((k[u] != 0u) & pred(k[u], i0 + u));
+  }
+  int total;
+  __syncthreads();   // earlier readers of L.scan are done
+  int at = wg_scan(c, 0, L, total);
+  for (int i0 = b0; i0 < b1; i0 += 4) {
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = i0 + u < b1 ? key_of(i0 + u) : 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NT + lane;
-      k[u] = i < n ? key_of(i) : 0u;
-      ps[u] = i < n ? pos_of(i) : 0;
-    }
-    uint64_t bl[4];
-    int tot = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      bl[u] = __ballot(k[u] != 0u && pred(k[u]));
-      tot += __popcll(bl[u]);
-    }
-    if (tot) {
-      int at = 0;
-      if (lane == 0) at = atomicAdd(&L.bcast[3], tot);
-      at = __builtin_amdgcn_readfirstlane(at);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = at + __popcll(bl[u] & ((1ull << lane) - 1ull));
-        if (((bl[u] >> lane) & 1ull) && s < kSelCap) {
-          L.sel_key[s] = k[u];
-          L.sel_pos[s] = ps[u];
+      if ((k[u] != 0u) & pred(k[u], i0 + u)) {
+        if (at < kSelCap) {
+          L.sel_key[at] = k[u];
+          L.sel_pos[at] = i0 + u;
         }
-        at += __popcll(bl[u]);
+        ++at;
       }
     }
   }
   __syncthreads();
-  return L.bcast[3];
+  const int ns = min(total, kSelCap);
+  constexpr int U = (kSelCap + NT - 1) / NT;
+  int32_t ps[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = threadIdx.x + u * NT;
+    ps[u] = q < ns ? pos_of(L.sel_pos[q]) : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = threadIdx.x + u * NT;
+    if (q < ns) L.sel_pos[q] = ps[u];
+  }
+  __syncthreads();
+  return total;
 }
 
 // Selection and output over the flat list, keys from key_of(i), positions from pos_of(i).
@@ -1048,18 +1067,17 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
   gt = 0;
   int ge = 0;
   uint32_t pmax = 0xffffffffu;
-  const int need_all = K_eff;
-  int ns;   // entries in the selection area: the selection and possibly a few more
-  auto sel_key = [&](int s) { return L.sel_key[s]; };
+  int ns;   // entries in the selection area, in flat order: the selection and maybe a few more
+  auto sel_key = [&](int q) { return L.sel_key[q]; };
   if (!enough) {
     if (mh.max_tau != 0u) return false;
-    ns = gather_sel(n, key_of, pos_of, [](uint32_t) { return true; }, L);
+    ns = gather_ordered(n, key_of, pos_of, [](uint32_t, int) { return true; }, L);
   } else {
     // one radix pass usually isolates a bin of a few keys holding the K_eff-th; every key at
     // or above that bin is gathered, and the exact K_eff-th is found among them
     const Narrowed nw = rm_narrow(n, key_of, K_eff, mh.lo, mh.hi, L);
     if (nw.above + nw.c <= kSelCap) {
-      ns = gather_sel(n, key_of, pos_of, [&](uint32_t k) { return k >= nw.base; }, L);
+      ns = gather_ordered(n, key_of, pos_of, [&](uint32_t k, int) { return k >= nw.base; }, L);
       if (nw.width == 0) {
         T = nw.base;
         gt = nw.above;
@@ -1074,26 +1092,10 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
       const int need = K_eff - gt;
       if (ge - gt > need) {
         // among keys equal to T the lower positions win: the need-th smallest tied position
-        auto tied = [&](int s) -> uint32_t { return L.sel_key[s] == T ? ~(uint32_t)L.sel_pos[s] : 0u; };
-        uint32_t lo = 0xffffffffu, hi = 0u;
-        for (int s = threadIdx.x; s < ns; s += NT) {
-          const uint32_t v = tied(s);
-          if (v) { lo = min(lo, v); hi = max(hi, v); }
-        }
-        lo = wave_min(lo);
-        hi = wave_max(hi);
-        __syncthreads();
-        if ((threadIdx.x & 63) == 0) {
-          L.range[threadIdx.x >> 6] = lo;
-          L.range[NWAVE + (threadIdx.x >> 6)] = hi;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) {
-          lo = min(lo, L.range[w]);
-          hi = max(hi, L.range[NWAVE + w]);
-        }
-        pmax = ~rm_kth(ns, tied, need, lo, hi, L).T;
+        auto tied = [&](int q) -> uint32_t {
+          return L.sel_key[q] == T ? ~(uint32_t)L.sel_pos[q] : 0u;
+        };
+        pmax = ~rm_kth(ns, tied, need, 0x80000000u, 0xffffffffu, L).T;
       }
     } else {
       // a crowd of equal keys: the exact selection over the whole flat list, then its entries
@@ -1104,110 +1106,129 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
       if (mh.max_tau > T) return false;
       const int need = K_eff - gt;
       if (ge - gt > need) {
-        // ties resolved over the flat list: positions are read only for keys equal to T
         auto tied = [&](int i) -> uint32_t { return key_of(i) == T ? ~(uint32_t)pos_of(i) : 0u; };
         pmax = ~rm_kth(n, tied, need, 0x80000000u, 0xffffffffu, L).T;
       }
-      // equal keys beyond the selection are not gathered: positions decide among them
-      ns = 0;
-      {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        __syncthreads();
-        if (threadIdx.x == 0) L.bcast[3] = 0;
-        __syncthreads();
-        for (int i0 = 64 * wave; i0 < n; i0 += NT) {
-          const int i = i0 + lane;
-          const uint32_t k = i < n ? key_of(i) : 0u;
-          const int32_t ps = i < n ? pos_of(i) : 0;
-          const bool tk = k != 0u && (k > T || (k == T && (uint32_t)ps <= pmax));
-          const uint64_t bl = __ballot(tk);
-          if (bl) {
-            int at = 0;
-            if (lane == 0) at = atomicAdd(&L.bcast[3], __popcll(bl));
-            at = __builtin_amdgcn_readfirstlane(at);
-            const int s = at + __popcll(bl & ((1ull << lane) - 1ull));
-            if (tk && s < kSelCap) {
-              L.sel_key[s] = k;
-              L.sel_pos[s] = ps;
-            }
-          }
-        }
-        __syncthreads();
-        ns = L.bcast[3];
-      }
+      const uint32_t TT = T, PM = pmax;
+      ns = gather_ordered(n, key_of, pos_of,
+                          [&](uint32_t k, int i) { return k > TT || (k == TT && (uint32_t)pos_of(i) <= PM); },
+                          L);
     }
   }
-  (void)need_all;
   ns = min(ns, kSelCap);
   // taken: above T, or equal to it at a position no later than pmax (T = 0: every entry)
-  auto take = [&](uint32_t k, int32_t ps) {
-    return k > T || (k == T && (uint32_t)ps <= pmax);
-  };
-  // Output order: a bitmap over one window of positions at a time (in the flat area, free
-  // now), each thread owning WPT consecutive words; the slot of a selected position is the
-  // count of selected positions in earlier words plus the set bits below it in its word.
-  constexpr int WPT = kWinWords / NT;
-  uint32_t* bm = L.flat;
-  uint16_t* pre = (uint16_t*)(L.flat + kWinWords);
-  const int V = min(p.q_vis[t], p.max_visible);
-  int done = 0;
-  for (int w0 = 0; w0 < V; w0 += 32 * kWinWords) {
-    __syncthreads();   // the flat area and the previous window are done with
+  // (bitwise operators: straight-line code, no branches)
+  auto take = [&](uint32_t k, int32_t ps) { return (k > T) | ((k == T) & ((uint32_t)ps <= pmax)); };
+  // Output order.  The selection area holds, in flat order, the runs of the splits, each in
+  // position order, and split r covers positions [r*split, (r+1)*split).  So the slot of a
+  // taken entry of split r is the count taken in splits before r plus its rank in its run:
+  // per-split counts (scanned in split order) and, per run, the taken count before its start.
+  const int nspl = (min(p.q_vis[t], p.max_visible) + p.split - 1) / p.split;
+  int* cnt = L.hist;                        // [nspl] taken per split, then the scan
+  int* first = (int*)L.flat;                // [nspl] taken entries before the run of a split
+  const int E = ((ns + NT - 1) / NT) | 1;
+  const int b0 = min(ns, E * (int)threadIdx.x), b1 = min(ns, b0 + E);
+  const uint32_t split = (uint32_t)p.split;
+  const float inv_split = 1.0f / (float)p.split;
+  __syncthreads();   // the histogram and the flat area are free
+  for (int r = threadIdx.x; r < nspl; r += NT) cnt[r] = 0;
+  __syncthreads();
+  int c = 0;
+  for (int q0 = b0; q0 < b1; q0 += 4) {
+    uint32_t k[4];
+    int32_t ps[4];
 #pragma unroll
-    for (int u = 0; u < WPT; u += 4)
-      *(u32x4*)(bm + WPT * threadIdx.x + u) = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    for (int s = threadIdx.x; s < ns; s += NT) {
-      const uint32_t o = (uint32_t)(L.sel_pos[s] - w0);
-      if (o < 32u * kWinWords && take(L.sel_key[s], L.sel_pos[s])) atomicOr(&bm[o >> 5], 1u << (o & 31));
+    for (int u = 0; u < 4; ++u) {
+      const int q = min(q0 + u, b1 - 1);
+      k[u] = L.sel_key[q];
+      ps[u] = L.sel_pos[q];
     }
-    __syncthreads();
-    uint32_t wv[WPT];
 #pragma unroll
-    for (int u = 0; u < WPT; u += 4) {
-      const u32x4 v = *(const u32x4*)(bm + WPT * threadIdx.x + u);
-      wv[u] = v.x;
-      wv[u + 1] = v.y;
-      wv[u + 2] = v.z;
-      wv[u + 3] = v.w;
+    for (int u = 0; u < 4; ++u) {
+      if ((q0 + u < b1) & take(k[u], ps[u])) {
+        ++c;
+        atomicAdd(&cnt[div_split((uint32_t)ps[u], split, inv_split)], 1);
+      }
     }
-    int c = 0;
+  }
+  int total;
+  const int fs0 = wg_scan(c, 0, L, total);
+  // exclusive scan of the per-split counts, PER splits per thread
+  {
+    constexpr int PER = kNSplitMax / NT;
+    int v[PER], loc = 0;
 #pragma unroll
-    for (int u = 0; u < WPT; ++u) c += __popc(wv[u]);
-    int total;
-    int at = wg_scan(c, 0, L, total);
-#pragma unroll
-    for (int u = 0; u < WPT; ++u) {
-      pre[WPT * threadIdx.x + u] = (uint16_t)at;
-      at += __popc(wv[u]);
+    for (int u = 0; u < PER; ++u) {
+      const int r = PER * threadIdx.x + u;
+      v[u] = r < nspl ? cnt[r] : 0;
+      loc += v[u];
     }
-    __syncthreads();
-    for (int s0 = threadIdx.x; s0 < ns; s0 += 4 * NT) {
-      uint32_t k[4], o[4];
-      int slot[4];
+    int tot2;
+    int b = wg_scan(loc, 1, L, tot2);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int r = PER * threadIdx.x + u;
+      if (r < nspl) cnt[r] = b;
+      b += v[u];
+    }
+  }
+  // run starts: the taken count before the first entry of each split's run
+  {
+    int fs = fs0;
+    uint32_t prev = b0 > 0 ? div_split((uint32_t)L.sel_pos[b0 - 1], split, inv_split) : 0xffffffffu;
+    for (int q0 = b0; q0 < b1; q0 += 4) {
+      uint32_t k[4];
+      int32_t ps[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int s = min(s0 + u * NT, ns - 1);
-        k[u] = L.sel_key[s];
-        o[u] = (uint32_t)(L.sel_pos[s] - w0);
+        const int q = min(q0 + u, b1 - 1);
+        k[u] = L.sel_key[q];
+        ps[u] = L.sel_pos[q];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t oo = min(o[u], 32u * kWinWords - 1u);
-        slot[u] = done + (int)pre[oo >> 5] + __popc(bm[oo >> 5] & ((1u << (oo & 31)) - 1u));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (s0 + u * NT < ns && o[u] < 32u * kWinWords && take(k[u], (int32_t)(o[u] + w0)) &&
-            slot[u] < K_eff) {
-          p.out_idx[(size_t)t * p.K + slot[u]] = (int)(o[u] + w0);
-          if (p.out_score) p.out_score[(size_t)t * p.K + slot[u]] = key_to_float(k[u]);
+        if (q0 + u < b1) {
+          const uint32_t r = div_split((uint32_t)ps[u], split, inv_split);
+          if (r != prev) first[r] = fs;
+          prev = r;
+          fs += take(k[u], ps[u]);
         }
       }
     }
-    done += total;
   }
-  pad_output(p, t, min(done, K_eff));
+  __syncthreads();
+  {
+    int fs = fs0;
+    for (int q0 = b0; q0 < b1; q0 += 4) {
+      uint32_t k[4];
+      int32_t ps[4];
+      int base[4], fst[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = min(q0 + u, b1 - 1);
+        k[u] = L.sel_key[q];
+        ps[u] = L.sel_pos[q];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t r = div_split((uint32_t)ps[u], split, inv_split);
+        base[u] = cnt[r];
+        fst[u] = first[r];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if ((q0 + u < b1) & take(k[u], ps[u])) {
+          const int slot = base[u] + fs - fst[u];
+          if (slot < K_eff) {
+            p.out_idx[(size_t)t * p.K + slot] = ps[u];
+            if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(k[u]);
+          }
+          ++fs;
+        }
+      }
+    }
+  }
+  pad_output(p, t, min(total, K_eff));
   if (threadIdx.x == 0) {
     st_agent(p.counters + 2 * t, 0u);
     st_agent(p.counters + 2 * t + 1, 0u);
@@ -1254,7 +1275,7 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff,
 template <int MODE>
 __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   constexpr int RB = region_bytes<MODE>();
-  static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kWinWords * 3 / 2, "shared region");
+  static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kNSplitMax, "shared region");
   __shared__ __attribute__((aligned(16))) uint8_t s_region[RB];
   __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSplitMax];
   __shared__ __attribute__((aligned(16))) float s_w[NWAVE * 64];
