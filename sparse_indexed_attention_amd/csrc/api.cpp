@@ -113,6 +113,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
   p.max_visible = queries->max_visible;
   p.q_dtype = q_dtype;
   p.k_dtype = k_dtype;
+  p.grid = pl.grid;
   p.split = pl.split;
   p.nsplit_max = pl.nsplit_max;
   p.cap = pl.cap;

@@ -15,14 +15,16 @@ constexpr int kSplitMax = 2048;        // context positions scored by one workgr
 constexpr int kNSplitMax = 2048;       // context splits per query
 constexpr int kMaxTopK = 2048;         // largest top_k
 constexpr int kMinFastBlock = 32;      // smallest page size of the MFMA path (one page per 32-position group)
+constexpr int kMinSplit = 512;         // shortest context split
 constexpr int kGenericMaxHD = 8192;    // n_heads * head_dim on the reference path
 constexpr int kGenericMaxHeads = 256;
 
 enum { kDtF32 = 0, kDtBF16 = 1, kDtFP8 = 2 };
 
 struct IndexerPlan {
+  int32_t grid;         // workgroups of the launch
   int32_t split;        // positions per context split (multiple of 64)
-  int32_t nsplit_max;   // splits of the longest visible prefix
+  int32_t nsplit_max;   // splits of the longest visible prefix (header rows per query)
   int32_t cap;          // candidate slots per split = min(split, top_k)
   size_t off_counters, off_hdr, off_ckey, off_cpos, bytes;
 };
@@ -37,7 +39,7 @@ struct IndexerParams {
   const int32_t* q_vis;
   int32_t T, H, D, K, max_visible;
   int32_t q_dtype, k_dtype;
-  int32_t split, nsplit_max, cap;
+  int32_t grid, split, nsplit_max, cap;
   int32_t* out_idx;
   float* out_score;
   uint32_t* counters;   // [T][2]         arrivals, flat-list length per query (self-resetting)
@@ -46,10 +48,11 @@ struct IndexerParams {
   int32_t* cand_pos;    // [T][2 * nsplit * cap] (+256) ... and positions
 };
 
-// Entries of one query's flat candidate list: room for every split's run twice (a re-scored
-// split appends a new run), rounded to whole 256-byte lines.
-__host__ __device__ inline size_t indexer_flat_stride(int32_t nsplit_max, int32_t cap) {
-  return ((size_t)2 * nsplit_max * cap + 63) / 64 * 64;
+// Entries of one query's flat candidate list.  A split emits at most its length, and a
+// re-scored split appends a new run of at most its length, so twice the longest visible prefix
+// is room enough; rounded to whole 256-byte lines.
+__host__ __device__ inline size_t indexer_flat_stride(int32_t max_visible) {
+  return ((size_t)2 * max_visible + 64 + 63) / 64 * 64;
 }
 
 IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k);

@@ -1058,7 +1058,7 @@ __device__ __forceinline__ int gather_ordered(int n, KeyOf key_of, PosOf pos_of,
 // Selection and output over the flat list, keys from key_of(i), positions from pos_of(i).
 // Returns false (writing nothing) when a split's threshold lies above the K_eff-th key T.
 template <class KeyOf, class PosOf>
-__device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int K_eff,
+__device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int K_eff, int split_len,
                                              const MergeHdr& mh, KeyOf key_of, PosOf pos_of,
                                              const Lds& L, uint32_t& T, int& gt, bool& enough) {
   const int n = mh.n_alloc;
@@ -1123,13 +1123,13 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
   // position order, and split r covers positions [r*split, (r+1)*split).  So the slot of a
   // taken entry of split r is the count taken in splits before r plus its rank in its run:
   // per-split counts (scanned in split order) and, per run, the taken count before its start.
-  const int nspl = (min(p.q_vis[t], p.max_visible) + p.split - 1) / p.split;
+  const int nspl = (min(p.q_vis[t], p.max_visible) + split_len - 1) / split_len;
   int* cnt = L.hist;                        // [nspl] taken per split, then the scan
   int* first = (int*)L.flat;                // [nspl] taken entries before the run of a split
   const int E = ((ns + NT - 1) / NT) | 1;
   const int b0 = min(ns, E * (int)threadIdx.x), b1 = min(ns, b0 + E);
-  const uint32_t split = (uint32_t)p.split;
-  const float inv_split = 1.0f / (float)p.split;
+  const uint32_t split = (uint32_t)split_len;
+  const float inv_split = 1.0f / (float)split_len;
   __syncthreads();   // the histogram and the flat area are free
   for (int r = threadIdx.x; r < nspl; r += NT) cnt[r] = 0;
   __syncthreads();
@@ -1240,10 +1240,10 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
 // agent-scope direct-to-LDS loads, then selects.  T, gt and enough are kept for the
 // re-scoring of failing splits.
 template <int MODE>
-__device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff,
+__device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, int split,
                                       const MergeHdr& mh, const Lds& L, uint32_t& T, int& gt,
                                       bool& enough) {
-  const size_t qflat = (size_t)t * indexer_flat_stride(p.nsplit_max, p.cap);
+  const size_t qflat = (size_t)t * indexer_flat_stride(p.max_visible);
   const uint32_t* gk = p.cand_key + qflat;
   const int32_t* gp = p.cand_pos + qflat;
   const int n = mh.n_alloc;
@@ -1251,7 +1251,7 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff,
   constexpr int FW = flat_words<MODE>();
   auto gkey = [&](int i) { return ld_agent(gk + i); };
   auto gpos = [&](int i) { return ld_agent(gp + i); };
-  if (nr > FW) return merge_select(p, t, K_eff, mh, gkey, gpos, L, T, gt, enough);
+  if (nr > FW) return merge_select(p, t, K_eff, split, mh, gkey, gpos, L, T, gt, enough);
   const bool pos_in = 2 * nr <= FW;
   uint32_t* fk = L.flat;
   int32_t* fp = (int32_t*)(L.flat + nr);
@@ -1263,8 +1263,8 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff,
   wait_vmcnt<0>();
   __syncthreads();
   auto lkey = [&](int i) { return fk[i]; };
-  if (pos_in) return merge_select(p, t, K_eff, mh, lkey, [&](int i) { return fp[i]; }, L, T, gt, enough);
-  return merge_select(p, t, K_eff, mh, lkey, gpos, L, T, gt, enough);
+  if (pos_in) return merge_select(p, t, K_eff, split, mh, lkey, [&](int i) { return fp[i]; }, L, T, gt, enough);
+  return merge_select(p, t, K_eff, split, mh, lkey, gpos, L, T, gt, enough);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1301,13 +1301,20 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   Lds Lm = L;
   Lm.hist = (int*)s_keys;
 
-  const int t = blockIdx.y, j = blockIdx.x;
+  // Workgroup -> (query t, split j).  Dispatch follows the linear index: the splits that exist
+  // for every query (small j) come first and the empty ones of short queries last, so the live
+  // workgroups spread over all the CUs, and within a block of T workgroups the queries are
+  // rotated by j so that each query's splits spread over the XCDs.
+  const int L0 = blockIdx.x;
+  const int j = L0 / p.T, t = (L0 - j * p.T + j) % p.T;
+  const int split = p.split;
+  const int cap = min(split, p.K);
   const int V = min(p.q_vis[t], p.max_visible);
   if (V <= 0) {
     if (j == 0) pad_output(p, t, 0);
     return;
   }
-  const int nsplit = (V + p.split - 1) / p.split;
+  const int nsplit = (V + split - 1) / split;
   if (j >= nsplit) return;
   const int seq = p.q_seq[t];
   const int K_eff = min(p.K, V);
@@ -1328,9 +1335,9 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   uint32_t T = 0u;
   int gt = 0;
   bool enough = false;
-  const size_t qflat = (size_t)t * indexer_flat_stride(p.nsplit_max, p.cap);   // the query's flat list
+  const size_t qflat = (size_t)t * indexer_flat_stride(p.max_visible);   // the query's flat list
   for (;;) {
-    const int start = cur * p.split, len = min(p.split, V - start);
+    const int start = cur * split, len = min(split, V - start);
     uint32_t klo, khi;
     score_split<MODE>(p, t, seq, start, len, L, gsp, klo, khi);
 
@@ -1353,7 +1360,7 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
       {
         const float e = (float)K_eff * (float)len / (float)V;
         int m = (int)ceilf(e + 4.f * sqrtf(e) + 4.f);
-        const int hard = min(len, p.cap);
+        const int hard = min(len, cap);
         m = min(m, hard);
         const int soft = min(hard, 2 * m);
         KeyBlock<kSplitMax / NT> kb;
@@ -1373,7 +1380,7 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
           }
         }
         // this split's run of the flat list
-        cnt = min(cnt, p.cap);
+        cnt = min(cnt, cap);
         if (threadIdx.x == 0) L.bcast[1] = (int)add_agent(p.counters + 2 * t + 1, (uint32_t)cnt);
         __syncthreads();
         const size_t cb = qflat + (size_t)L.bcast[1];
@@ -1401,7 +1408,7 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
         L.bcast[0] = add_agent(p.counters + 2 * t, 1u) == (uint32_t)(nsplit - 1);
       __syncthreads();
       if (!L.bcast[0]) return;
-      if (merge<MODE>(p, t, K_eff, load_headers(p, t, nsplit, Lm), Lm, T, gt, enough)) return;
+      if (merge<MODE>(p, t, K_eff, split, load_headers(p, t, nsplit, Lm), Lm, T, gt, enough)) return;
       refill = true;
       cur = -1;
     } else {
@@ -1442,7 +1449,7 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
     wait_all_memory();
     __syncthreads();
     if (nxt < 0) {
-      merge<MODE>(p, t, K_eff, load_headers(p, t, nsplit, Lm), Lm, T, gt, enough);   // certified
+      merge<MODE>(p, t, K_eff, split, load_headers(p, t, nsplit, Lm), Lm, T, gt, enough);   // certified
       return;
     }
     cur = nxt;
@@ -1457,14 +1464,15 @@ IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
   if (const char* e = getenv("DSA_INDEXER_TARGET_WG")) target_wg = atoll(e) > 0 ? atoll(e) : 512;
   int64_t split = ((int64_t)T * max_visible + target_wg - 1) / target_wg;
   split = (split + 63) / 64 * 64;
-  if (split < 512) split = 512;
+  if (split < kMinSplit) split = kMinSplit;
   if (split > kSplitMax) split = kSplitMax;
   pl.split = (int32_t)split;
   pl.nsplit_max = (int32_t)((max_visible + split - 1) / split);
   pl.cap = (int32_t)(split < top_k ? split : top_k);
+  pl.grid = pl.nsplit_max * T;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   // flat candidate lists, plus one 1 KB load of slack past the last
-  const size_t slots = (size_t)T * indexer_flat_stride(pl.nsplit_max, pl.cap) + 256;
+  const size_t slots = (size_t)T * indexer_flat_stride(max_visible) + 256;
   size_t off = 0;
   pl.off_counters = off; off = al(off + (size_t)T * 8);
   pl.off_hdr = off;      off = al(off + (size_t)T * pl.nsplit_max * 32);
@@ -1475,7 +1483,7 @@ IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
 }
 
 hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream) {
-  const dim3 grid(p.nsplit_max, p.T), block(NT);
+  const dim3 grid(p.grid), block(NT);
   if (!fast_path) hipLaunchKernelGGL(indexer_topk_kernel<0>, grid, block, 0, stream, p);
   else if (p.k_dtype == kDtFP8) hipLaunchKernelGGL(indexer_topk_kernel<2>, grid, block, 0, stream, p);
   else hipLaunchKernelGGL(indexer_topk_kernel<1>, grid, block, 0, stream, p);
