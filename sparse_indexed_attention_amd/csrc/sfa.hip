@@ -42,6 +42,7 @@ constexpr int kTileSlots = kTileRows * kLdsChunks;       // 2336
 constexpr int kTileBytes = kTileSlots * 16;              // 37376
 constexpr int kTileLoads = (kTileSlots + 63) / 64;       // 37 direct-to-LDS loads per tile
 constexpr int kTileBufs = 3;                             // LDS tile buffers (two tiles ahead)
+constexpr int kBtLds = 8192;                             // block-table entries staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -73,6 +74,12 @@ __device__ __forceinline__ void load16_to_lds(const void* gaddr, uint32_t lds_in
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(gaddr), "s"(lds) : "memory", "m0");
 }
+// 4 bytes per active lane from a per-lane global address into LDS at lds + 4 * lane.
+__device__ __forceinline__ void load4_to_lds(const void* gaddr, uint32_t lds_in) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gaddr), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Row of the 32x32 MFMA accumulator element r held by lane half h (lane column = l & 31).
@@ -96,6 +103,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   constexpr int LPW_MIN = kTileLoads / NW;          // ... and at least
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kTileBufs][kTileBytes];
   __shared__ int32_t rows[kMaxTopK];                // pool row of each slice entry, -1 if none
+  __shared__ int32_t bt_lds[kBtLds];                // the sequence's block-table row
   __shared__ __attribute__((aligned(16))) float hv[NW][32];   // per-head values of a wave
 
   // workgroup -> (query, head group, slice); consecutive workgroups go to different XCDs, so
@@ -125,15 +133,44 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
 #pragma unroll
     for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qb + 16 * s);
   }
-  // pool rows of the slice
+  // Pool rows of the slice.  The positions, and the sequence's whole block-table row when it
+  // fits in LDS, are requested together with the queries, so the lookup costs one memory round
+  // trip instead of two chained ones.
+  constexpr int UI = kMaxTopK / NTS;                 // slice entries per thread (at most)
+  int32_t posr[UI];
   {
     const int32_t* idx = p.idx + (size_t)t * p.K + j0;
-    for (int i = tid; i < ntiles * kTileRows; i += NTS) {
-      const int pos = i < nrows ? idx[i] : -1;
-      rows[i] = pos >= 0 ? (int32_t)pool_row(p.L, seq, pos) : -1;
+#pragma unroll
+    for (int u = 0; u < UI; ++u) {
+      const int i = tid + u * NTS;
+      posr[u] = i < nrows ? idx[i] : -1;
     }
   }
+  const bool stage_bt = p.L.bt != nullptr && p.L.bt_stride <= kBtLds;
+  if (stage_bt) {
+    const int32_t* btrow = p.L.bt + (size_t)seq * p.L.bt_stride;
+    for (int c0 = 64 * wave; c0 < p.L.bt_stride; c0 += NTS)
+      if (c0 + lane < p.L.bt_stride) load4_to_lds(btrow + c0 + lane, lds_u32(bt_lds + c0));
+  }
   wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < UI; ++u) {
+    const int i = tid + u * NTS;
+    if (i < ntiles * kTileRows) {
+      const int pos = posr[u];
+      int32_t row = -1;
+      if (pos >= 0) {
+        if (stage_bt) {
+          const int sh = p.L.bs_log2;
+          row = (bt_lds[pos >> sh] << sh) | (pos & ((1 << sh) - 1));
+        } else {
+          row = (int32_t)pool_row(p.L, seq, pos);
+        }
+      }
+      rows[i] = row;
+    }
+  }
   __syncthreads();
 
   const uint8_t* kv = (const uint8_t*)p.kv;
