@@ -42,7 +42,8 @@ constexpr int kTileSlots = kTileRows * kLdsChunks;       // 2336
 constexpr int kTileBytes = kTileSlots * 16;              // 37376
 constexpr int kTileLoads = (kTileSlots + 63) / 64;       // 37 direct-to-LDS loads per tile
 constexpr int kTileBufs = 3;                             // LDS tile buffers (two tiles ahead)
-constexpr int kBtLds = 8192;                             // block-table entries staged in LDS
+constexpr int kBtLds = 4096;                             // block-table entries staged in LDS
+constexpr int kPStride = 80;                             // bytes per head row of the shared P tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -104,7 +105,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kTileBufs][kTileBytes];
   __shared__ int32_t rows[kMaxTopK];                // pool row of each slice entry, -1 if none
   __shared__ int32_t bt_lds[kBtLds];                // the sequence's block-table row
-  __shared__ __attribute__((aligned(16))) float hv[NW][32];   // per-head values of a wave
+  __shared__ __attribute__((aligned(16))) float hv[NW * 32];   // per-head values
+  __shared__ __attribute__((aligned(16))) uint8_t plds[NW * 32 * kPStride];   // P of the tile
 
   // workgroup -> (query, head group, slice); consecutive workgroups go to different XCDs, so
   // the head groups of one (query, slice) are placed 8 apart and share an XCD's L2
@@ -182,11 +184,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   // on that.
   auto issue = [&](int tile, int buf) {
     uint8_t* tb = tiles[buf];
+    // an opaque zero: the slot arithmetic below is redone per call instead of being hoisted
+    // out of the tile loop into registers that the attention step needs
+    int z0 = 0;
+    asm volatile("" : "+v"(z0));
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int I = wave + NW * u;
       if (LPW != LPW_MIN && I >= kTileLoads) break;
-      const int P = 64 * I + lane;
+      const int P = 64 * I + lane + z0;
       const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
       if (P < kTileSlots && ch < kRowChunks) {
         const int row = rows[tile * kTileRows + rr];
@@ -235,8 +241,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   // 2^64 bf16 operands and fp32 sums of 2^11 terms keep their full relative precision.  A
   // head whose scores pass m2 + 64 is flagged, and the combine kernel recomputes it with the
   // reference method.
+  //
+  // O += P . V is split by output dims: wave w owns dims [DW*w, DW*w + DW) of every head of
+  // the workgroup, so each wave reads only its quarter of V from LDS (the transposing reads
+  // move half the bytes per instruction of plain ones, and V was the largest LDS stream).
+  // The probabilities computed by the head-owner waves are exchanged through a small LDS tile.
+  constexpr int DW = kSfaDv / NW;                  // output dims per wave
+  constexpr int NB = DW / 32;                      // 32-dim blocks per wave
   float m2 = -INFINITY, l = 0.f;
-  f32x16 o[16];
+  f32x16 o[NW * NB];                               // [head block][dim block]
   bool over = false;
   // V operand for dims 32nb .. +31, k step kk: in each 16-lane group, lane i supplies row
   // 16kk + 8jj + 4hh + i/4, dims 32nb + 16(c/16) + 4(i%4) .. +3; the transposing read returns
@@ -261,16 +274,29 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
       pe[e] = live ? __builtin_amdgcn_exp2f(z[e] - m2) : 0.f;
       l += pe[e];
     }
-    // P as the A operand of k step kk: k slot 8hh + u is row 16kk + 8(u/4) + 4hh + u%4,
-    // i.e. accumulator elements 8kk .. 8kk+7 as they stand
-    bf16x8 pa[2];
+    // P as the A operand of k step kk: k slot 8hh + u is row 16kk + 8(u/4) + 4hh + u%4, i.e.
+    // accumulator elements 8kk .. 8kk+7 as they stand.  Head row c of this wave goes to the
+    // shared tile in that k order, 16 bytes per k step.
+    {
+      bf16x8 pw[2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      pa[0][u] = (__bf16)pe[u];
-      pa[1][u] = (__bf16)pe[8 + u];
+      for (int u = 0; u < 8; ++u) {
+        pw[0][u] = (__bf16)pe[u];
+        pw[1][u] = (__bf16)pe[8 + u];
+      }
+      uint8_t* prow = plds + (32 * wave + c) * kPStride + 16 * hh;
+      *(bf16x8*)prow = pw[0];
+      *(bf16x8*)(prow + 32) = pw[1];
     }
+    __syncthreads();                             // every head's P is in the tile
+    bf16x8 pa[NW][2];
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pa[hb][kk] = *(const bf16x8*)(plds + (32 * hb + c) * kPStride + 32 * kk + 16 * hh);
     auto vread = [&](int nb, s16x4 (&v)[4]) {
-      const int dim = 32 * nb + vdim;
+      const int dim = DW * wave + 32 * nb + vdim;
       const int cho = tile_off(0, dim >> 3) + 2 * (dim & 7);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -280,21 +306,25 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     s16x4 vb[2][4];
     vread(0, vb[0]);
 #pragma unroll
-    for (int nb = 0; nb < 16; ++nb) {
-      if (nb + 1 < 16) vread(nb + 1, vb[(nb + 1) & 1]);
+    for (int nb = 0; nb < NB; ++nb) {
+      if (nb + 1 < NB) vread(nb + 1, vb[(nb + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       const s16x4* v = vb[nb & 1];
+      bf16x8 b[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[2 * kk], v[2 * kk + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], b, o[nb], 0, 0, 0);
-      }
+      for (int kk = 0; kk < 2; ++kk)
+        b[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[2 * kk], v[2 * kk + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          o[hb * NB + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb][kk], b[kk], o[hb * NB + nb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
 #pragma unroll
-  for (int n = 0; n < 16; ++n) o[n] = f32x16{};
+  for (int n = 0; n < NW * NB; ++n) o[n] = f32x16{};
   // Tiles stream through kTileBufs LDS buffers, kTileBufs - 1 of them ahead of the one being
   // computed.
   static_assert(kTileBufs == 3, "prologue below issues three tiles");
@@ -309,52 +339,62 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     else wait_vmcnt<0>();                        // this wave's loads of `tile` have landed
     __syncthreads();                             // ... and every other wave's
     attend(tile, tiles[buf]);
-    __syncthreads();                             // the buffer is free again
+    __syncthreads();                             // the buffer and the P tile are free again
     if (tile + kTileBufs < ntiles) issue(tile + kTileBufs, buf);
     buf = buf == kTileBufs - 1 ? 0 : buf + 1;
   }
 
   // per-head totals: the two lane halves of a column hold disjoint rows of its head
   const float lt = xhalf_sum(l);
-  if (hh == 0) hv[wave][c] = lt > 0.f ? 1.f / lt : 0.f;
+  if (hh == 0) hv[32 * wave + c] = lt > 0.f ? 1.f / lt : 0.f;
   const uint32_t flagword = (uint32_t)__ballot(over);   // bit c: head h0 + c
+  __syncthreads();                                      // every head's 1 / l
+  const int hgb = hg * 32 * NW;                         // first head of the workgroup
+  // accumulator (hb, nb) element 4j + i of lane (hh, c): head hgb + 32hb + 8j + 4hh + i,
+  // dim DW*wave + 32nb + c
   if (p.nsplit == 1) {
-    uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + h0) * kSfaDv;
+    uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + hgb) * kSfaDv + DW * wave + c;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 inv = *(const f32x4*)&hv[wave][8 * j + 4 * hh];
+    for (int hb = 0; hb < NW; ++hb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hd = 8 * j + 4 * hh + i;
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 inv = *(const f32x4*)&hv[32 * hb + 8 * j + 4 * hh];
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb)
-          out[hd * kSfaDv + 32 * nb + c] = __builtin_bit_cast(uint16_t, (__bf16)(o[nb][4 * j + i] * inv[i]));
+        for (int i = 0; i < 4; ++i) {
+          const int hd = 32 * hb + 8 * j + 4 * hh + i;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            out[hd * kSfaDv + 32 * nb] = __builtin_bit_cast(uint16_t, (__bf16)(o[hb * NB + nb][4 * j + i] * inv[i]));
+        }
       }
-    }
     if (p.lse && hh == 0)
       p.lse[(size_t)t * p.H + h0 + c] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
   } else {
-    // Partial of this slice: O / l in fp16, stored as the accumulators lie in the registers.
-    // Record (j, np) of lane (hh, c) holds heads 8j + 4hh + i (i < 4) at dims 32(2np + s) + c
-    // (s < 2), value 4s + i.  A wave's 32 heads form one 32 KB block per (query, slice).
-    uint8_t* po = (uint8_t*)p.part_o + ((((size_t)t * (p.H / 32) + hw) * p.nsplit + r) * 32) * 1024 + 16 * lane;
+    // Partial of this slice: O / l in fp16, stored as the accumulators lie in the registers,
+    // one 32 KB block per (query, head group, slice, wave).  Record (hb*4 + j)*(NB/2) + np of
+    // lane (hh, c) holds heads 32hb + 8j + 4hh + i (i < 4) at dims DW*wave + 32(2np + s) + c
+    // (s < 2), value 4s + i.
+    uint8_t* po = (uint8_t*)p.part_o +
+                  ((((size_t)t * p.n_hg + hg) * p.nsplit + r) * NW + wave) * 32 * 1024 + 16 * lane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 inv = *(const f32x4*)&hv[wave][8 * j + 4 * hh];
+    for (int hb = 0; hb < NW; ++hb)
 #pragma unroll
-      for (int np = 0; np < 8; ++np) {
-        uint32_t w[4];
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 inv = *(const f32x4*)&hv[32 * hb + 8 * j + 4 * hh];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int np = 0; np < NB / 2; ++np) {
+          uint32_t w[4];
 #pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const _Float16 a = (_Float16)(o[2 * np + s][4 * j + i] * inv[i]);
-            const _Float16 b = (_Float16)(o[2 * np + s][4 * j + i + 1] * inv[i + 1]);
-            w[2 * s + i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-          }
-        *(u32x4*)(po + (size_t)(8 * j + np) * 1024) = u32x4{w[0], w[1], w[2], w[3]};
+          for (int sd = 0; sd < 2; ++sd)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              const _Float16 a = (_Float16)(o[hb * NB + 2 * np + sd][4 * j + i] * inv[i]);
+              const _Float16 b = (_Float16)(o[hb * NB + 2 * np + sd][4 * j + i + 1] * inv[i + 1]);
+              w[2 * sd + i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+            }
+          *(u32x4*)(po + (size_t)((hb * 4 + j) * (NB / 2) + np) * 1024) = u32x4{w[0], w[1], w[2], w[3]};
+        }
       }
-    }
     if (hh == 0) {
       float* pm = p.part_ml + (((size_t)t * p.H + h0 + c) * p.nsplit + r) * 2;
       pm[0] = m2;
@@ -437,18 +477,18 @@ __global__ __launch_bounds__(kRefThreads) void sfa_reference_kernel(SfaParams p)
   reference_head<kRefThreads>(p, blockIdx.y, blockIdx.x, ws);
 }
 
-// Merge of the index-list slices.  A workgroup owns (query, 8 heads, half of the 512 output
-// dims): the log-sum-exp weights of the slices, then per thread one 16-byte record of the
-// fp16 partials per slice, summed in fp32.  Heads flagged by the MFMA kernel (scores far above
-// the exponent reference) are recomputed by the reference method in the first half's
-// workgroup and skipped by the other; a head whose merged output is not finite (a partial
-// beyond the fp16 range) is recomputed by the workgroup that saw it.  With a single slice the
-// MFMA kernel wrote the output and only the flags are checked.
+// Merge of the index-list slices.  A workgroup owns (query, 16 heads of one 32-head block, the
+// output dims of one wave of the MFMA kernel): the log-sum-exp weights of the slices, then per
+// thread one 16-byte record of the fp16 partials per slice, summed in fp32.  Heads flagged by
+// the MFMA kernel (scores far above the exponent reference) are recomputed by the reference
+// method in the workgroup of the first dim range and skipped by the others; a head whose
+// merged output is not finite (a partial beyond the fp16 range) is recomputed by the
+// workgroup that saw it.  With a single slice the MFMA kernel wrote the output and only the
+// flags are checked.
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSlices = 64;
 static_assert(kMaxTopK / kTileRows <= kMaxSlices, "a slice holds at least one tile");
-constexpr int kCombineFirst = 32;                    // partial records loaded before the weights
-constexpr int kCombineBatch = 16;                    // ... and per batch after them
+constexpr int kCombineBatch = 16;                    // partial loads in flight per thread
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -461,101 +501,127 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams p) {
   __shared__ RefSmem ws;
-  __shared__ __attribute__((aligned(16))) float wgt[kMaxSlices][8];
+  __shared__ __attribute__((aligned(16))) float wgt[kMaxSlices][16];
   __shared__ uint32_t flagged, nonfinite;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_hw = p.H / 32;
-  const int half = blockIdx.x & 1, j = (blockIdx.x >> 1) & 3, hw = blockIdx.x >> 3;
+  const int NW = p.heads_per_wg / 32;                 // waves (dim ranges) of the MFMA kernel
+  const int DW = kSfaDv / NW, NB = DW / 32;
+  const int half = blockIdx.x & 1;
+  const int hb = (blockIdx.x >> 1) % NW;
+  const int w = (blockIdx.x >> 1) / NW % NW;
+  const int hg = (blockIdx.x >> 1) / (NW * NW);
   const int t = blockIdx.y;
-  const int hb = hw * 32 + 8 * j;                     // heads hb .. hb + 7
+  const int hw = hg * NW + hb;                        // 32-head block
+  const int hb0 = hw * 32 + 16 * half;                // heads hb0 .. hb0 + 15
   const int S = p.nsplit;
-  // record np of lane ln: heads hb + 4hh + i, dims 64np + 32s + c, value 4s + i.  The first
-  // slices' records are requested before anything else, so that their latency overlaps the
-  // weight computation.
-  const int np = 4 * half + wave, hh = lane >> 5, c = lane & 31;
-  const uint8_t* src = (const uint8_t*)p.part_o +
-                       ((((size_t)t * n_hw + hw) * S * 32) + 8 * j + np) * 1024 + 16 * lane;
-  u32x4 w0[kCombineFirst];
-  if (S > 1) {
-#pragma unroll
-    for (int u = 0; u < kCombineFirst; ++u)
-      w0[u] = u < S ? *(const u32x4*)(src + (size_t)u * 32 * 1024) : u32x4{0u, 0u, 0u, 0u};
-  }
+  // slot (record, lane): record (hb*4 + j)*(NB/2) + np with j = 2*half + jl, value 4s + i:
+  // head hb0 + 8jl + 4hh + i, dim DW*w + 32(2np + s) + c
+  const int nslot = NB * 64;
+  const uint8_t* blk = (const uint8_t*)p.part_o + (((size_t)t * p.n_hg + hg) * S * NW + w) * 32 * 1024;
+  const size_t rstride = (size_t)NW * 32 * 1024;      // from one slice to the next
   if (wave == 0) {
-    uint32_t f = lane < S ? p.flags[((size_t)t * n_hw + hw) * S + lane] : 0u;
+    uint32_t f = lane < S ? p.flags[((size_t)t * (p.H / 32) + hw) * S + lane] : 0u;
     for (int off = 32; off >= 1; off >>= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
     if (lane == 0) {
-      flagged = (f >> (8 * j)) & 0xffu;
+      flagged = (f >> (16 * half)) & 0xffffu;
       nonfinite = 0u;
     }
   }
   if (S > 1) {
-    // weights of heads `wave` and `wave + 4`, lane r holding slice r
-    const int k0 = wave, k1 = wave + 4;
-    float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
-    if (lane < S) {
-      const float2 a = *(const float2*)(p.part_ml + (((size_t)t * p.H + hb + k0) * S + lane) * 2);
-      const float2 b = *(const float2*)(p.part_ml + (((size_t)t * p.H + hb + k1) * S + lane) * 2);
-      m0 = a.x, l0 = a.y, m1 = b.x, l1 = b.y;
+    // weights of heads 4*wave .. 4*wave + 3 (of the 16), lane r holding slice r
+    float m[4], lv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      m[k] = -INFINITY;
+      lv[k] = 0.f;
+      if (lane < S) {
+        const float2 a = *(const float2*)(p.part_ml + (((size_t)t * p.H + hb0 + 4 * wave + k) * S + lane) * 2);
+        m[k] = a.x;
+        lv[k] = a.y;
+      }
     }
-    const float M0 = wave_max(m0), M1 = wave_max(m1);
-    const float e0 = (M0 == -INFINITY || lane >= S) ? 0.f : exp2f(m0 - M0) * l0;
-    const float e1 = (M1 == -INFINITY || lane >= S) ? 0.f : exp2f(m1 - M1) * l1;
-    const float L0 = wave_sum(e0), L1 = wave_sum(e1);
-    if (lane < S) {
-      wgt[lane][k0] = L0 > 0.f ? e0 / L0 : 0.f;
-      wgt[lane][k1] = L1 > 0.f ? e1 / L1 : 0.f;
-    }
-    if (p.lse && half == 0 && lane == 0) {
-      p.lse[(size_t)t * p.H + hb + k0] = L0 > 0.f ? (M0 + log2f(L0)) * kLn2 : -INFINITY;
-      p.lse[(size_t)t * p.H + hb + k1] = L1 > 0.f ? (M1 + log2f(L1)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float M = wave_max(m[k]);
+      const float e = (M == -INFINITY || lane >= S) ? 0.f : exp2f(m[k] - M) * lv[k];
+      const float Lsum = wave_sum(e);
+      if (lane < S) wgt[lane][4 * wave + k] = Lsum > 0.f ? e / Lsum : 0.f;
+      if (p.lse && w == 0 && lane == 0)
+        p.lse[(size_t)t * p.H + hb0 + 4 * wave + k] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
     }
   }
   __syncthreads();
   if (S > 1) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int slot = tid; slot < nslot; slot += kCombineThreads) {
+      const int ln = slot & 63, rl = slot >> 6;        // lane of the record, record of the WG
+      const int jl = rl / (NB / 2), np = rl % (NB / 2);
+      const int rec = (hb * 4 + 2 * half + jl) * (NB / 2) + np;
+      const int hh = ln >> 5, c = ln & 31;
+      const uint8_t* src = blk + (size_t)rec * 1024 + 16 * ln;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int r0 = 0; r0 < S; r0 += kCombineBatch) {
+        u32x4 v[kCombineBatch];
 #pragma unroll
-    for (int u = 0; u < kCombineFirst; ++u) {
-      const f32x4 wr = u < S ? *(const f32x4*)&wgt[u][4 * hh] : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kCombineBatch; ++u)
+          v[u] = r0 + u < S ? *(const u32x4*)(src + (size_t)(r0 + u) * rstride) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const uint32_t bits = (w0[u][v >> 1] >> (16 * (v & 1))) & 0xffffu;
-        acc[v] += wr[v & 3] * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-      }
-    }
-    for (int r0 = kCombineFirst; r0 < S; r0 += kCombineBatch) {
-      u32x4 w[kCombineBatch];
+        for (int u = 0; u < kCombineBatch; ++u) {
+          const f32x4 wr = r0 + u < S ? *(const f32x4*)&wgt[r0 + u][8 * jl + 4 * hh] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u)
-        w[u] = r0 + u < S ? *(const u32x4*)(src + (size_t)(r0 + u) * 32 * 1024) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u) {
-        if (r0 + u >= S) break;
-        const f32x4 wr = *(const f32x4*)&wgt[r0 + u][4 * hh];
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const uint32_t bits = (w[u][v >> 1] >> (16 * (v & 1))) & 0xffffu;
-          acc[v] += wr[v & 3] * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t bits = (v[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            acc[e] += wr[e & 3] * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+          }
         }
       }
-    }
-    const uint32_t skip = flagged >> (4 * hh);
-    uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + hb + 4 * hh) * kSfaDv + 64 * np + c;
+      const uint32_t skip = flagged >> (8 * jl + 4 * hh);
+      uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + hb0 + 8 * jl + 4 * hh) * kSfaDv + DW * w + 64 * np + c;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int i = v & 3, sd = v >> 2;
-      if ((skip >> i) & 1u) continue;
-      if (!__builtin_isfinite(acc[v])) atomicOr(&nonfinite, 1u << (4 * hh + i));
-      out[i * kSfaDv + 32 * sd] = (uint16_t)f32_to_bf16_bits(acc[v]);
+      for (int e = 0; e < 8; ++e) {
+        const int i = e & 3, sd = e >> 2;
+        if ((skip >> i) & 1u) continue;
+        if (!__builtin_isfinite(acc[e])) atomicOr(&nonfinite, 1u << (8 * jl + 4 * hh + i));
+        out[i * kSfaDv + 32 * sd] = (uint16_t)f32_to_bf16_bits(acc[e]);
+      }
     }
   }
   __syncthreads();
-  uint32_t m = (half == 0 ? flagged : 0u) | nonfinite;
-  while (m) {
-    const int k = __builtin_ctz(m);
-    m &= m - 1;
-    reference_head<kCombineThreads>(p, t, hb + k, ws);
+  uint32_t mm = (w == 0 ? flagged : 0u) | nonfinite;
+  while (mm) {
+    const int k = __builtin_ctz(mm);
+    mm &= mm - 1;
+    reference_head<kCombineThreads>(p, t, hb0 + k, ws);
     __syncthreads();
+  }
+}
+
+// With a single slice the MFMA kernel wrote the output itself; this kernel only looks at the
+// flags (one word per 32 heads of a query, one per thread) and recomputes every flagged head
+// by the reference method, one after the other in the workgroup that found it.
+__global__ __launch_bounds__(kCombineThreads) void sfa_flag_fixup_kernel(SfaParams p) {
+  __shared__ RefSmem ws;
+  __shared__ uint32_t found[kCombineThreads];
+  __shared__ int nfound;
+  const int n_hw = p.H / 32;
+  const int wid = blockIdx.x * kCombineThreads + threadIdx.x;   // (query, 32-head block)
+  if (threadIdx.x == 0) nfound = 0;
+  __syncthreads();
+  if (wid < p.T * n_hw) {
+    const uint32_t f = p.flags[wid];
+    if (f) found[atomicAdd(&nfound, 1)] = (uint32_t)wid;
+  }
+  __syncthreads();
+  const int nf = nfound;
+  for (int q = 0; q < nf; ++q) {
+    const uint32_t w = found[q];
+    const int t = (int)(w / n_hw), hw = (int)(w % n_hw);
+    uint32_t m = p.flags[w];
+    while (m) {
+      const int k = __builtin_ctz(m);
+      m &= m - 1;
+      reference_head<kCombineThreads>(p, t, hw * 32 + k, ws);
+      __syncthreads();
+    }
   }
 }
 
@@ -574,7 +640,7 @@ SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path) {
     // the (query, head group) pairs alone do not fill the chip, the index list is split into
     // slices (at most 1024 rows each) until about one workgroup per CU runs.
     const bool wide = (int64_t)T * (H / 128) >= 256;
-    pl.heads_per_wg = (H % 128 == 0) ? 128 : (H % 96 == 0) ? 96 : (H % 64 == 0) ? 64 : 32;
+    pl.heads_per_wg = (H % 128 == 0) ? 128 : (H % 64 == 0) ? 64 : 32;
     pl.n_hg = H / pl.heads_per_wg;
     const int64_t max_ns = (K + kTileRows - 1) / kTileRows;
     int64_t ns = 1;
@@ -614,14 +680,21 @@ hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream) {
   const dim3 grid(pairs * p.n_hg);
   switch (p.heads_per_wg) {
     case 128: hipLaunchKernelGGL(sfa_mfma_kernel<4>, grid, dim3(256), 0, stream, p); break;
-    case 96: hipLaunchKernelGGL(sfa_mfma_kernel<3>, grid, dim3(192), 0, stream, p); break;
     case 64: hipLaunchKernelGGL(sfa_mfma_kernel<2>, grid, dim3(128), 0, stream, p); break;
     default: hipLaunchKernelGGL(sfa_mfma_kernel<1>, grid, dim3(64), 0, stream, p); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // merges the slices, and recomputes any flagged head (with one slice it only checks flags)
-  hipLaunchKernelGGL(sfa_combine_kernel, dim3(p.H / 4, p.T), dim3(kCombineThreads), 0, stream, p);
+  if (p.nsplit > 1) {
+    const int nw = p.heads_per_wg / 32;
+    hipLaunchKernelGGL(sfa_combine_kernel, dim3(p.n_hg * nw * nw * 2, p.T), dim3(kCombineThreads), 0,
+                       stream, p);
+  } else {
+    const int words = p.T * (p.H / 32);
+    hipLaunchKernelGGL(sfa_flag_fixup_kernel, dim3((words + kCombineThreads - 1) / kCombineThreads),
+                       dim3(kCombineThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
