@@ -117,6 +117,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
   p.split = pl.split;
   p.nsplit_max = pl.nsplit_max;
   p.cap = pl.cap;
+  p.rs = pl.rs;
   p.out_idx = out_idx;
   p.out_score = out_score;
   uint8_t* ws = static_cast<uint8_t*>(workspace);

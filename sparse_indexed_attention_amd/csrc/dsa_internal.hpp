@@ -25,7 +25,8 @@ struct IndexerPlan {
   int32_t grid;         // workgroups of the launch
   int32_t split;        // positions per context split (multiple of 64)
   int32_t nsplit_max;   // splits of the longest visible prefix (header rows per query)
-  int32_t cap;          // candidate slots per split = min(split, top_k)
+  int32_t cap;          // candidates per split at most = min(split, top_k)
+  int32_t rs;           // candidate slots per split: cap rounded up to 4
   size_t off_counters, off_hdr, off_ckey, off_cpos, bytes;
 };
 
@@ -39,21 +40,14 @@ struct IndexerParams {
   const int32_t* q_vis;
   int32_t T, H, D, K, max_visible;
   int32_t q_dtype, k_dtype;
-  int32_t grid, split, nsplit_max, cap;
+  int32_t grid, split, nsplit_max, cap, rs;
   int32_t* out_idx;
   float* out_score;
-  uint32_t* counters;   // [T][2]         arrivals, flat-list length per query (self-resetting)
-  uint32_t* hdr;        // [T][nsplit][8] emitted count, threshold key, run offset, key range
-  uint32_t* cand_key;   // [T][2 * nsplit * cap] (+256) flat candidate lists: keys
-  int32_t* cand_pos;    // [T][2 * nsplit * cap] (+256) ... and positions
+  uint32_t* counters;   // [T]                  split arrivals per query (self-resetting)
+  uint32_t* hdr;        // [T][nsplit_max][8]   emitted count, threshold key, key range
+  uint32_t* cand_key;   // [T][nsplit_max][rs] one run of candidates per split: keys
+  int32_t* cand_pos;    // [T][nsplit_max][rs] ... and positions
 };
-
-// Entries of one query's flat candidate list.  A split emits at most its length, and a
-// re-scored split appends a new run of at most its length, so twice the longest visible prefix
-// is room enough; rounded to whole 256-byte lines.
-__host__ __device__ inline size_t indexer_flat_stride(int32_t max_visible) {
-  return ((size_t)2 * max_visible + 64 + 63) / 64 * 64;
-}
 
 IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k);
 hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream);

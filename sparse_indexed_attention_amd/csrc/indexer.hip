@@ -22,9 +22,9 @@
 //     wherever they sit;
 //   * each split picks a threshold key by radix selection over its LDS scores so that a
 //     little more than its expected share of the Top-K survives, and writes those candidates
-//     (order-preserving key, position) to the workspace in position order;
-//   * the last split of a query to arrive (atomic counter) gathers the candidate keys into
-//     LDS, finds the exact K_eff-th key by radix selection, and checks that every split's
+//     (order-preserving key, position) in position order to its own run of the workspace;
+//   * the last split of a query to arrive (atomic counter) copies the runs into LDS in split
+//     order, finds the exact K_eff-th key by radix selection, and checks that every split's
 //     threshold lies at or below it - then the candidates provably contain the exact answer.
 //     A split whose threshold was too high is re-scored by the merging workgroup and
 //     contributes its exact local Top-K instead (rare unless the top positions crowd into a
@@ -61,9 +61,9 @@ template <int MODE>
 constexpr int region_bytes() {
   return MODE == 0 ? 65536 : Ring<MODE>::D * NWAVE * Ring<MODE>::SLOT;
 }
-// Merge layout of the region: the selection (keys, flat indices, then positions), then the
-// query's flat candidate list (keys, then positions when they fit), whose space the ordering
-// of the output reuses once the selection is gathered.
+// Merge layout of the region: the selection (keys, then virtual indices turned positions),
+// the run starts of the query's splits, then the candidate runs copied in split order (keys,
+// then positions when they fit).
 constexpr int kSelCap = kMaxTopK + 64;           // the selection and one histogram bin
 constexpr int kSelBytes = kSelCap * 8;
 template <int MODE>
@@ -79,7 +79,7 @@ struct Lds {
   int* hist;          // [kBins]
   uint32_t* sel_key;  // [kSelCap] merge: keys of the selection (and a few more)
   int32_t* sel_pos;   // [kSelCap] merge: their positions
-  uint32_t* flat;     // [flat_words] merge: flat candidate keys (+ positions)
+  uint32_t* flat;     // [flat_words] merge: run starts, candidate keys (+ positions)
   int* res;           // [4]
   int* scan;          // [2 * NWAVE + 2]
   int* wcnt;          // [2 * NWAVE]
@@ -823,19 +823,22 @@ __device__ __forceinline__ void pad_output(const IndexerParams& p, int t, int fr
 // ---------------------------------------------------------------------------------------
 // Merge of a query's split candidates (run by the last split to arrive).
 //
-// Each split appends its candidates (key, position), in position order, to the query's flat
-// candidate list at an offset it takes from an atomic counter, so the list is a sequence of
-// runs in arrival order.  The merge finds the bin of the K_eff-th key by range-fitted radix
-// passes over that list, gathers every entry at or above the bin in flat order, and finds the
-// exact K_eff-th key T (and, among keys equal to T, the lower positions) within the gathered
-// set.  Since split r covers positions [r*split, (r+1)*split) and its run is in position
-// order, the output slot of a taken entry is the count taken in earlier splits plus its rank
-// in its run.  Keys of runs replaced by a re-scored split are zeroed, and key 0 lies below
-// every real key.
+// Split r writes its candidates (key, position), in position order, to its own run of slots
+// [r*rs, r*rs + count) of the query's candidate area (rs = cap rounded up to 4), zeroes the
+// keys of the rest of the run's last 4-entry chunk, and writes its count to its header.  The
+// merge reads the runs in split order as one list, the "virtual" list, in which every run
+// takes whole chunks: entry v lies in the run r with pre[r] <= v < pre[r+1], where pre[r]
+// sums the counts of the splits before r, each rounded up to 4.  Key 0 lies below every real
+// key and marks the padding.  Split r covers positions [r*split, (r+1)*split), so the virtual
+// list is in position order.  The merge finds the bin of the K_eff-th key by range-fitted radix passes over the
+// list, gathers every entry at or above that bin in virtual order, finds the exact K_eff-th
+// key T (and, among keys equal to T, the lower positions) within the gathered set, and
+// writes the taken entries in gathered order: the output comes out sorted by position with
+// no sort and no per-split bookkeeping.
 // ---------------------------------------------------------------------------------------
 struct MergeHdr {
-  int n_alloc;        // entries in the flat list
-  int n_real;         // candidates of the live runs
+  int n;              // length of the virtual list (a multiple of 4)
+  int n_real;         // candidates of all runs
   uint32_t max_tau;   // largest split threshold
   uint32_t lo, hi;    // every candidate key lies in [lo, hi]
 };
@@ -844,64 +847,175 @@ __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// x / d for x < 2^24 with a float reciprocal and one correction step (an integer division is
-// a long instruction sequence).
-__device__ __forceinline__ uint32_t div_split(uint32_t x, uint32_t d, float inv) {
-  uint32_t q = (uint32_t)((float)x * inv);
-  q -= (uint32_t)(q * d > x);
-  q += (uint32_t)((q + 1u) * d <= x);
-  return q;
-}
-
-// Split header words: emitted count, threshold, run offset, smallest and largest emitted key.
+// Split header words: emitted count, threshold, (unused), smallest and largest emitted key.
 constexpr int kHdrWords = 8;
 
-// Split headers reduced: candidate total, largest threshold, key range; the flat list's length.
+// Reduces the split headers of query t and writes the run starts pre[0 .. nsplit] to LDS
+// (pre[nsplit] = the list's length).  Thread i reads the headers of a contiguous block of
+// splits, so one workgroup scan yields the starts.
 __device__ __forceinline__ MergeHdr load_headers(const IndexerParams& p, int t, int nsplit,
-                                                 const Lds& L) {
+                                                 uint32_t* pre, const Lds& L) {
+  constexpr int PER = kNSplitMax / NT;
   const uint32_t* hdr = p.hdr + (size_t)t * p.nsplit_max * kHdrWords;
-  int c = 0;
+  const int per = (nsplit + NT - 1) / NT;
+  const int j0 = min(nsplit, per * (int)threadIdx.x), j1 = min(nsplit, j0 + per);
+  uint32_t cnt[PER], tj[PER], lj[PER], hj[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const uint32_t* h = hdr + kHdrWords * (j0 + u);
+    const bool in = j0 + u < j1;
+    cnt[u] = in ? ld_agent(h) : 0u;
+    tj[u] = in ? ld_agent(h + 1) : 0u;
+    lj[u] = in ? ld_agent(h + 3) : 0xffffffffu;
+    hj[u] = in ? ld_agent(h + 4) : 0u;
+  }
+  int c = 0, c4 = 0;
   uint32_t tau = 0u, lo = 0xffffffffu, hi = 0u;
-  for (int jj = threadIdx.x; jj < nsplit; jj += NT) {
-    const uint32_t cnt = ld_agent(hdr + kHdrWords * jj);
-    const uint32_t tj = ld_agent(hdr + kHdrWords * jj + 1);
-    const uint32_t lj = ld_agent(hdr + kHdrWords * jj + 3);
-    const uint32_t hj = ld_agent(hdr + kHdrWords * jj + 4);
-    c += (int)cnt;
-    tau = max(tau, tj);
-    if (cnt) {
-      lo = min(lo, lj);
-      hi = max(hi, hj);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    c += (int)cnt[u];
+    c4 += (int)((cnt[u] + 3u) & ~3u);
+    tau = max(tau, tj[u]);
+    if (cnt[u]) {
+      lo = min(lo, lj[u]);
+      hi = max(hi, hj[u]);
     }
   }
+  int total;
+  int b = wg_scan(c4, 0, L, total);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if (j0 + u < j1) pre[j0 + u] = (uint32_t)b;
+    b += (int)((cnt[u] + 3u) & ~3u);
+  }
+  if (threadIdx.x == 0) pre[nsplit] = (uint32_t)total;
   c = wave_scan_add(c);
   c = __builtin_amdgcn_readlane(c, 63);
   tau = wave_max(tau);
   lo = wave_min(lo);
   hi = wave_max(hi);
   const int wave = threadIdx.x >> 6;
-  __syncthreads();   // earlier readers of L.res / L.range / L.wcnt are done
   if ((threadIdx.x & 63) == 0) {
-    L.res[wave] = c;
     L.wcnt[wave] = (int)tau;
+    L.wcnt[NWAVE + wave] = c;
     L.range[wave] = lo;
     L.range[NWAVE + wave] = hi;
   }
   __syncthreads();
   MergeHdr h;
+  h.n = total;
   h.n_real = 0;
   h.max_tau = 0u;
   h.lo = 0xffffffffu;
   h.hi = 0u;
 #pragma unroll
   for (int w = 0; w < NWAVE; ++w) {
-    h.n_real += L.res[w];
     h.max_tau = max(h.max_tau, (uint32_t)L.wcnt[w]);
+    h.n_real += L.wcnt[NWAVE + w];
     h.lo = min(h.lo, L.range[w]);
     h.hi = max(h.hi, L.range[NWAVE + w]);
   }
-  h.n_alloc = (int)ld_agent(p.counters + 2 * t + 1);
   return h;
+}
+
+// Runs holding the virtual indices v[u] (v[u] < pre[nsplit]; entries with v[u] < 0 are left
+// at run 0): the largest r with pre[r] <= v, and pre[r], by a branch-free binary search whose
+// LDS reads for all U indices are in flight together.
+template <int U>
+__device__ __forceinline__ void runs_of(const uint32_t* pre, int nsplit, const int (&v)[U],
+                                        int (&r)[U], int (&pr)[U]) {
+  int step = 1;
+  while (2 * step < nsplit) step *= 2;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    r[u] = 0;
+    pr[u] = 0;
+  }
+  for (; step >= 1; step >>= 1) {
+    uint32_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = r[u] + step < nsplit ? pre[r[u] + step] : 0xffffffffu;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool up = v[u] >= 0 && x[u] <= (uint32_t)v[u];
+      r[u] += up ? step : 0;
+      pr[u] = up ? (int)x[u] : pr[u];
+    }
+  }
+}
+
+// Slot of virtual index v in the query's candidate area (run stride rs).
+__device__ __forceinline__ int run_slot(const uint32_t* pre, int nsplit, int rs, int v) {
+  int vv[1] = {v}, r[1], pr[1];
+  runs_of<1>(pre, nsplit, vv, r, pr);
+  return r[0] * rs + v - pr[0];
+}
+
+// Copies the virtual list (n entries, a multiple of 4) into LDS: keys to lk and, when lp is not
+// null, positions to lp, with agent-scope direct-to-LDS loads of 16 bytes per lane.  Every run
+// takes whole 4-entry chunks.  Long runs (64 entries or more on average) are copied one run
+// per load (lane l: chunk l of the run; wave w copies runs w, w + 4, ...).  Short runs would
+// leave most lanes of such a load idle, so then a load fills 64 consecutive chunks of the list
+// instead, each lane finding its chunk's run by binary search.
+__device__ __forceinline__ void stage_runs(const uint32_t* gk, const int32_t* gp, int rs,
+                                           int nsplit, int n, const uint32_t* pre, uint32_t* lk,
+                                           int32_t* lp) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int per = lp ? 2 : 1;
+  int issued = 0;
+  auto throttle = [&]() {
+    issued += per;
+    if (issued >= 56) {   // at most 56 loads in flight: inside the 6-bit load counter
+      wait_vmcnt<40>();
+      issued = 40;
+    }
+  };
+  if (n >= 64 * nsplit) {
+    for (int r0 = wave; r0 < nsplit; r0 += 64 * NWAVE) {
+      // lane l: the bounds of run r0 + 4 l
+      const int rl = min(r0 + NWAVE * lane, nsplit - 1);
+      const int bl = (int)pre[rl];
+      const int el = (int)pre[rl + 1];
+      const int nr = min(64, (nsplit - r0 + NWAVE - 1) / NWAVE);
+      for (int u = 0; u < nr; ++u) {
+        const int r = r0 + NWAVE * u;
+        const int b = __builtin_amdgcn_readlane(bl, u);
+        const int c = __builtin_amdgcn_readlane(el, u) - b;
+        for (int i = 0; i < c; i += 256) {
+          if (4 * lane < c - i) {
+            const uint32_t src = 4u * (uint32_t)(r * rs + i + 4 * lane);
+            load_to_lds<16, true>(gk, src, lds_addr(lk + b + i));
+            if (lp) load_to_lds<16, true>(gp, src, lds_addr(lp + b + i));
+          }
+          throttle();
+        }
+      }
+    }
+  } else {
+    constexpr int B = 4;
+    const int nc = n >> 2;
+    for (int i0 = 0; 64 * (wave + NWAVE * i0) < nc; i0 += B) {
+      int v[B], r[B], pr[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int c = 64 * (wave + NWAVE * (i0 + u)) + lane;
+        v[u] = c < nc ? 4 * c : -1;
+      }
+      runs_of<B>(pre, nsplit, v, r, pr);
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int cb = 64 * (wave + NWAVE * (i0 + u));
+        if (cb >= nc) break;
+        if (v[u] >= 0) {
+          const uint32_t src = 4u * (uint32_t)(r[u] * rs + v[u] - pr[u]);
+          load_to_lds<16, true>(gk, src, lds_addr(lk + 4 * cb));
+          if (lp) load_to_lds<16, true>(gp, src, lds_addr(lp + 4 * cb));
+        }
+        throttle();
+      }
+    }
+  }
+  wait_vmcnt<0>();
 }
 
 // Row-major selection over entries [0, n) whose keys come from key_of(i) (0: no entry).
@@ -1001,13 +1115,15 @@ __device__ __forceinline__ Kth rm_kth(int n, KeyOf key_of, int k, uint32_t lo, u
   return Kth{kt.T, nw.above + kt.gt, nw.above + kt.ge};
 }
 
-// Compacts the entries with pred(key, i) into the selection area, keeping their flat order:
-// thread i scans the contiguous block [E*i, E*i + E) of the list (E odd, so that the LDS
-// reads of a wave fall in distinct banks), counts, takes its offset from a workgroup scan,
-// then writes flat indices; the positions follow with all reads in flight.  Returns the
-// count (at most kSelCap are stored).
-template <class KeyOf, class PosOf, class Pred>
-__device__ __forceinline__ int gather_ordered(int n, KeyOf key_of, PosOf pos_of, Pred pred,
+// Compacts the entries with pred(key, v) into the selection area, keeping their virtual
+// order: thread i scans the contiguous block [E*i, E*i + E) of the list (E odd, so that the
+// LDS reads of a wave fall in distinct banks), counts, takes its offset from a workgroup
+// scan, then writes keys and virtual indices; pos_batch(v, ps) then turns U virtual indices
+// per thread into positions with all reads in flight.  Returns the count (at most kSelCap
+// are stored).
+constexpr int kGatherU = (kSelCap + NT - 1) / NT;
+template <class KeyOf, class Pred, class PosBatch>
+__device__ __forceinline__ int gather_ordered(int n, KeyOf key_of, Pred pred, PosBatch pos_batch,
                                               const Lds& L) {
   const int E = ((n + NT - 1) / NT) | 1;
   const int b0 = min(n, E * (int)threadIdx.x), b1 = min(n, b0 + E);
@@ -1039,15 +1155,16 @@ __device__ __forceinline__ int gather_ordered(int n, KeyOf key_of, PosOf pos_of,
   }
   __syncthreads();
   const int ns = min(total, kSelCap);
-  constexpr int U = (kSelCap + NT - 1) / NT;
-  int32_t ps[U];
+  int v[kGatherU];
+  int32_t ps[kGatherU];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < kGatherU; ++u) {
     const int q = threadIdx.x + u * NT;
-    ps[u] = q < ns ? pos_of(L.sel_pos[q]) : 0;
+    v[u] = q < ns ? L.sel_pos[q] : -1;
   }
+  pos_batch(v, ps);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < kGatherU; ++u) {
     const int q = threadIdx.x + u * NT;
     if (q < ns) L.sel_pos[q] = ps[u];
   }
@@ -1055,29 +1172,31 @@ __device__ __forceinline__ int gather_ordered(int n, KeyOf key_of, PosOf pos_of,
   return total;
 }
 
-// Selection and output over the flat list, keys from key_of(i), positions from pos_of(i).
-// Returns false (writing nothing) when a split's threshold lies above the K_eff-th key T.
-template <class KeyOf, class PosOf>
-__device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int K_eff, int split_len,
+// Selection and output over the virtual list, keys from key_of(v), positions from pos_of(v)
+// one at a time or pos_batch for a batch.  Returns false (writing nothing) when a split's
+// threshold lies above the K_eff-th key T.
+template <class KeyOf, class PosOf, class PosBatch>
+__device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int K_eff,
                                              const MergeHdr& mh, KeyOf key_of, PosOf pos_of,
-                                             const Lds& L, uint32_t& T, int& gt, bool& enough) {
-  const int n = mh.n_alloc;
+                                             PosBatch pos_batch, const Lds& L, uint32_t& T,
+                                             int& gt, bool& enough) {
+  const int n = mh.n;
   enough = mh.n_real >= K_eff;
   T = 0u;
   gt = 0;
   int ge = 0;
   uint32_t pmax = 0xffffffffu;
-  int ns;   // entries in the selection area, in flat order: the selection and maybe a few more
+  int ns;   // entries in the selection area, in virtual order: the selection and maybe a few more
   auto sel_key = [&](int q) { return L.sel_key[q]; };
   if (!enough) {
     if (mh.max_tau != 0u) return false;
-    ns = gather_ordered(n, key_of, pos_of, [](uint32_t, int) { return true; }, L);
+    ns = gather_ordered(n, key_of, [](uint32_t, int) { return true; }, pos_batch, L);
   } else {
     // one radix pass usually isolates a bin of a few keys holding the K_eff-th; every key at
     // or above that bin is gathered, and the exact K_eff-th is found among them
     const Narrowed nw = rm_narrow(n, key_of, K_eff, mh.lo, mh.hi, L);
     if (nw.above + nw.c <= kSelCap) {
-      ns = gather_ordered(n, key_of, pos_of, [&](uint32_t k, int) { return k >= nw.base; }, L);
+      ns = gather_ordered(n, key_of, [&](uint32_t k, int) { return k >= nw.base; }, pos_batch, L);
       if (nw.width == 0) {
         T = nw.base;
         gt = nw.above;
@@ -1098,7 +1217,7 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
         pmax = ~rm_kth(ns, tied, need, 0x80000000u, 0xffffffffu, L).T;
       }
     } else {
-      // a crowd of equal keys: the exact selection over the whole flat list, then its entries
+      // a crowd of equal keys: the exact selection over the whole list, then its entries
       const Kth kt = rm_kth(n, key_of, K_eff, mh.lo, mh.hi, L);
       T = kt.T;
       gt = kt.gt;
@@ -1110,161 +1229,95 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
         pmax = ~rm_kth(n, tied, need, 0x80000000u, 0xffffffffu, L).T;
       }
       const uint32_t TT = T, PM = pmax;
-      ns = gather_ordered(n, key_of, pos_of,
+      ns = gather_ordered(n, key_of,
                           [&](uint32_t k, int i) { return k > TT || (k == TT && (uint32_t)pos_of(i) <= PM); },
-                          L);
+                          pos_batch, L);
     }
   }
   ns = min(ns, kSelCap);
-  // taken: above T, or equal to it at a position no later than pmax (T = 0: every entry)
-  // (bitwise operators: straight-line code, no branches)
-  auto take = [&](uint32_t k, int32_t ps) { return (k > T) | ((k == T) & ((uint32_t)ps <= pmax)); };
-  // Output order.  The selection area holds, in flat order, the runs of the splits, each in
-  // position order, and split r covers positions [r*split, (r+1)*split).  So the slot of a
-  // taken entry of split r is the count taken in splits before r plus its rank in its run:
-  // per-split counts (scanned in split order) and, per run, the taken count before its start.
-  const int nspl = (min(p.q_vis[t], p.max_visible) + split_len - 1) / split_len;
-  int* cnt = L.hist;                        // [nspl] taken per split, then the scan
-  int* first = (int*)L.flat;                // [nspl] taken entries before the run of a split
+  // Output.  The selection area holds, in position order, every taken entry and at most 64
+  // more (keys of the K_eff-th key's bin below T, or equal to T past pmax): taken are the
+  // keys above T and those equal to T at positions up to pmax (T = 0: every entry).  Thread
+  // i takes a contiguous block of the area; a workgroup scan of the taken counts gives the
+  // output slots.
+  constexpr int EMAX = kGatherU | 1;
   const int E = ((ns + NT - 1) / NT) | 1;
   const int b0 = min(ns, E * (int)threadIdx.x), b1 = min(ns, b0 + E);
-  const uint32_t split = (uint32_t)split_len;
-  const float inv_split = 1.0f / (float)split_len;
-  __syncthreads();   // the histogram and the flat area are free
-  for (int r = threadIdx.x; r < nspl; r += NT) cnt[r] = 0;
-  __syncthreads();
+  uint32_t k[EMAX];
+  int32_t ps[EMAX];
+  bool tk[EMAX];
   int c = 0;
-  for (int q0 = b0; q0 < b1; q0 += 4) {
-    uint32_t k[4];
-    int32_t ps[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = min(q0 + u, b1 - 1);
-      k[u] = L.sel_key[q];
-      ps[u] = L.sel_pos[q];
-    }
+  for (int u = 0; u < EMAX; ++u) {
+    const int q = max(0, min(b0 + u, ns - 1));
+    k[u] = L.sel_key[q];
+    ps[u] = L.sel_pos[q];
+  }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if ((q0 + u < b1) & take(k[u], ps[u])) {
-        ++c;
-        atomicAdd(&cnt[div_split((uint32_t)ps[u], split, inv_split)], 1);
-      }
-    }
+  for (int u = 0; u < EMAX; ++u) {
+    tk[u] = (b0 + u < b1) & ((k[u] > T) | ((k[u] == T) & ((uint32_t)ps[u] <= pmax)));
+    c += tk[u];
   }
   int total;
-  const int fs0 = wg_scan(c, 0, L, total);
-  // exclusive scan of the per-split counts, PER splits per thread
-  {
-    constexpr int PER = kNSplitMax / NT;
-    int v[PER], loc = 0;
+  __syncthreads();   // earlier readers of L.scan are done
+  int slot = wg_scan(c, 1, L, total);
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int r = PER * threadIdx.x + u;
-      v[u] = r < nspl ? cnt[r] : 0;
-      loc += v[u];
-    }
-    int tot2;
-    int b = wg_scan(loc, 1, L, tot2);
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int r = PER * threadIdx.x + u;
-      if (r < nspl) cnt[r] = b;
-      b += v[u];
-    }
-  }
-  // run starts: the taken count before the first entry of each split's run
-  {
-    int fs = fs0;
-    uint32_t prev = b0 > 0 ? div_split((uint32_t)L.sel_pos[b0 - 1], split, inv_split) : 0xffffffffu;
-    for (int q0 = b0; q0 < b1; q0 += 4) {
-      uint32_t k[4];
-      int32_t ps[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int q = min(q0 + u, b1 - 1);
-        k[u] = L.sel_key[q];
-        ps[u] = L.sel_pos[q];
+  for (int u = 0; u < EMAX; ++u) {
+    if (tk[u]) {
+      if (slot < K_eff) {
+        p.out_idx[(size_t)t * p.K + slot] = ps[u];
+        if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(k[u]);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (q0 + u < b1) {
-          const uint32_t r = div_split((uint32_t)ps[u], split, inv_split);
-          if (r != prev) first[r] = fs;
-          prev = r;
-          fs += take(k[u], ps[u]);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  {
-    int fs = fs0;
-    for (int q0 = b0; q0 < b1; q0 += 4) {
-      uint32_t k[4];
-      int32_t ps[4];
-      int base[4], fst[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int q = min(q0 + u, b1 - 1);
-        k[u] = L.sel_key[q];
-        ps[u] = L.sel_pos[q];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t r = div_split((uint32_t)ps[u], split, inv_split);
-        base[u] = cnt[r];
-        fst[u] = first[r];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if ((q0 + u < b1) & take(k[u], ps[u])) {
-          const int slot = base[u] + fs - fst[u];
-          if (slot < K_eff) {
-            p.out_idx[(size_t)t * p.K + slot] = ps[u];
-            if (p.out_score) p.out_score[(size_t)t * p.K + slot] = key_to_float(k[u]);
-          }
-          ++fs;
-        }
-      }
+      ++slot;
     }
   }
   pad_output(p, t, min(total, K_eff));
-  if (threadIdx.x == 0) {
-    st_agent(p.counters + 2 * t, 0u);
-    st_agent(p.counters + 2 * t + 1, 0u);
-  }
+  if (threadIdx.x == 0) st_agent(p.counters + t, 0u);
   return true;
 }
 
-// Stages the flat list in LDS when it fits (keys; positions too when there is room) with
-// agent-scope direct-to-LDS loads, then selects.  T, gt and enough are kept for the
+// Run starts from the headers, then the virtual list staged in LDS when it fits (keys;
+// positions too when there is room), then the selection.  T, gt and enough are kept for the
 // re-scoring of failing splits.
 template <int MODE>
-__device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, int split,
-                                      const MergeHdr& mh, const Lds& L, uint32_t& T, int& gt,
-                                      bool& enough) {
-  const size_t qflat = (size_t)t * indexer_flat_stride(p.max_visible);
-  const uint32_t* gk = p.cand_key + qflat;
-  const int32_t* gp = p.cand_pos + qflat;
-  const int n = mh.n_alloc;
-  const int nr = (n + 255) / 256 * 256;             // whole 1 KB loads
+__device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, int nsplit,
+                                      const Lds& L, uint32_t& T, int& gt, bool& enough) {
   constexpr int FW = flat_words<MODE>();
-  auto gkey = [&](int i) { return ld_agent(gk + i); };
-  auto gpos = [&](int i) { return ld_agent(gp + i); };
-  if (nr > FW) return merge_select(p, t, K_eff, split, mh, gkey, gpos, L, T, gt, enough);
-  const bool pos_in = 2 * nr <= FW;
-  uint32_t* fk = L.flat;
-  int32_t* fp = (int32_t*)(L.flat + nr);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int c = 256 * wave; c < n; c += 256 * NWAVE) {
-    load_to_lds<16, true>(gk + c, 16u * lane, lds_addr(fk + c));
-    if (pos_in) load_to_lds<16, true>(gp + c, 16u * lane, lds_addr(fp + c));
-  }
-  wait_vmcnt<0>();
+  uint32_t* pre = L.flat;
+  const int pw = (nsplit + 4) & ~3;   // pre[0 .. nsplit], whole 16-byte words
+  const MergeHdr mh = load_headers(p, t, nsplit, pre, L);
+  const int rs = p.rs;
+  const size_t qb = (size_t)t * p.nsplit_max * rs;
+  const uint32_t* gk = p.cand_key + qb;
+  const int32_t* gp = p.cand_pos + qb;
+  const int n = mh.n;
+  // the list is staged in LDS when it fits (keys; positions too when there is room), else
+  // read from the runs in global memory
+  auto gkey = [&](int v) { return ld_agent(gk + run_slot(pre, nsplit, rs, v)); };
+  auto gpos = [&](int v) { return ld_agent(gp + run_slot(pre, nsplit, rs, v)); };
+  auto gpos_batch = [&](const int (&v)[kGatherU], int32_t (&ps)[kGatherU]) {
+    int r[kGatherU], pr[kGatherU];
+    runs_of<kGatherU>(pre, nsplit, v, r, pr);
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u)
+      ps[u] = v[u] >= 0 ? ld_agent(gp + r[u] * rs + v[u] - pr[u]) : 0;
+  };
+  if (n > FW - pw) return merge_select(p, t, K_eff, mh, gkey, gpos, gpos_batch, L, T, gt, enough);
+  const bool pos_in = 2 * n <= FW - pw;
+  uint32_t* fk = L.flat + pw;
+  int32_t* fp = (int32_t*)(fk + n);
+  stage_runs(gk, gp, rs, nsplit, n, pre, fk, pos_in ? fp : nullptr);
   __syncthreads();
-  auto lkey = [&](int i) { return fk[i]; };
-  if (pos_in) return merge_select(p, t, K_eff, split, mh, lkey, [&](int i) { return fp[i]; }, L, T, gt, enough);
-  return merge_select(p, t, K_eff, split, mh, lkey, gpos, L, T, gt, enough);
+  auto lkey = [&](int v) { return fk[v]; };
+  if (pos_in) {
+    auto lpos = [&](int v) { return fp[v]; };
+    auto lpos_batch = [&](const int (&v)[kGatherU], int32_t (&ps)[kGatherU]) {
+#pragma unroll
+      for (int u = 0; u < kGatherU; ++u) ps[u] = v[u] >= 0 ? fp[v[u]] : 0;
+    };
+    return merge_select(p, t, K_eff, mh, lkey, lpos, lpos_batch, L, T, gt, enough);
+  }
+  return merge_select(p, t, K_eff, mh, lkey, gpos, gpos_batch, L, T, gt, enough);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1275,7 +1328,7 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
 template <int MODE>
 __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   constexpr int RB = region_bytes<MODE>();
-  static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kNSplitMax, "shared region");
+  static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kNSplitMax + 4, "shared region");
   __shared__ __attribute__((aligned(16))) uint8_t s_region[RB];
   __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSplitMax];
   __shared__ __attribute__((aligned(16))) float s_w[NWAVE * 64];
@@ -1335,7 +1388,6 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   uint32_t T = 0u;
   int gt = 0;
   bool enough = false;
-  const size_t qflat = (size_t)t * indexer_flat_stride(p.max_visible);   // the query's flat list
   for (;;) {
     const int start = cur * split, len = min(split, V - start);
     uint32_t klo, khi;
@@ -1379,11 +1431,9 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
             cnt = kt.ge <= hard ? kt.ge : kt.gt;
           }
         }
-        // this split's run of the flat list
+        // this split's run of the candidate area
         cnt = min(cnt, cap);
-        if (threadIdx.x == 0) L.bcast[1] = (int)add_agent(p.counters + 2 * t + 1, (uint32_t)cnt);
-        __syncthreads();
-        const size_t cb = qflat + (size_t)L.bcast[1];
+        const size_t cb = ((size_t)t * p.nsplit_max + cur) * p.rs;
         block_emit(kb, tau, 0x7fffffff,
                    [&](int slot, int i, uint32_t k) {
                      if (slot < cnt) {
@@ -1392,11 +1442,11 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
                      }
                    },
                    L);
+        if ((int)threadIdx.x < ((cnt + 3) & ~3) - cnt) st_agent(p.cand_key + cb + cnt + threadIdx.x, 0u);
         if (threadIdx.x == 0) {
           uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * kHdrWords;
           st_agent(h, (uint32_t)cnt);
           st_agent(h + 1, tau);
-          st_agent(h + 2, (uint32_t)L.bcast[1]);
           st_agent(h + 3, max(tau, klo));
           st_agent(h + 4, khi);
         }
@@ -1405,23 +1455,18 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
       wait_all_memory();
       __syncthreads();
       if (threadIdx.x == 0)
-        L.bcast[0] = add_agent(p.counters + 2 * t, 1u) == (uint32_t)(nsplit - 1);
+        L.bcast[0] = add_agent(p.counters + t, 1u) == (uint32_t)(nsplit - 1);
       __syncthreads();
       if (!L.bcast[0]) return;
-      if (merge<MODE>(p, t, K_eff, split, load_headers(p, t, nsplit, Lm), Lm, T, gt, enough)) return;
+      if (merge<MODE>(p, t, K_eff, nsplit, Lm, T, gt, enough)) return;
       refill = true;
       cur = -1;
     } else {
-      // exact local Top-min(len, K_eff) of a failing split replaces its candidates: the old
-      // run's keys are zeroed and the new run is appended to the flat list
+      // exact local Top-min(len, K_eff) of a failing split replaces its run (at most cap)
       const int kk = min(len, K_eff);
       const Kth kt = radix_kth(L.keys, len, kk, klo, khi, L);
       uint32_t* h = p.hdr + ((size_t)t * p.nsplit_max + cur) * kHdrWords;
-      const int old_cnt = (int)ld_agent(h), old_off = (int)ld_agent(h + 2);
-      for (int i = threadIdx.x; i < old_cnt; i += NT) st_agent(p.cand_key + qflat + old_off + i, 0u);
-      if (threadIdx.x == 0) L.bcast[1] = (int)add_agent(p.counters + 2 * t + 1, (uint32_t)kk);
-      __syncthreads();
-      const size_t cb = qflat + (size_t)L.bcast[1];
+      const size_t cb = ((size_t)t * p.nsplit_max + cur) * p.rs;
       emit_sel(L.keys, len, kt.T, kk - kt.gt,
                [&](int slot, int i, uint32_t k) {
                  if (slot < kk) {
@@ -1430,10 +1475,10 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
                  }
                },
                L);
+      if ((int)threadIdx.x < ((kk + 3) & ~3) - kk) st_agent(p.cand_key + cb + kk + threadIdx.x, 0u);
       if (threadIdx.x == 0) {
         st_agent(h, (uint32_t)kk);
         st_agent(h + 1, 0u);
-        st_agent(h + 2, (uint32_t)L.bcast[1]);
         st_agent(h + 3, kt.T);
         st_agent(h + 4, khi);
       }
@@ -1449,7 +1494,7 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
     wait_all_memory();
     __syncthreads();
     if (nxt < 0) {
-      merge<MODE>(p, t, K_eff, split, load_headers(p, t, nsplit, Lm), Lm, T, gt, enough);   // certified
+      merge<MODE>(p, t, K_eff, nsplit, Lm, T, gt, enough);   // certified
       return;
     }
     cur = nxt;
@@ -1469,12 +1514,13 @@ IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
   pl.split = (int32_t)split;
   pl.nsplit_max = (int32_t)((max_visible + split - 1) / split);
   pl.cap = (int32_t)(split < top_k ? split : top_k);
+  pl.rs = (pl.cap + 3) / 4 * 4;
   pl.grid = pl.nsplit_max * T;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  // flat candidate lists, plus one 1 KB load of slack past the last
-  const size_t slots = (size_t)T * indexer_flat_stride(max_visible) + 256;
+  // one run of rs candidate slots per split
+  const size_t slots = (size_t)T * pl.nsplit_max * pl.rs;
   size_t off = 0;
-  pl.off_counters = off; off = al(off + (size_t)T * 8);
+  pl.off_counters = off; off = al(off + (size_t)T * 4);
   pl.off_hdr = off;      off = al(off + (size_t)T * pl.nsplit_max * 32);
   pl.off_ckey = off;     off = al(off + slots * 4);
   pl.off_cpos = off;     off = al(off + slots * 4);

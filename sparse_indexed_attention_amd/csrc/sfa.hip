@@ -641,6 +641,10 @@ SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path) {
     // slices (at most 1024 rows each) until about one workgroup per CU runs.
     const bool wide = (int64_t)T * (H / 128) >= 256;
     pl.heads_per_wg = (H % 128 == 0) ? 128 : (H % 64 == 0) ? 64 : 32;
+    if (const char* e = getenv("DSA_SFA_HPW")) {
+      const int v = atoi(e);
+      if ((v == 32 || v == 64 || v == 128) && H % v == 0) pl.heads_per_wg = v;
+    }
     pl.n_hg = H / pl.heads_per_wg;
     const int64_t max_ns = (K + kTileRows - 1) / kTileRows;
     int64_t ns = 1;
