@@ -13,6 +13,14 @@ Formats:
   is the token's largest magnitude divided by 448 in fp32 (an all-zero token gets 1), the
   code is the fp32 quotient value/scale rounded to the nearest e4m3 value, ties to the even
   code, magnitudes above 448 saturating to 448.
+* fp8 latent KV rows for SFA, quantized per token and per tile of 128 columns ("Day0
+  Adaptation and Performance Optimization for Novel Long-Sequence Reasoning Models", section
+  4; "Large Model Inference Acceleration: Day-0 Adaptation...", section 2.2).  The pages fix
+  the granularity, not the scale's format; the reading taken here: the scale of a tile is the
+  smallest power of two 2^e (e >= -126) with max|x| <= 448 * 2^e over the tile (1 for an
+  all-zero tile), the code is x / scale (exact) rounded to the nearest e4m3 value, ties to
+  the even code; the 64 rope columns of the 576-wide latent row stay in bf16.  A row is 656
+  bytes: 512 codes, 64 bf16 (little-endian), then the four scales as fp32.
 """
 from __future__ import annotations
 
@@ -51,13 +59,16 @@ def decode_fp8_e4m3(codes: np.ndarray) -> np.ndarray:
 
 
 def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
-    """Stored tensor -> float64, dtype in {f32, bf16, fp8} (fp8 without its scale)."""
+    """Stored tensor -> float64, dtype in {f32, bf16, fp8} (fp8 without its scale), or
+    fp8_rows for the tile-quantized latent rows (with their scales)."""
     if dtype == "f32":
         return arr.astype(np.float64)
     if dtype == "bf16":
         return decode_bf16(arr)
     if dtype == "fp8":
         return decode_fp8_e4m3(arr)
+    if dtype == "fp8_rows":
+        return decode_kv_fp8_rows(arr)
     raise ValueError(dtype)
 
 
@@ -101,3 +112,45 @@ def quantize_fp8_per_token(x: np.ndarray):
     scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
     quot = np.divide(x, scale[:, None], dtype=np.float32)
     return encode_fp8_e4m3(quot), scale
+
+
+KV_FP8_ROW_BYTES = 656
+KV_NOPE = 512
+KV_TILE = 128
+
+
+def kv_fp8_tile_scale(amax: np.ndarray) -> np.ndarray:
+    """float32 tile maxima -> float32 scales: the smallest power of two 2^e, e >= -126, with
+    amax <= 448 * 2^e; 1 where amax == 0.  With amax = f * 2^k, 0.5 <= f < 1 (frexp, exact):
+    448 * 2^e = 0.875 * 2^(e + 9), so e = k - 9 when f <= 0.875 and k - 8 otherwise."""
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    f, k = np.frexp(a)
+    e = np.where(f > 0.875, k - 8, k - 9)
+    e = np.maximum(e, -126)
+    out = np.ldexp(1.0, e).astype(np.float32)
+    return np.where(a == 0.0, np.float32(1.0), out).astype(np.float32)
+
+
+def quantize_kv_fp8_rows(x: np.ndarray) -> np.ndarray:
+    """float32 [n, 576] latent rows -> uint8 [n, 656] fp8 rows (format above)."""
+    x = np.asarray(x, dtype=np.float32)
+    n = x.shape[0]
+    tiles = x[:, :KV_NOPE].reshape(n, KV_NOPE // KV_TILE, KV_TILE)
+    scale = kv_fp8_tile_scale(np.max(np.abs(tiles), axis=2))
+    quot = np.divide(tiles, scale[:, :, None], dtype=np.float32)
+    out = np.empty((n, KV_FP8_ROW_BYTES), dtype=np.uint8)
+    out[:, :KV_NOPE] = encode_fp8_e4m3(quot).reshape(n, KV_NOPE)
+    out[:, KV_NOPE:640] = encode_bf16_rne(x[:, KV_NOPE:]).astype("<u2").view(np.uint8)
+    out[:, 640:] = scale.astype("<f4").view(np.uint8)
+    return out
+
+
+def decode_kv_fp8_rows(rows: np.ndarray) -> np.ndarray:
+    """uint8 [n, 656] fp8 rows -> float64 [n, 576] (exact: code * scale, bf16 rope)."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    n = rows.shape[0]
+    scale = rows[:, 640:].copy().view("<f4").astype(np.float64)
+    nope = decode_fp8_e4m3(rows[:, :KV_NOPE]).reshape(n, KV_NOPE // KV_TILE, KV_TILE)
+    nope = (nope * scale[:, :, None]).reshape(n, KV_NOPE)
+    rope = decode_bf16(rows[:, KV_NOPE:640].copy().view("<u2"))
+    return np.concatenate([nope, rope], axis=1)

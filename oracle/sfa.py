@@ -16,7 +16,9 @@ per occurrence):
     O = (P @ R[:, :d_v]) / sum_j P  (H x d_v)
     LSE = max_j Z + log(sum_j P)    natural log
 
-With no row at all, O = 0 and LSE = -inf.  Float64 throughout.
+With no row at all, O = 0 and LSE = -inf.  Float64 throughout.  With fp8 latent rows
+(kv_dtype "fp8": bf16 queries, rows quantized per 128-column tile, see codecs) R is the
+dequantized row, code times tile scale, exactly.
 """
 from __future__ import annotations
 
@@ -47,8 +49,9 @@ def sfa_query(inp, t: int, idx_row: np.ndarray):
     pos = np.asarray(idx_row, dtype=np.int64)
     pos = pos[pos != -1]
     rows = logical_rows(inp.block_table, inp.block_size, inp.seq_stride, b, pos)
-    R = decode(inp.kv_pool[rows], spec.kv_dtype)
-    q = decode(inp.q_sfa[t], spec.kv_dtype)
+    fp8 = spec.kv_dtype == "fp8"
+    R = decode(inp.kv_pool[rows], "fp8_rows" if fp8 else spec.kv_dtype)
+    q = decode(inp.q_sfa[t], "bf16" if fp8 else spec.kv_dtype)
     return sfa_dense(q, R, spec.softmax_scale, spec.d_v)
 
 

@@ -83,3 +83,76 @@ def test_fp8_per_token_quantizer_matches_torch_route():
     # each token's largest magnitude maps to +-448 exactly
     big = np.abs(x[np.arange(4096) != 5]).argmax(axis=1)
     assert np.all(oracle.decode_fp8_e4m3(codes[np.arange(4096) != 5][np.arange(4095), big]) ** 2 == 448.0 ** 2)
+
+
+# ---- fp8 latent KV rows (per token, per 128-column tile, power-of-two scale) --------------
+
+def test_kv_tile_scale_is_the_smallest_sufficient_power_of_two():
+    """Checked in exact float64 arithmetic from the definition: 448 * s covers the tile's
+    maximum, half of s does not (unless s is the floor 2^-126), and s is a power of two."""
+    rng = np.random.default_rng(5)
+    a = np.concatenate([
+        (rng.standard_normal(200000) * np.exp(rng.uniform(-80, 80, 200000))),
+        448.0 * np.ldexp(1.0, np.arange(-130, 120)),            # boundaries: 448 * 2^k
+        1.75 * np.ldexp(1.0, np.arange(-130, 120)),              # mantissa exactly 1.75
+        np.nextafter(np.float32(448.0) * np.ldexp(np.float32(1), np.arange(-20, 20)).astype(np.float32),
+                     np.float32(np.inf)),                        # just above a boundary
+        [1e-45, 1e-40, 1e-38, 3.4e38, 1.0, 448.0, 449.0],
+    ]).astype(np.float32)
+    a = np.abs(a[np.isfinite(a) & (a != 0)])
+    s = oracle.kv_fp8_tile_scale(a).astype(np.float64)
+    af = a.astype(np.float64)
+    m, _ = np.frexp(s)
+    assert np.all(m == 0.5)                                      # powers of two
+    assert np.all(af <= 448.0 * s)
+    floor = s == 2.0 ** -126
+    assert np.all(floor | (af > 448.0 * s / 2))
+    assert np.all(s >= 2.0 ** -126)
+    assert oracle.kv_fp8_tile_scale(np.float32([0.0]))[0] == 1.0
+
+
+def test_kv_fp8_rows_roundtrip_representable_values():
+    """Rows built from e4m3 values times a power of two, each tile holding a +-448 code so
+    that its scale is forced: quantizing the decoded row gives the same bytes back, and the
+    byte layout (codes, bf16 rope, fp32 scales) is the documented one."""
+    rng = np.random.default_rng(6)
+    n = 64
+    finite = np.arange(0, 127)                                   # +0 .. +448
+    codes = rng.choice(finite, size=(n, 512)) | (rng.integers(0, 2, (n, 512)) << 7)
+    codes[:, ::128] = 0x7E | (rng.integers(0, 2, (n, 4)) << 7)   # |448| in every tile
+    e = rng.integers(-20, 20, size=(n, 4))
+    scale = np.ldexp(1.0, e).astype(np.float32)
+    nope = oracle.decode_fp8_e4m3(codes.astype(np.uint8)).reshape(n, 4, 128) * scale[:, :, None]
+    rope_bits = to_bf16_bits(rng.standard_normal((n, 64)).astype(np.float32))
+    x = np.concatenate([nope.reshape(n, 512), oracle.decode_bf16(rope_bits)], axis=1).astype(np.float32)
+    rows = oracle.quantize_kv_fp8_rows(x)
+    assert rows.shape == (n, oracle.KV_FP8_ROW_BYTES)
+    assert np.array_equal(rows[:, :512], codes.astype(np.uint8))
+    assert np.array_equal(rows[:, 512:640].copy().view("<u2"), rope_bits)
+    assert np.array_equal(rows[:, 640:].copy().view("<f4"), scale)
+    assert np.array_equal(oracle.decode_kv_fp8_rows(rows), x.astype(np.float64))
+
+
+def test_kv_fp8_codes_are_the_nearest_e4m3_values():
+    """Brute force over the 253 finite e4m3 values: every code decodes to a nearest value of
+    x / scale (ties to the even code), and no tile saturates."""
+    rng = np.random.default_rng(7)
+    n = 200
+    x = (rng.standard_normal((n, 576)) * np.exp(rng.uniform(-6, 6, (n, 1)))).astype(np.float32)
+    x[3, :128] = 0.0                                             # all-zero tile: scale 1
+    rows = oracle.quantize_kv_fp8_rows(x)
+    scale = rows[:, 640:].copy().view("<f4").astype(np.float64)
+    assert scale[3, 0] == 1.0 and np.all(rows[3, :128] == 0)
+    q = x[:, :512].astype(np.float64).reshape(n, 4, 128) / scale[:, :, None]
+    assert np.abs(q).max() <= 448.0
+    table = oracle.fp8_e4m3_table()
+    vals = table[np.isfinite(table)]
+    got = oracle.decode_fp8_e4m3(rows[:, :512]).reshape(n, 4, 128)
+    d = np.abs(q[..., None] - vals[None, None, None, :])
+    best = d.min(axis=-1)
+    assert np.array_equal(np.abs(q - got), best)
+    # dequantized error bound: half the e4m3 spacing at the top binade, times the scale
+    deq = oracle.decode_kv_fp8_rows(rows)
+    err = np.abs(deq[:, :512] - x[:, :512]).reshape(n, 4, 128)
+    assert np.all(err <= 16.0 * scale[:, :, None])
+    assert np.array_equal(deq[:, 512:], oracle.decode_bf16(to_bf16_bits(x[:, 512:])))

@@ -126,3 +126,38 @@ def test_mutations_fail_the_bf16_bound_on_sharp_inputs():
     assert not oracle.check_attention(O_noscale, O, 2e-2).ok
     O_shift, _ = oracle.sfa_dense(q, np.roll(rows, -64, axis=1), spec.softmax_scale, 512)
     assert not oracle.check_attention(O_shift, O, 2e-2).ok
+
+
+def test_fp8_rows_path_equals_the_f32_path_on_representable_rows():
+    """SFA over fp8 latent rows reads the row through the tile scales: with rows whose values
+    are exactly representable (e4m3 codes times powers of two, bf16 rope), the fp8 path and
+    the fp32 path over the same values give identical results; a row read with a wrong tile
+    scale, or with the rope columns misplaced, would not."""
+    import dataclasses
+    spec = scaled_spec(workload(1), seq_lens=[700], sfa_heads=16, top_k=64, block_size=64,
+                       permute=True, extra_blocks=1)
+    inp = make_inputs(spec, seed=11, sfa_dist="sharp")
+    rng = np.random.default_rng(12)
+    rows = rows_of(inp, 0, np.arange(700))
+    codes = rng.integers(0, 127, size=(700, 512)) | (rng.integers(0, 2, (700, 512)) << 7)
+    codes[:, ::128] = 0x7E
+    e = rng.integers(-12, -4, size=(700, 4))
+    vals = oracle.decode_fp8_e4m3(codes.astype(np.uint8)).reshape(700, 4, 128) * np.ldexp(1.0, e)[:, :, None]
+    rope = oracle.decode_bf16(oracle.encode_bf16_rne(rng.standard_normal((700, 64)).astype(np.float32) * 0.05))
+    x = np.concatenate([vals.reshape(700, 512), rope], axis=1).astype(np.float32)
+    inp.kv_pool[rows] = x
+    pool8 = np.zeros((inp.kv_pool.shape[0], oracle.KV_FP8_ROW_BYTES), np.uint8)
+    pool8[rows] = oracle.quantize_kv_fp8_rows(x)
+    q_bf16 = oracle.encode_bf16_rne(inp.q_sfa)
+    inp.q_sfa[...] = oracle.decode_bf16(q_bf16)
+    inp8 = dataclasses.replace(inp, spec=dataclasses.replace(spec, kv_dtype="fp8"), kv_pool=pool8,
+                               q_sfa=q_bf16)
+    idx = rng.choice(700, size=(1, 64), replace=False)
+    O32, L32 = oracle.sfa(inp, idx)
+    O8, L8 = oracle.sfa(inp8, idx)
+    assert np.array_equal(O8, O32) and np.array_equal(L8, L32)
+    # a swapped pair of tile scales changes the result
+    bad = pool8.copy()
+    bad[rows, 640:644], bad[rows, 644:648] = pool8[rows, 644:648], pool8[rows, 640:644]
+    Ob, _ = oracle.sfa(dataclasses.replace(inp8, kv_pool=bad), idx)
+    assert np.abs(Ob - O32).max() > 1e-3
