@@ -16,7 +16,10 @@ Prints one JSON line (see the keys below), including the roofline of the dominan
 recorded around it in every 16th step of the timed region; an event pair costs the GPU a few
 microseconds, so the other steps run unbracketed) and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--config 4]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--config 4] [--sfa-kv fp8]
+
+--sfa-kv fp8 stores the latent cache as fp8 rows quantized per 128-column tile (written by
+dsa_store_kv on the GPU before timing) instead of bf16 rows.
 """
 from __future__ import annotations
 
@@ -58,16 +61,33 @@ def indexer_bytes(spec, V):
     return b
 
 
+KV_FP8_ROW_BYTES = 656
+
+
 def sfa_bytes(spec, V):
     """Algorithmic bytes of one SFA launch: the index list, the selected latent rows, the
-    queries and the outputs."""
-    e = ELEM[spec.kv_dtype]
+    queries and the outputs (fp8 rows: 656 bytes, bf16 queries and outputs)."""
+    fp8 = spec.kv_dtype == "fp8"
+    e = 2 if fp8 else ELEM[spec.kv_dtype]
+    row = KV_FP8_ROW_BYTES if fp8 else spec.d_qk * e
     b = 0
     for v in V:
         k_eff = min(spec.top_k, int(v))
-        b += 4 * spec.top_k + k_eff * spec.d_qk * e
+        b += 4 * spec.top_k + k_eff * row
         b += spec.sfa_heads * (spec.d_qk * e + spec.d_v * e)
     return b
+
+
+class Fp8RowsOfBf16Pool:
+    """The oracle's fp8 rows of a bf16 latent pool, quantized when indexed (the CPU baseline
+    reads only the selected rows of each query)."""
+
+    def __init__(self, bf16_pool):
+        self.pool = bf16_pool
+
+    def __getitem__(self, rows):
+        import oracle
+        return oracle.quantize_kv_fp8_rows(oracle.decode(self.pool[rows], "bf16").astype(np.float32))
 
 
 def sfa_flops(spec, V):
@@ -142,6 +162,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sfa-kv", choices=("bf16", "fp8"), default="bf16",
+                    help="latent cache storage read by SFA")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel for scaling the HBM byte counters) and exit")
@@ -174,6 +196,10 @@ def main():
     seed = args.seed or args.config
     print(f"bench: generating {spec.name} (seed {seed})", file=sys.stderr, flush=True)
     inp = make_inputs(spec, seed=seed)
+    if args.sfa_kv == "fp8":
+        import dataclasses
+        spec = dataclasses.replace(spec, kv_dtype="fp8", name=spec.name + "_fp8kv")
+        inp = dataclasses.replace(inp, spec=spec, kv_pool=Fp8RowsOfBf16Pool(inp.kv_pool))
     V = [int(v) for v in inp.q_visible]
     T = spec.num_queries
 
@@ -183,7 +209,18 @@ def main():
     copies = args.copies or max(3, min(12, math.ceil(1.0e9 / per_copy) + 1))
     if spec.name.startswith("prefill"):
         copies = args.copies or 1
-    base = to_device(inp, "cuda")
+    if args.sfa_kv == "fp8":
+        bf16_pool = inp.kv_pool.pool
+        inp.kv_pool = bf16_pool
+        base = to_device(inp, "cuda")
+        n = base.kv_pool.shape[0]
+        pool8 = torch.zeros((n, KV_FP8_ROW_BYTES), dtype=torch.uint8, device="cuda")
+        dsa.store_kv(base.kv_pool, torch.arange(n, dtype=torch.int64, device="cuda"), pool8)
+        torch.cuda.synchronize()
+        base.kv_pool = pool8
+        inp.kv_pool = Fp8RowsOfBf16Pool(bf16_pool)
+    else:
+        base = to_device(inp, "cuda")
     devs = [base]
     for _ in range(copies - 1):
         c = copy.copy(base)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
   DSA_OK = 0,
@@ -91,6 +91,20 @@ typedef struct {
 #define DSA_MAX_CONTEXT (1 << 22)  /* longest visible prefix a query may have (4M tokens)    */
 #define DSA_MAX_TOPK 2048
 
+/* FP8 latent KV row (kv_dtype / pool_dtype DSA_FP8_E4M3, MLA geometry d_qk = 576, d_v = 512):
+ * the SFA cache quantized per token and per tile of 128 elements ("Day0 Adaptation and
+ * Performance Optimization for Novel Long-Sequence Reasoning Models", section 4; "Day0
+ * Adaptation and Sparse Attention Optimization for Long-Sequence LLM Inference", section 5;
+ * "Optimizing and Deploying Ultra-Long Sequence Inference Architectures", section II; "Large
+ * Model Inference Acceleration: Day-0 Adaptation...", section 2.2).  One row is 656 bytes:
+ *   bytes [0, 512)    e4m3 codes of columns 0 .. 511, four tiles of 128 columns;
+ *   bytes [512, 640)  columns 512 .. 575 (the rope part) as bf16, little-endian;
+ *   bytes [640, 656)  the four tiles' scales as fp32.
+ * Column j < 512 is code_j * scale[j / 128].  A tile's scale is the smallest power of two
+ * 2^e (-126 <= e <= 127) with max |x| <= 448 * 2^e over the tile (1 for an all-zero tile), so
+ * x / scale never saturates and every dequantized value is exact in bf16. */
+#define DSA_KV_FP8_ROW_BYTES 656
+
 /* ---------------------------------------------------------------------------------------
  * Lightning indexer + Top-K
  *
@@ -138,8 +152,10 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
  *     out_lse[t, h] = log(sum_j exp(z_j))           (natural log; optional)
  * With J empty: out = 0 and out_lse = -inf.
  *
- * dtype applies to q, kv_pool and out: BF16 (fp32 accumulation, MFMA) or F32 (reference
- * mode, fp32 throughout).  d_qk % 64 == 0, d_v % 64 == 0, d_v <= d_qk <= 1024,
+ * dtype applies to q and out: BF16 (fp32 accumulation, MFMA) or F32 (reference mode, fp32
+ * throughout).  kv_dtype is the storage of kv_pool: the same as dtype, or FP8_E4M3 with
+ * dtype BF16 for the tile-quantized rows above (d_qk = 576 and d_v = 512 only; R_j is the
+ * dequantized row).  d_qk % 64 == 0, d_v % 64 == 0, d_v <= d_qk <= 1024,
  * 1 <= n_heads <= 1024; the BF16 path needs n_heads % 32 == 0, d_qk = 576 and d_v = 512 (the
  * MLA latent geometry), other shapes run the reference path.  idx entries must be -1 or
  * positions whose rows exist; they need not be sorted.
@@ -150,7 +166,8 @@ size_t dsa_sparse_attn_workspace_size(int32_t num_queries, int32_t n_heads, int3
                                       int32_t d_v);
 
 dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool,
-                           int32_t n_heads, int32_t d_qk, int32_t d_v, float softmax_scale,
+                           dsa_dtype kv_dtype, int32_t n_heads, int32_t d_qk, int32_t d_v,
+                           float softmax_scale,
                            const dsa_layout* layout, const dsa_queries* queries,
                            const int32_t* idx, int32_t top_k, void* out, float* out_lse,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -166,7 +183,10 @@ dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool,
  *   all zero), code = fp8(k / scale) rounded to nearest even, saturating at +-448; the scale
  *   goes to k_scale[slot[i]].
  * dsa_store_kv: kv_new [n_tokens, d_qk] (src_dtype F32 or BF16) -> kv_pool rows slot[i] in
- *   pool_dtype (F32 or BF16; F32 -> BF16 rounds to nearest even).
+ *   pool_dtype (F32 or BF16; F32 -> BF16 rounds to nearest even), or FP8_E4M3 for the
+ *   tile-quantized rows of DSA_KV_FP8_ROW_BYTES bytes (d_qk = 576): per tile the scale
+ *   defined there, code = fp8(x / scale) rounded to nearest even; the rope columns are
+ *   rounded to bf16 (nearest even) or copied.
  * slot[i] is the pool row (block * block_size + offset) of token i; rows must be distinct.
  * --------------------------------------------------------------------------------------- */
 dsa_status dsa_store_index_keys(const float* k_new, int32_t n_tokens, int32_t head_dim,

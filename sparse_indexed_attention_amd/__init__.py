@@ -67,7 +67,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dsa_indexer_topk.restype = _I32
     lib.dsa_sparse_attn_workspace_size.argtypes = [_I32, _I32, _I32, _I32]
     lib.dsa_sparse_attn_workspace_size.restype = _SZ
-    lib.dsa_sparse_attn.argtypes = [_P, _I32, _P, _I32, _I32, _I32, ctypes.c_float,
+    lib.dsa_sparse_attn.argtypes = [_P, _I32, _P, _I32, _I32, _I32, _I32, ctypes.c_float,
                                     ctypes.POINTER(DsaLayout), ctypes.POINTER(DsaQueries),
                                     _P, _I32, _P, _P, _P, _SZ, _P]
     lib.dsa_sparse_attn.restype = _I32
@@ -167,8 +167,10 @@ def indexer_topk(q, head_w, k_pool, k_scale, layout: DsaLayout, q_seq, q_visible
 def sparse_attn(q, kv_pool, idx, layout: DsaLayout, q_seq, softmax_scale: float, d_v: int = 512,
                 *, out=None, out_lse=None, want_lse: bool = True, workspace=None, stream=None):
     """Sparse Flash Attention.  q [T, H, d_qk] and kv_pool [rows, d_qk] share one dtype
-    (float32, or bfloat16 / int16 bits); idx [T, K] int32 logical positions, -1 skipped.
-    Returns (out [T, H, d_v] in that dtype, lse [T, H] float32 or None)."""
+    (float32, or bfloat16 / int16 bits), or kv_pool holds fp8 latent rows (uint8 [rows, 656],
+    with bf16 q; the layout of DSA_KV_FP8_ROW_BYTES in include/dsa.h); idx [T, K] int32
+    logical positions, -1 skipped.  Returns (out [T, H, d_v] in q's dtype, lse [T, H] float32
+    or None)."""
     torch = _torch()
     lib = load()
     T, H, dqk = q.shape
@@ -180,7 +182,7 @@ def sparse_attn(q, kv_pool, idx, layout: DsaLayout, q_seq, softmax_scale: float,
     queries = make_queries(q_seq, None, 0)
     if workspace is None:
         workspace = zeroed_workspace(sfa_workspace_bytes(T, H, K, d_v), q.device)
-    st = lib.dsa_sparse_attn(_ptr(q), _dtype_code(q), _ptr(kv_pool), H, dqk, d_v,
+    st = lib.dsa_sparse_attn(_ptr(q), _dtype_code(q), _ptr(kv_pool), _dtype_code(kv_pool), H, dqk, d_v,
                              float(softmax_scale), ctypes.byref(layout), ctypes.byref(queries),
                              _ptr(idx), K, _ptr(out), _ptr(out_lse), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream))
@@ -199,7 +201,8 @@ def store_index_keys(k_new, slot, k_pool, k_scale=None, stream=None):
 
 
 def store_kv(kv_new, slot, kv_pool, stream=None):
-    """kv_new [n, d_qk] (float32 | bf16 bits) -> kv_pool rows slot[i] in kv_pool's dtype."""
+    """kv_new [n, d_qk] (float32 | bf16 bits) -> kv_pool rows slot[i] in kv_pool's dtype
+    (uint8 [rows, 656]: the fp8 latent rows of include/dsa.h, d_qk = 576)."""
     st = load().dsa_store_kv(_ptr(kv_new), _dtype_code(kv_new), kv_new.shape[0], kv_new.shape[1],
                              _ptr(slot), _ptr(kv_pool), _dtype_code(kv_pool), _stream(stream))
     if st != 0:

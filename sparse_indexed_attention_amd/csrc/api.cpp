@@ -137,14 +137,17 @@ size_t dsa_sparse_attn_workspace_size(int32_t num_queries, int32_t n_heads, int3
   return plan_sfa(num_queries, n_heads, top_k, d_v, n_heads % 32 == 0).bytes;
 }
 
-dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool, int32_t n_heads,
-                           int32_t d_qk, int32_t d_v, float softmax_scale,
+dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool,
+                           dsa_dtype kv_dtype, int32_t n_heads, int32_t d_qk, int32_t d_v,
+                           float softmax_scale,
                            const dsa_layout* layout, const dsa_queries* queries,
                            const int32_t* idx, int32_t top_k, void* out, float* out_lse,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !kv_pool || !idx || !out) return DSA_ERR_NULL;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (kv_dtype != dtype && !(kv_dtype == DSA_FP8_E4M3 && dtype == DSA_BF16)) return DSA_ERR_DTYPE;
   if (n_heads < 1 || n_heads > 1024) return DSA_ERR_SHAPE;
+  if (kv_dtype == DSA_FP8_E4M3 && (d_qk != kSfaDqk || d_v != kSfaDv)) return DSA_ERR_UNSUPPORTED;
   if (d_qk < 64 || d_qk % 64 != 0 || d_v < 64 || d_v % 64 != 0 || d_v > d_qk) return DSA_ERR_SHAPE;
   if (d_qk > 1024) return DSA_ERR_UNSUPPORTED;
   if (top_k < 1) return DSA_ERR_SHAPE;
@@ -173,6 +176,7 @@ dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool, 
   p.K = top_k;
   p.scale = softmax_scale;
   p.dtype = dtype;
+  p.kv_dtype = kv_dtype;
   p.heads_per_wg = pl.heads_per_wg;
   p.n_hg = pl.n_hg;
   p.rows_per_split = pl.rows_per_split;
@@ -206,9 +210,10 @@ dsa_status dsa_store_kv(const void* kv_new, dsa_dtype src_dtype, int32_t n_token
                         const int64_t* slot, void* kv_pool, dsa_dtype pool_dtype, void* stream) {
   if (!kv_new || !slot || !kv_pool) return DSA_ERR_NULL;
   if ((src_dtype != DSA_F32 && src_dtype != DSA_BF16) ||
-      (pool_dtype != DSA_F32 && pool_dtype != DSA_BF16))
+      (pool_dtype != DSA_F32 && pool_dtype != DSA_BF16 && pool_dtype != DSA_FP8_E4M3))
     return DSA_ERR_DTYPE;
   if (n_tokens < 1 || n_tokens > (1 << 30) || d_qk < 1) return DSA_ERR_SHAPE;
+  if (pool_dtype == DSA_FP8_E4M3 && d_qk != kSfaDqk) return DSA_ERR_UNSUPPORTED;
   if (misaligned(kv_new) || misaligned(slot) || misaligned(kv_pool)) return DSA_ERR_ALIGN;
   const hipError_t e = launch_store_kv(kv_new, src_dtype, n_tokens, d_qk, slot, kv_pool,
                                        pool_dtype, static_cast<hipStream_t>(stream));

@@ -55,6 +55,7 @@ hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t st
 // ------------------------------------------------------------------ sparse attention
 constexpr int kSfaDqk = 576;
 constexpr int kSfaDv = 512;
+constexpr int kSfaRowF8 = 656;        // fp8 latent row: 512 codes, 64 bf16, 4 fp32 tile scales
 
 struct SfaPlan {
   int32_t heads_per_wg;   // heads handled by one workgroup (fast path)
@@ -73,6 +74,7 @@ struct SfaParams {
   int32_t T, H, dqk, dv, K;
   float scale;
   int32_t dtype;
+  int32_t kv_dtype;       // dtype, or kDtFP8 for the tile-quantized latent rows
   int32_t heads_per_wg, n_hg, rows_per_split, nsplit;
   void* out;              // [T, H, d_v]
   float* lse;             // [T, H] or nullptr

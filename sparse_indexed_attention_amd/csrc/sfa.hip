@@ -25,6 +25,11 @@
 //     lane holds), and the V operand comes straight from the row-major tile through the
 //     transposing LDS read ds_read_b64_tr_b16, which gathers one dim of four rows into a lane.
 //   * Slices of the index list are merged by a log-sum-exp weighted combine kernel.
+//   * fp8 latent rows (656 bytes: four 128-column tiles of e4m3 codes with power-of-two
+//     scales, the rope columns in bf16): tiles of fp8 rows stream into four smaller LDS
+//     staging buffers (three or four tiles in flight instead of two), and one pass widens
+//     the landed tile into the bf16 tile with v_cvt_scalef32_pk_bf16_fp8, exactly (a code
+//     times a power of two is a bf16 value); the contractions then run as above.
 // Reference path (fp32 storage or other shapes): one workgroup per (query, head), fp32.
 
 #include <cstdlib>
@@ -42,6 +47,11 @@ constexpr int kTileSlots = kTileRows * kLdsChunks;       // 2336
 constexpr int kTileBytes = kTileSlots * 16;              // 37376
 constexpr int kTileLoads = (kTileSlots + 63) / 64;       // 37 direct-to-LDS loads per tile
 constexpr int kTileBufs = 3;                             // LDS tile buffers (two tiles ahead)
+constexpr int kRowChunksF8 = kSfaRowF8 / 16;             // 41 sixteen-byte chunks per fp8 row
+constexpr int kTileSlotsF8 = kTileRows * kRowChunksF8;   // 1312 (rows packed, no padding)
+constexpr int kTileBytesF8 = kTileSlotsF8 * 16;          // 20992
+constexpr int kTileLoadsF8 = (kTileSlotsF8 + 63) / 64;   // 21
+constexpr int kStageBufs = 4;                            // fp8 staging buffers
 constexpr int kBtLds = 4096;                             // block-table entries staged in LDS
 constexpr int kPStride = 80;                             // bytes per head row of the shared P tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -97,12 +107,15 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-template <int NW>
+template <int NW, bool F8>
 __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   constexpr int NTS = NW * 64;
-  constexpr int LPW = (kTileLoads + NW - 1) / NW;  // loads per wave per tile (at most)
-  constexpr int LPW_MIN = kTileLoads / NW;          // ... and at least
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[kTileBufs][kTileBytes];
+  constexpr int TLOADS = F8 ? kTileLoadsF8 : kTileLoads;
+  constexpr int LPW = (TLOADS + NW - 1) / NW;      // loads per wave per tile (at most)
+  constexpr int LPW_MIN = TLOADS / NW;              // ... and at least
+  // bf16 tiles (fp8 rows: one, filled from the staging buffers)
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[F8 ? 1 : kTileBufs][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[F8 ? kStageBufs : 1][F8 ? kTileBytesF8 : 16];
   __shared__ int32_t rows[kMaxTopK];                // pool row of each slice entry, -1 if none
   __shared__ int32_t bt_lds[kBtLds];                // the sequence's block-table row
   __shared__ __attribute__((aligned(16))) float hv[NW * 32];   // per-head values
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   // each wave issues the same number of loads for every tile: the vmcnt waits below count
   // on that.
   auto issue = [&](int tile, int buf) {
-    uint8_t* tb = tiles[buf];
+    uint8_t* tb = F8 ? stage[buf] : tiles[buf];
     // an opaque zero: the slot arithmetic below is redone per call instead of being hoisted
     // out of the tile loop into registers that the attention step needs
     int z0 = 0;
@@ -191,13 +204,49 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int I = wave + NW * u;
-      if (LPW != LPW_MIN && I >= kTileLoads) break;
+      if (LPW != LPW_MIN && I >= TLOADS) break;
       const int P = 64 * I + lane + z0;
-      const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
-      if (P < kTileSlots && ch < kRowChunks) {
-        const int row = rows[tile * kTileRows + rr];
-        load16_to_lds(row >= 0 ? kv + (size_t)row * kRowBytes + 16 * ch : zero, lds_u32(tb + 1024 * I));
+      if constexpr (F8) {
+        // fp8 rows are packed in the staging buffer: slot P is chunk P % 41 of row P / 41
+        const int rr = P / kRowChunksF8, ch = P - rr * kRowChunksF8;
+        if (P < kTileSlotsF8) {
+          const int row = rows[tile * kTileRows + rr];
+          load16_to_lds(row >= 0 ? kv + (size_t)row * kSfaRowF8 + 16 * ch : zero, lds_u32(tb + 1024 * I));
+        }
+      } else {
+        const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
+        if (P < kTileSlots && ch < kRowChunks) {
+          const int row = rows[tile * kTileRows + rr];
+          load16_to_lds(row >= 0 ? kv + (size_t)row * kRowBytes + 16 * ch : zero, lds_u32(tb + 1024 * I));
+        }
       }
+    }
+  };
+  // fp8 rows: widens the staged tile into the bf16 tile.  Work item s = (row s / 36, 16-column
+  // group g = s % 36): groups 0..31 are codes of tile g / 8, widened with its scale; groups
+  // 32..35 are the bf16 rope columns, copied.
+  auto widen = [&](const uint8_t* sb, uint8_t* tb) {
+    for (int s = tid; s < kTileRows * 36; s += NTS) {
+      const int rr = s / 36, g = s - rr * 36;
+      const uint8_t* srow = sb + rr * kSfaRowF8;
+      u32x4 w0, w1;
+      if (g < 32) {
+        const u32x4 cd = *(const u32x4*)(srow + 16 * g);
+        const float sc = *(const float*)(srow + 640 + 4 * (g >> 3));
+        uint32_t o[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd[k], sc, false));
+          o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd[k], sc, true));
+        }
+        w0 = u32x4{o[0], o[1], o[2], o[3]};
+        w1 = u32x4{o[4], o[5], o[6], o[7]};
+      } else {
+        w0 = *(const u32x4*)(srow + 512 + 32 * (g - 32));
+        w1 = *(const u32x4*)(srow + 512 + 32 * (g - 32) + 16);
+      }
+      *(u32x4*)(tb + tile_off(rr, 2 * g)) = w0;
+      *(u32x4*)(tb + tile_off(rr, 2 * g + 1)) = w1;
     }
   };
 
@@ -325,6 +374,27 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
 
 #pragma unroll
   for (int n = 0; n < NW * NB; ++n) o[n] = f32x16{};
+  if constexpr (F8) {
+    // fp8 tiles stream through kStageBufs staging buffers; a landed tile is widened into the
+    // bf16 tile, which frees its staging buffer for the tile kStageBufs later
+    static_assert(kStageBufs == 4 && 3 * LPW_MIN < 64, "waits below");
+    for (int i = 0; i < kStageBufs && i < ntiles; ++i) issue(i, i);
+    int buf = 0;
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int ahead = min(ntiles - 1 - tile, kStageBufs - 1);   // later tiles in flight
+      if (ahead >= 3) wait_vmcnt<3 * LPW_MIN>();
+      else if (ahead == 2) wait_vmcnt<2 * LPW_MIN>();
+      else if (ahead == 1) wait_vmcnt<LPW_MIN>();
+      else wait_vmcnt<0>();
+      __syncthreads();                           // every wave's loads of `tile` have landed
+      widen(stage[buf], tiles[0]);
+      __syncthreads();                           // the bf16 tile is complete, the buffer free
+      if (tile + kStageBufs < ntiles) issue(tile + kStageBufs, buf);
+      attend(tile, tiles[0]);
+      __syncthreads();                           // the bf16 tile and the P tile are free again
+      buf = buf == kStageBufs - 1 ? 0 : buf + 1;
+    }
+  } else {
   // Tiles stream through kTileBufs LDS buffers, kTileBufs - 1 of them ahead of the one being
   // computed.
   static_assert(kTileBufs == 3, "prologue below issues three tiles");
@@ -342,6 +412,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     __syncthreads();                             // the buffer and the P tile are free again
     if (tile + kTileBufs < ntiles) issue(tile + kTileBufs, buf);
     buf = buf == kTileBufs - 1 ? 0 : buf + 1;
+  }
   }
 
   // per-head totals: the two lane halves of a column hold disjoint rows of its head
@@ -422,7 +493,13 @@ __device__ void reference_head(const SfaParams& p, int t, int h, RefSmem& ws) {
     ws.qs[d] = f32 ? ((const float*)p.q)[qi] : bf16_bits_to_f32(((const uint16_t*)p.q)[qi]);
   }
   __syncthreads();
+  const bool f8 = p.kv_dtype == kDtFP8;
   auto kvat = [&](int64_t row, int d) -> float {
+    if (f8) {
+      const uint8_t* r8 = (const uint8_t*)p.kv + (size_t)row * kSfaRowF8;
+      if (d < kSfaDv) return fp8_e4m3_to_f32(r8[d]) * ((const float*)(r8 + 640))[d >> 7];
+      return bf16_bits_to_f32(((const uint16_t*)(r8 + kSfaDv))[d - kSfaDv]);
+    }
     const size_t i = (size_t)row * p.dqk + d;
     return f32 ? ((const float*)p.kv)[i] : bf16_bits_to_f32(((const uint16_t*)p.kv)[i]);
   };
@@ -682,10 +759,20 @@ hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream) {
   // one workgroup per (query, slice) pair rounded up to whole groups of 8, times head groups
   const int pairs = (p.T * p.nsplit + 7) / 8 * 8;
   const dim3 grid(pairs * p.n_hg);
+  const bool f8 = p.kv_dtype == kDtFP8;
   switch (p.heads_per_wg) {
-    case 128: hipLaunchKernelGGL(sfa_mfma_kernel<4>, grid, dim3(256), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(sfa_mfma_kernel<2>, grid, dim3(128), 0, stream, p); break;
-    default: hipLaunchKernelGGL(sfa_mfma_kernel<1>, grid, dim3(64), 0, stream, p); break;
+    case 128:
+      if (f8) hipLaunchKernelGGL((sfa_mfma_kernel<4, true>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((sfa_mfma_kernel<4, false>), grid, dim3(256), 0, stream, p);
+      break;
+    case 64:
+      if (f8) hipLaunchKernelGGL((sfa_mfma_kernel<2, true>), grid, dim3(128), 0, stream, p);
+      else hipLaunchKernelGGL((sfa_mfma_kernel<2, false>), grid, dim3(128), 0, stream, p);
+      break;
+    default:
+      if (f8) hipLaunchKernelGGL((sfa_mfma_kernel<1, true>), grid, dim3(64), 0, stream, p);
+      else hipLaunchKernelGGL((sfa_mfma_kernel<1, false>), grid, dim3(64), 0, stream, p);
+      break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -35,7 +35,7 @@ def run_sfa(m, inp, idx, d=None, *, workspace=None):
     out, lse = m.sparse_attn(d.q_sfa, d.kv_pool, ti, layout_of(m, d), d.q_seq,
                              inp.spec.softmax_scale, inp.spec.d_v, workspace=workspace)
     torch.cuda.synchronize()
-    O = oracle.decode(bits_of(out), inp.spec.kv_dtype)
+    O = oracle.decode(bits_of(out), "bf16" if inp.spec.kv_dtype == "fp8" else inp.spec.kv_dtype)
     return O, lse.cpu().numpy().astype(np.float64)
 
 

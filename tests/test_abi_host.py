@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     for s in range(8):
         assert lib.dsa_status_string(s).startswith(b"DSA_")
 
@@ -101,11 +101,14 @@ def test_workspace_sizes_are_monotone(lib):
 
 
 def _sfa_call(lib, m, **kw):
-    args = dict(q=A[0], dt=1, kv=A[2], H=128, dqk=576, dv=512, scale=1 / 24, idx=A[3], K=2048,
-                out=A[4], lse=A[5], ws=A[6], wsb=1 << 40)
+    args = dict(q=A[0], dt=1, kv=A[2], kvd=None, H=128, dqk=576, dv=512, scale=1 / 24, idx=A[3],
+                K=2048, out=A[4], lse=A[5], ws=A[6], wsb=1 << 40)
     args.update(kw)
+    if args["kvd"] is None:
+        args["kvd"] = args["dt"]
     lay, qs = _lq(m)
-    return lib.dsa_sparse_attn(args["q"], args["dt"], args["kv"], args["H"], args["dqk"], args["dv"],
+    return lib.dsa_sparse_attn(args["q"], args["dt"], args["kv"], args["kvd"], args["H"], args["dqk"],
+                               args["dv"],
                                args["scale"], ctypes.byref(lay), ctypes.byref(qs), args["idx"],
                                args["K"], args["out"], args["lse"], args["ws"], args["wsb"], None)
 
@@ -124,6 +127,11 @@ def test_sparse_attn_validation(lib):
     assert _sfa_call(lib, m, out=A[4] + 4) == 6
     assert _sfa_call(lib, m, wsb=8) == 5
     assert _sfa_call(lib, m, scale=float("nan")) == 2
+    # fp8 latent rows: bf16 queries and the 576/512 geometry only
+    assert _sfa_call(lib, m, kvd=2, dt=0) == 3
+    assert _sfa_call(lib, m, kvd=0, dt=1) == 3
+    assert _sfa_call(lib, m, kvd=2, dqk=640, dv=512) == 4
+    assert _sfa_call(lib, m, kvd=2, dqk=576, dv=448) == 4
 
 
 def test_store_validation(lib):
@@ -133,3 +141,4 @@ def test_store_validation(lib):
     assert lib.dsa_store_index_keys(A[0], 4, 128, A[1], A[2], 7, A[3], None) == 3
     assert lib.dsa_store_kv(A[0], 2, 4, 576, A[1], A[2], 1, None) == 3
     assert lib.dsa_store_kv(A[0], 1, 4, 576, A[1] + 8, A[2], 1, None) == 6
+    assert lib.dsa_store_kv(A[0], 1, 4, 512, A[1], A[2], 2, None) == 4   # fp8 rows: d_qk 576 only

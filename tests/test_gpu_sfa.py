@@ -16,7 +16,7 @@ from tests.helpers import rows_of
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": (2e-2, 1e-4), "f32": (1e-5, 1e-6)}
+TOL = {"bf16": (2e-2, 1e-4), "f32": (1e-5, 1e-6), "fp8": (2e-2, 1e-4)}
 
 
 def oracle_idx(inp, K=None, seed=0, minus_one_frac=0.0):
