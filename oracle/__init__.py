@@ -24,7 +24,8 @@ forms, brute force, library routines); see tests/test_oracle_*.py.
 """
 from .codecs import (decode, decode_bf16, decode_fp8_e4m3, fp8_e4m3_table, encode_bf16_rne,
                      encode_fp8_e4m3, quantize_fp8_per_token, kv_fp8_tile_scale,
-                     quantize_kv_fp8_rows, decode_kv_fp8_rows, KV_FP8_ROW_BYTES)
+                     quantize_kv_fp8_rows, decode_kv_fp8_rows, KV_FP8_ROW_BYTES,
+                     mx_scale_bytes, quantize_mxfp8, decode_mxfp8)
 from .paging import logical_rows, depage
 from .indexer import (index_scores, to_fp32_score, topk_order, IndexerResult,
                       indexer_topk_query, indexer_topk)
@@ -34,7 +35,8 @@ from .compare import TopkCheck, check_topk_row, check_topk, AttnCheck, check_att
 __all__ = [
     "decode", "decode_bf16", "decode_fp8_e4m3", "fp8_e4m3_table", "encode_bf16_rne",
     "encode_fp8_e4m3", "quantize_fp8_per_token", "kv_fp8_tile_scale", "quantize_kv_fp8_rows",
-    "decode_kv_fp8_rows", "KV_FP8_ROW_BYTES", "logical_rows", "depage", "index_scores",
+    "decode_kv_fp8_rows", "KV_FP8_ROW_BYTES", "mx_scale_bytes", "quantize_mxfp8",
+    "decode_mxfp8", "logical_rows", "depage", "index_scores",
     "to_fp32_score", "topk_order", "IndexerResult", "indexer_topk_query", "indexer_topk",
     "sfa_dense", "sfa_query", "sfa", "TopkCheck", "check_topk_row", "check_topk",
     "AttnCheck", "check_attention",

@@ -21,6 +21,15 @@ Formats:
   all-zero tile), the code is x / scale (exact) rounded to the nearest e4m3 value, ties to
   the even code; the 64 rope columns of the 576-wide latent row stay in bf16.  A row is 656
   bytes: 512 codes, 64 bf16 (little-endian), then the four scales as fp32.
+* MXFP8 with groups of 32 for the indexer's queries and keys ("Day0 Adaptation and
+  Performance Optimization for Novel Long-Sequence Reasoning Models", section 4; "Day0
+  Adaptation and Sparse Attention Optimization for Long-Sequence LLM Inference", section 5;
+  "Optimizing and Deploying Ultra-Long Sequence Inference Architectures", section II), read
+  as the OCP microscaling format: every 32 consecutive elements share an E8M0 scale byte s,
+  the value 2^(s - 127); s = floor(log2(max|x|)) - 8 + 127 over the group (8 is the exponent
+  of e4m3's largest power of two), clamped to [0, 254], and 0 for an all-zero group; each
+  code is x / 2^(s - 127) (exact) rounded to the nearest e4m3 value, ties to the even code,
+  saturating at +-448.
 """
 from __future__ import annotations
 
@@ -154,3 +163,36 @@ def decode_kv_fp8_rows(rows: np.ndarray) -> np.ndarray:
     nope = (nope * scale[:, :, None]).reshape(n, KV_NOPE)
     rope = decode_bf16(rows[:, KV_NOPE:640].copy().view("<u2"))
     return np.concatenate([nope, rope], axis=1)
+
+
+MX_GROUP = 32
+
+
+def mx_scale_bytes(amax: np.ndarray) -> np.ndarray:
+    """Group maxima (float32, >= 0) -> E8M0 bytes: floor(log2(amax)) - 8 + 127 clamped to
+    [0, 254]; 0 where amax == 0.  floor(log2(amax)) = k - 1 for amax = f * 2^k, 0.5 <= f < 1
+    (frexp, exact)."""
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    _, k = np.frexp(a)
+    b = np.clip(k - 1 - 8 + 127, 0, 254)
+    return np.where(a == 0.0, 0, b).astype(np.uint8)
+
+
+def quantize_mxfp8(x: np.ndarray):
+    """float32 [..., D] (D % 32 == 0) -> (uint8 codes [..., D], uint8 E8M0 bytes [..., D/32])."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (D // MX_GROUP, MX_GROUP))
+    sb = mx_scale_bytes(np.max(np.abs(g), axis=-1))
+    scale = np.ldexp(np.float32(1.0), sb.astype(np.int32) - 127).astype(np.float32)
+    quot = np.divide(g, scale[..., None], dtype=np.float32)
+    return encode_fp8_e4m3(quot).reshape(x.shape), sb
+
+
+def decode_mxfp8(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
+    """(uint8 codes [..., D], uint8 E8M0 bytes [..., D/32]) -> float64 [..., D] (exact)."""
+    v = decode_fp8_e4m3(codes)
+    D = v.shape[-1]
+    g = v.reshape(v.shape[:-1] + (D // MX_GROUP, MX_GROUP))
+    g = g * np.ldexp(1.0, scale_bytes.astype(np.int64) - 127)[..., None]
+    return g.reshape(v.shape)

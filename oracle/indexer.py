@@ -18,6 +18,9 @@ per-head scores are the Batch x Head x Seq intermediate of section 2.1).  The pa
 formula; the per-head dot product, ReLU, the head weights and the lowest-position tie-break
 are this project's reading.  One key vector per token is shared by all indexer heads.  fp8
 keys are dequantized (code value times the token's fp32 scale) before the dot product.
+MXFP8 keys (k_dtype "mxfp8": codes and one E8M0 byte per 32 dims, see codecs) are
+dequantized the same way, and the query is then quantized to MXFP8 too, per head and group
+of 32 dims, before the dot product: the pages quantize both index Q and K dynamically.
 Everything is float64; products of bf16/fp8/fp32 operands are exact in float64.
 """
 from __future__ import annotations
@@ -27,7 +30,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from .codecs import decode
+from .codecs import decode, decode_mxfp8, quantize_mxfp8
 from .paging import logical_rows
 
 _POS_CHUNK = 1 << 16     # positions are scored independently; the loop only bounds memory
@@ -71,6 +74,8 @@ def query_keys(inp, t: int) -> np.ndarray:
     b = int(inp.q_seq[t])
     V = int(inp.q_visible[t])
     rows = logical_rows(inp.block_table, inp.block_size, inp.seq_stride, b, np.arange(V))
+    if inp.spec.k_dtype == "mxfp8":
+        return decode_mxfp8(inp.k_pool[rows], inp.k_scale[rows])
     keys = decode(inp.k_pool[rows], inp.spec.k_dtype)
     if inp.spec.k_dtype == "fp8":
         keys = keys * inp.k_scale[rows].astype(np.float64)[:, None]
@@ -82,6 +87,8 @@ def indexer_topk_query(inp, t: int, S: Optional[np.ndarray] = None) -> IndexerRe
     V = int(inp.q_visible[t])
     if S is None:
         q = decode(inp.q_idx[t], spec.q_dtype)
+        if spec.k_dtype == "mxfp8":
+            q = decode_mxfp8(*quantize_mxfp8(q.astype(np.float32)))
         w = inp.w[t].astype(np.float64)
         S = index_scores(q, w, query_keys(inp, t))
     S32 = to_fp32_score(S)

@@ -156,3 +156,49 @@ def test_kv_fp8_codes_are_the_nearest_e4m3_values():
     err = np.abs(deq[:, :512] - x[:, :512]).reshape(n, 4, 128)
     assert np.all(err <= 16.0 * scale[:, :, None])
     assert np.array_equal(deq[:, 512:], oracle.decode_bf16(to_bf16_bits(x[:, 512:])))
+
+
+# ---- MXFP8 (groups of 32, E8M0 power-of-two scales) -----------------------------------------
+
+def test_mx_scale_byte_is_floor_log2_minus_8():
+    """Checked in exact float64 from the definition: 2^(e + 8) <= amax < 2^(e + 9) for the
+    scale 2^e, unless clamped at the ends of the E8M0 range; 0 for an all-zero group."""
+    rng = np.random.default_rng(8)
+    a = np.concatenate([
+        np.abs(rng.standard_normal(100000) * np.exp(rng.uniform(-85, 85, 100000))),
+        np.ldexp(1.0, np.arange(-149, 128)),                   # exact powers of two
+        np.nextafter(np.ldexp(np.float32(1), np.arange(-100, 100)).astype(np.float32), np.float32(0)),
+    ]).astype(np.float32)
+    a = a[np.isfinite(a) & (a > 0)]
+    e = oracle.mx_scale_bytes(a).astype(np.int64) - 127
+    af = a.astype(np.float64)
+    inner = (e > -127) & (e < 127)
+    assert np.all(np.ldexp(1.0, e[inner] + 8) <= af[inner])
+    assert np.all(af[inner] < np.ldexp(1.0, e[inner] + 9))
+    assert np.all(af[e == -127] < 2.0 ** -118)
+    assert oracle.mx_scale_bytes(np.float32([0.0]))[0] == 0
+
+
+def test_mx_codes_are_the_nearest_clamped_e4m3_values():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((300, 128)) * np.exp(rng.uniform(-5, 5, (300, 1)))).astype(np.float32)
+    x[7, :32] = 0.0
+    codes, sb = oracle.quantize_mxfp8(x)
+    assert codes.shape == x.shape and sb.shape == (300, 4)
+    scale = np.ldexp(1.0, sb.astype(np.int64) - 127)
+    q = np.clip(x.astype(np.float64).reshape(300, 4, 32) / scale[..., None], -448.0, 448.0)
+    table = oracle.fp8_e4m3_table()
+    vals = table[np.isfinite(table)]
+    got = oracle.decode_fp8_e4m3(codes).reshape(300, 4, 32)
+    best = np.abs(q[..., None] - vals).min(axis=-1)
+    assert np.array_equal(np.abs(q - got), best)
+    assert np.all(codes[7, :32] == 0)
+    assert np.array_equal(oracle.decode_mxfp8(codes, sb), got.reshape(300, 128) * np.repeat(scale, 32, axis=1))
+
+
+def test_mx_is_lossless_on_small_integers():
+    """Integers in [-8, 8]: the group scale is at most 2^-5 and every value times 32 is an
+    e4m3 value, so quantizing loses nothing."""
+    rng = np.random.default_rng(10)
+    x = rng.integers(-8, 9, size=(500, 128)).astype(np.float32)
+    assert np.array_equal(oracle.decode_mxfp8(*oracle.quantize_mxfp8(x)), x.astype(np.float64))

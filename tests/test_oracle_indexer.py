@@ -170,3 +170,34 @@ def test_planted_ties_have_intended_status():
     assert not (set(groups["exterior"].tolist()) & sel)
     bnd = groups["boundary"]
     assert [p in sel for p in bnd.tolist()] == [True] + [False] * (len(bnd) - 1)
+
+
+def test_mxfp8_path_quantizes_query_and_keys():
+    """With integer-exact queries and keys (lossless in MXFP8) the MXFP8 path equals the fp32
+    path exactly; with general values it equals the fp32 path run on the MX-dequantized query
+    and keys, which differs from the unquantized scores."""
+    import dataclasses
+    rng = np.random.default_rng(3)
+    spec = scaled_spec(workload(1), seq_lens=[700], idx_heads=8, idx_dim=64, top_k=50)
+    inp = make_inputs(spec, seed=3, with_sfa=False)
+    rows = rows_of(inp, 0, np.arange(700))
+    for exact in (True, False):
+        kf = (rng.integers(-8, 9, (700, 64)) if exact else rng.standard_normal((700, 64))).astype(np.float32)
+        qf = (rng.integers(-8, 9, inp.q_idx.shape) if exact else rng.standard_normal(inp.q_idx.shape)).astype(np.float32)
+        inp.k_pool[rows] = kf
+        inp.q_idx[...] = qf
+        codes = np.zeros(inp.k_pool.shape, np.uint8)
+        sb = np.zeros((inp.k_pool.shape[0], 2), np.uint8)
+        codes[rows], sb[rows] = oracle.quantize_mxfp8(kf)
+        mx = dataclasses.replace(inp, spec=dataclasses.replace(spec, k_dtype="mxfp8"),
+                                 k_pool=codes, k_scale=sb)
+        S_mx = oracle.indexer_topk_query(mx, 0).S32
+        S_f32 = oracle.indexer_topk_query(inp, 0).S32
+        if exact:
+            assert np.array_equal(S_mx, S_f32)
+        else:
+            deq = dataclasses.replace(inp, k_pool=inp.k_pool.copy(), q_idx=inp.q_idx.copy())
+            deq.k_pool[rows] = oracle.decode_mxfp8(codes[rows], sb[rows]).astype(np.float32)
+            deq.q_idx[...] = oracle.decode_mxfp8(*oracle.quantize_mxfp8(qf)).astype(np.float32)
+            assert np.array_equal(S_mx, oracle.indexer_topk_query(deq, 0).S32)
+            assert not np.array_equal(S_mx, S_f32)
