@@ -19,12 +19,16 @@ microseconds, so the other steps run unbracketed) and the CPU oracle timed on a 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--config 4] [--sfa-kv fp8]
 
 --sfa-kv fp8 stores the latent cache as fp8 rows quantized per 128-column tile (written by
-dsa_store_kv on the GPU before timing) instead of bf16 rows.
+dsa_store_kv on the GPU before timing) instead of bf16 rows.  --idx-keys mxfp8 stores the
+index keys in MXFP8 (e4m3 codes, one E8M0 scale byte per group of 32 dims, written by
+dsa_store_index_keys on the GPU from the same N(0,1) keys) instead of fp8 with per-token
+scales; the CPU baseline then reads the oracle's quantization of the same keys.
 """
 from __future__ import annotations
 
 import argparse
 import copy
+import dataclasses
 import hashlib
 import json
 import math
@@ -40,7 +44,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode queries/sec (indexer+TopK+SFA) at 128K ctx; % peak HBM BW / MFMA"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+ELEM = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "indexer_counters.json")
 
 
@@ -48,7 +52,7 @@ def indexer_bytes(spec, V):
     """Algorithmic bytes one indexer launch must move: every visible key (+ its fp8 scale),
     one block-table entry per 64-token page, the queries and head weights, the index list."""
     ek = ELEM[spec.k_dtype]
-    sk = 4 if spec.k_dtype == "fp8" else 0
+    sk = {"fp8": 4, "mxfp8": spec.idx_dim // 32}.get(spec.k_dtype, 0)
     eq = ELEM[spec.q_dtype]
     b = 0
     for v in V:
@@ -88,6 +92,31 @@ class Fp8RowsOfBf16Pool:
     def __getitem__(self, rows):
         import oracle
         return oracle.quantize_kv_fp8_rows(oracle.decode(self.pool[rows], "bf16").astype(np.float32))
+
+
+class MxKeysOfF32Pool:
+    """The oracle's MXFP8 quantization of an fp32 key pool, done when indexed (the CPU baseline
+    reads only the visible rows of each query): part(0) gives the codes, part(1) the E8M0
+    bytes; the two reads of one row set share one quantization."""
+
+    def __init__(self, f32_pool):
+        self.pool = f32_pool
+        self._last = (None, None)
+
+    def _get(self, rows):
+        key = hashlib.sha1(np.ascontiguousarray(rows).tobytes()).digest()
+        if self._last[0] != key:
+            import oracle
+            self._last = (key, oracle.quantize_mxfp8(self.pool[rows]))
+        return self._last[1]
+
+    def part(self, i):
+        outer = self
+
+        class _Part:
+            def __getitem__(self, rows):
+                return outer._get(rows)[i]
+        return _Part()
 
 
 def sfa_flops(spec, V):
@@ -147,7 +176,9 @@ def cpu_baseline(inp, budget_s=12.0):
             break
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} whole queries (indexer + Top-K + SFA) of the same workload, "
+            "sample": f"{done} whole queries (indexer + Top-K + SFA) of the same workload"
+                      + (" (each including the oracle's MXFP8 quantization of its visible keys)"
+                         if inp.spec.k_dtype == "mxfp8" else "") + ", "
                       f"{el:.1f} s wall, NumPy float64 with {threads} BLAS threads on "
                       f"{cores} available cores"}
 
@@ -164,6 +195,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sfa-kv", choices=("bf16", "fp8"), default="bf16",
                     help="latent cache storage read by SFA")
+    ap.add_argument("--idx-keys", choices=("default", "mxfp8"), default="default",
+                    help="index key storage (default: the workload's)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel for scaling the HBM byte counters) and exit")
@@ -195,15 +228,17 @@ def main():
     spec = workload(args.config)
     seed = args.seed or args.config
     print(f"bench: generating {spec.name} (seed {seed})", file=sys.stderr, flush=True)
+    mx_keys = args.idx_keys == "mxfp8"
+    if mx_keys:
+        spec = dataclasses.replace(spec, k_dtype="f32")
     inp = make_inputs(spec, seed=seed)
     if args.sfa_kv == "fp8":
-        import dataclasses
         spec = dataclasses.replace(spec, kv_dtype="fp8", name=spec.name + "_fp8kv")
         inp = dataclasses.replace(inp, spec=spec, kv_pool=Fp8RowsOfBf16Pool(inp.kv_pool))
     V = [int(v) for v in inp.q_visible]
     T = spec.num_queries
 
-    step_bytes_idx = indexer_bytes(spec, V)
+    step_bytes_idx = indexer_bytes(dataclasses.replace(spec, k_dtype="mxfp8") if mx_keys else spec, V)
     step_bytes_sfa = sfa_bytes(spec, V)
     per_copy = step_bytes_idx + step_bytes_sfa
     copies = args.copies or max(3, min(12, math.ceil(1.0e9 / per_copy) + 1))
@@ -221,6 +256,18 @@ def main():
         inp.kv_pool = Fp8RowsOfBf16Pool(bf16_pool)
     else:
         base = to_device(inp, "cuda")
+    if mx_keys:
+        # the product's cache writer quantizes the fp32 keys on the GPU; the CPU baseline gets
+        # the oracle's quantization of the same keys
+        n, D = base.k_pool.shape
+        kp = torch.zeros((n, D), dtype=torch.uint8, device="cuda")
+        ks = torch.zeros((n, D // 32), dtype=torch.uint8, device="cuda")
+        dsa.store_index_keys(base.k_pool, torch.arange(n, dtype=torch.int64, device="cuda"), kp, ks)
+        torch.cuda.synchronize()
+        base.k_pool, base.k_scale = kp, ks
+        spec = dataclasses.replace(spec, k_dtype="mxfp8", name=spec.name + "_mxkeys")
+        mxq = MxKeysOfF32Pool(inp.k_pool)
+        inp = dataclasses.replace(inp, spec=spec, k_pool=mxq.part(0), k_scale=mxq.part(1))
     devs = [base]
     for _ in range(copies - 1):
         c = copy.copy(base)

@@ -57,7 +57,8 @@ typedef enum {
 typedef enum {
   DSA_F32 = 0,             /* IEEE binary32                                                 */
   DSA_BF16 = 1,            /* bfloat16 bits in uint16                                       */
-  DSA_FP8_E4M3 = 2         /* OCP fp8 e4m3 "fn" (no infinities, max 448), one byte          */
+  DSA_FP8_E4M3 = 2,        /* OCP fp8 e4m3 "fn" (no infinities, max 448), one byte          */
+  DSA_MXFP8_E4M3 = 3       /* OCP MXFP8: e4m3 codes, one E8M0 scale byte per 32 elements    */
 } dsa_dtype;
 
 /* Paged-cache layout, shared by every pool of a call (index keys, their scales, latent KV).
@@ -112,7 +113,14 @@ typedef struct {
  *     x[h]   = sum_d q[t, h, d] * key(s)[d]          h < n_heads, d < head_dim
  *     S[s]   = sum_h head_w[t, h] * max(x[h], 0)
  * with key(s) = k_pool row of s, times k_scale[row] when k_dtype is FP8_E4M3.  One key
- * vector per token serves every indexer head.  Scores are fp32.  The call keeps the
+ * vector per token serves every indexer head.  With k_dtype MXFP8_E4M3 (the pages' group-32
+ * MXFP8 quantization of index Q and K: "Day0 Adaptation and Performance Optimization for
+ * Novel Long-Sequence Reasoning Models", section 4; "Optimizing and Deploying Ultra-Long
+ * Sequence Inference Architectures", section II) key(s)[d] = code * 2^(e - 127) with e the
+ * row's scale byte of group d / 32, and the query is quantized the same way inside the call,
+ * per head and group of 32 dims (E8M0 byte = floor(log2 max|q|) - 8 + 127 clamped to
+ * [0, 254], 0 for an all-zero group; code = e4m3(q * 2^(127 - byte)), nearest even,
+ * saturated), before the dot products.  Scores are fp32.  The call keeps the
  * K_eff = min(top_k, V) largest scores, the lower position first among equal scores (-0 and
  * +0 compare equal), and writes their positions (logical positions within the sequence, not
  * pool rows) to out_idx[t, 0 .. K_eff) in ascending position order, then -1 up to top_k.
@@ -121,12 +129,15 @@ typedef struct {
  * Accepted inputs
  *   q:      [T, n_heads, head_dim], q_dtype F32 or BF16
  *   head_w: [T, n_heads] fp32 (any global scale folded in by the caller)
- *   k_pool: [pool_rows, head_dim], k_dtype F32, BF16 or FP8_E4M3
- *   k_scale:[pool_rows] fp32, required for FP8_E4M3, ignored otherwise
- *   1 <= n_heads * head_dim <= 8192, head_dim % 8 == 0, 1 <= top_k <= DSA_MAX_TOPK.
- * The fast path (MFMA scoring) runs for q BF16, keys BF16 or FP8_E4M3, n_heads 64, head_dim
- * 128 and a contiguous layout or block_size >= 32.  Every other accepted combination runs a
- * reference path that scores in fp64.
+ *   k_pool: [pool_rows, head_dim], k_dtype F32, BF16, FP8_E4M3 or MXFP8_E4M3 (codes)
+ *   k_scale:[pool_rows] fp32 for FP8_E4M3; for MXFP8_E4M3 the E8M0 bytes
+ *           [pool_rows, head_dim / 32] (passed through this pointer); ignored otherwise
+ *   1 <= n_heads * head_dim <= 8192, head_dim % 8 == 0 (% 32 for MXFP8_E4M3),
+ *   1 <= top_k <= DSA_MAX_TOPK.
+ * The fast path (MFMA scoring) runs for q BF16, keys BF16, FP8_E4M3 or MXFP8_E4M3, n_heads
+ * 64, head_dim 128 and a contiguous layout or block_size >= 32; fp8 codes are widened to bf16
+ * exactly (with their scale where it is a power of two) and summed in fp32.  Every other
+ * accepted combination runs a reference path that scores in fp64.
  *
  * workspace: dsa_indexer_topk_workspace_size(...) bytes.  It MUST be zero-filled before its
  * first use; every call leaves it zero-filled again where that matters, so one buffer can be
@@ -182,6 +193,9 @@ dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool,
  *   section 3) with one fp32 scale per token: scale = max_d |k| / 448 (1 if the token is
  *   all zero), code = fp8(k / scale) rounded to nearest even, saturating at +-448; the scale
  *   goes to k_scale[slot[i]].
+ *   k_dtype MXFP8_E4M3 (head_dim % 32 == 0): per group of 32 dims the E8M0 byte and codes
+ *   defined under dsa_indexer_topk; the bytes go to ((uint8_t*)k_scale)[slot[i] * head_dim / 32
+ *   + group].
  * dsa_store_kv: kv_new [n_tokens, d_qk] (src_dtype F32 or BF16) -> kv_pool rows slot[i] in
  *   pool_dtype (F32 or BF16; F32 -> BF16 rounds to nearest even), or FP8_E4M3 for the
  *   tile-quantized rows of DSA_KV_FP8_ROW_BYTES bytes (d_qk = 576): per tile the scale

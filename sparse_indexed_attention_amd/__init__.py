@@ -18,7 +18,7 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa.so")
 
-DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_MXFP8_E4M3 = 0, 1, 2, 3
 DSA_MAX_TOPK = 2048
 DSA_MAX_CONTEXT = 1 << 22
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_DTYPE",
@@ -100,6 +100,15 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
 
 
+def _key_dtype(k_pool, k_scale) -> int:
+    """Index-key storage: MXFP8 when the scales are bytes (E8M0, one per 32 dims), else the
+    pool's own dtype (fp8 codes with fp32 per-token scales, bf16 or fp32)."""
+    torch = _torch()
+    if k_scale is not None and k_scale.dtype == torch.uint8:
+        return DSA_MXFP8_E4M3
+    return _dtype_code(k_pool)
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -143,7 +152,9 @@ def indexer_topk(q, head_w, k_pool, k_scale, layout: DsaLayout, q_seq, q_visible
     """Fused lightning indexer + Top-K.  Shapes as in include/dsa.h:
     q [T, H_I, D_I] (float32 | bfloat16/int16 bits), head_w [T, H_I] float32,
     k_pool [rows, D_I] (float32 | bfloat16 bits | fp8 codes as uint8/float8_e4m3fn),
-    k_scale [rows] float32 for fp8 keys.  Returns (idx [T, K] int32, score or None)."""
+    k_scale [rows] float32 for fp8 keys, or uint8 [rows, D/32] E8M0 bytes for MXFP8 keys (the
+    query is then quantized to MXFP8 inside the call).  Returns (idx [T, K] int32, score or
+    None)."""
     torch = _torch()
     lib = load()
     T, H, D = q.shape
@@ -155,7 +166,7 @@ def indexer_topk(q, head_w, k_pool, k_scale, layout: DsaLayout, q_seq, q_visible
     if workspace is None:
         workspace = zeroed_workspace(indexer_workspace_bytes(T, max_visible, top_k), q.device)
     st = lib.dsa_indexer_topk(_ptr(q), _dtype_code(q), _ptr(head_w), _ptr(k_pool),
-                              _dtype_code(k_pool), _ptr(k_scale), H, D, ctypes.byref(layout),
+                              _key_dtype(k_pool, k_scale), _ptr(k_scale), H, D, ctypes.byref(layout),
                               ctypes.byref(queries), top_k, _ptr(out_idx), _ptr(out_score),
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream))
@@ -192,9 +203,10 @@ def sparse_attn(q, kv_pool, idx, layout: DsaLayout, q_seq, softmax_scale: float,
 
 
 def store_index_keys(k_new, slot, k_pool, k_scale=None, stream=None):
-    """k_new [n, D] float32 -> k_pool rows slot[i] (int64) in k_pool's dtype."""
+    """k_new [n, D] float32 -> k_pool rows slot[i] (int64) in k_pool's dtype; with uint8
+    codes and uint8 k_scale [rows, D/32], MXFP8 (E8M0 byte per 32 dims)."""
     st = load().dsa_store_index_keys(_ptr(k_new), k_new.shape[0], k_new.shape[1], _ptr(slot),
-                                     _ptr(k_pool), _dtype_code(k_pool), _ptr(k_scale),
+                                     _ptr(k_pool), _key_dtype(k_pool, k_scale), _ptr(k_scale),
                                      _stream(stream))
     if st != 0:
         raise DsaError("dsa_store_index_keys", st)

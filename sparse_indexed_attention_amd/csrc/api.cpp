@@ -57,7 +57,8 @@ Layout make_layout(const dsa_layout* L) {
 
 bool indexer_fast(dsa_dtype q_dtype, dsa_dtype k_dtype, int32_t H, int32_t D,
                   const dsa_layout* L) {
-  return q_dtype == DSA_BF16 && (k_dtype == DSA_BF16 || k_dtype == DSA_FP8_E4M3) && H == 64 &&
+  return q_dtype == DSA_BF16 &&
+         (k_dtype == DSA_BF16 || k_dtype == DSA_FP8_E4M3 || k_dtype == DSA_MXFP8_E4M3) && H == 64 &&
          D == 128 && (!L->block_table || L->block_size >= kMinFastBlock);
 }
 
@@ -81,9 +82,12 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
                             float* out_score, void* workspace, size_t workspace_bytes,
                             void* stream) {
   if (!q || !head_w || !k_pool || !out_idx) return DSA_ERR_NULL;
-  if (k_dtype == DSA_FP8_E4M3 && !k_scale) return DSA_ERR_NULL;
+  if ((k_dtype == DSA_FP8_E4M3 || k_dtype == DSA_MXFP8_E4M3) && !k_scale) return DSA_ERR_NULL;
   if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
-  if (k_dtype != DSA_F32 && k_dtype != DSA_BF16 && k_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  if (k_dtype != DSA_F32 && k_dtype != DSA_BF16 && k_dtype != DSA_FP8_E4M3 &&
+      k_dtype != DSA_MXFP8_E4M3)
+    return DSA_ERR_DTYPE;
+  if (k_dtype == DSA_MXFP8_E4M3 && head_dim % 32 != 0) return DSA_ERR_SHAPE;
   if (n_heads < 1 || head_dim < 8 || head_dim % 8 != 0) return DSA_ERR_SHAPE;
   if ((int64_t)n_heads * head_dim > kGenericMaxHD || n_heads > kGenericMaxHeads)
     return DSA_ERR_UNSUPPORTED;
@@ -102,7 +106,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
   p.q = q;
   p.w = head_w;
   p.k_pool = k_pool;
-  p.k_scale = k_dtype == DSA_FP8_E4M3 ? k_scale : nullptr;
+  p.k_scale = (k_dtype == DSA_FP8_E4M3 || k_dtype == DSA_MXFP8_E4M3) ? k_scale : nullptr;
   p.L = make_layout(layout);
   p.q_seq = queries->q_seq;
   p.q_vis = queries->q_visible;
@@ -196,8 +200,11 @@ dsa_status dsa_store_index_keys(const float* k_new, int32_t n_tokens, int32_t he
                                 const int64_t* slot, void* k_pool, dsa_dtype k_dtype,
                                 float* k_scale, void* stream) {
   if (!k_new || !slot || !k_pool) return DSA_ERR_NULL;
-  if (k_dtype == DSA_FP8_E4M3 && !k_scale) return DSA_ERR_NULL;
-  if (k_dtype != DSA_F32 && k_dtype != DSA_BF16 && k_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  if ((k_dtype == DSA_FP8_E4M3 || k_dtype == DSA_MXFP8_E4M3) && !k_scale) return DSA_ERR_NULL;
+  if (k_dtype != DSA_F32 && k_dtype != DSA_BF16 && k_dtype != DSA_FP8_E4M3 &&
+      k_dtype != DSA_MXFP8_E4M3)
+    return DSA_ERR_DTYPE;
+  if (k_dtype == DSA_MXFP8_E4M3 && head_dim % 32 != 0) return DSA_ERR_SHAPE;
   if (n_tokens < 1 || n_tokens > (1 << 30) || head_dim < 1) return DSA_ERR_SHAPE;
   if (misaligned(k_new) || misaligned(slot) || misaligned(k_pool) || misaligned(k_scale))
     return DSA_ERR_ALIGN;

@@ -19,7 +19,7 @@ constexpr int kMinSplit = 512;         // shortest context split
 constexpr int kGenericMaxHD = 8192;    // n_heads * head_dim on the reference path
 constexpr int kGenericMaxHeads = 256;
 
-enum { kDtF32 = 0, kDtBF16 = 1, kDtFP8 = 2 };
+enum { kDtF32 = 0, kDtBF16 = 1, kDtFP8 = 2, kDtMX = 3 };
 
 struct IndexerPlan {
   int32_t grid;         // workgroups of the launch

@@ -54,6 +54,7 @@ constexpr int kBins = 2048;               // radix bins per pass
 template <int MODE> struct Ring { static constexpr int D = 1, SLOT = 0; };
 template <> struct Ring<1> { static constexpr int D = 2, SLOT = 8192; };          // bf16 keys
 template <> struct Ring<2> { static constexpr int D = 4, SLOT = 4096 + 256; };    // fp8 keys + scales
+template <> struct Ring<3> : Ring<2> {};                                           // MXFP8 keys + scale bytes
 
 // Bytes of the kernel's shared region: the scorer's ring while scoring, then the selection
 // arrays.
@@ -210,6 +211,11 @@ __device__ __forceinline__ float relu(float x) {
 // 64), whose block id is one wave-uniform scalar load.  Group indices past the wave's run
 // are clamped onto its last group (harmless re-reads) so every step issues the same loads
 // and the hardware waits stay exact.
+// MXFP8 keys (MODE 3) move like fp8 keys (128 code bytes and a 4-byte word of E8M0 scales per
+// token); the codes are widened with their group's power-of-two scale, exactly, and the
+// query is quantized to MXFP8 by the workgroup and dequantized into LDS (exact in bf16 for
+// scale bytes >= 3, i.e. groups whose largest magnitude is at least 2^-116), so the products
+// are the bf16 path's and every sum is the same fp32 accumulation.
 template <bool FP8, bool PAGED, int MODE>
 __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int seq, int start,
                                            int len, const Lds& L, uint32_t& kr_lo, uint32_t& kr_hi) {
@@ -231,17 +237,53 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
   const int ngroups = (len + 31) >> 5;
   const int per = (ngroups + NWAVE - 1) / NWAVE;
   const int g0 = min(ngroups, wave * per), g1 = min(ngroups, g0 + per);
-  if (g0 >= g1) return;
+  constexpr bool MX = MODE == 3;
+  const uint16_t* qb = (const uint16_t*)p.q + (size_t)t * (64 * 128);
+  if constexpr (MX) {
+    // MXFP8: the workgroup quantizes the query, thread i the group of 32 dims 32 (i % 4) ..
+    // of head i / 4, and leaves the dequantized values (exact in bf16: an e4m3 value times a
+    // power of two) in the ring's LDS, where every wave reads its operands.  All waves pass
+    // the same barriers: before the writes (the region may still be read by the previous
+    // phase) and after every wave has its copy (before any ring load or early return).
+    static_assert(NT == 64 * 4, "one thread per group of the query");
+    __syncthreads();
+    uint16_t* qs = (uint16_t*)L.region + (threadIdx.x >> 2) * 128 + 32 * (threadIdx.x & 3);
+    const uint16_t* src = qb + (threadIdx.x >> 2) * 128 + 32 * (threadIdx.x & 3);
+    bf16x8 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *(const bf16x8*)(src + 8 * u);
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[u][e]));
+    const uint32_t sbyte = mx_scale_byte(amax);
+    const float inv = mx_inv_scale(sbyte), sc = mx_scale_f32(sbyte);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      bf16x8 r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        r[e] = (__bf16)(fp8_e4m3_to_f32(f32_to_fp8_e4m3_nb((float)v[u][e] * inv)) * sc);
+      *(bf16x8*)(qs + 8 * u) = r;
+    }
+    __syncthreads();
+  }
+  if (g0 >= g1) {
+    if constexpr (MX) __syncthreads();
+    return;
+  }
   static_assert(kSplitMax / 32 / NWAVE <= 64, "one lane per group of a wave's run");
   // One round trip brings the query (registers), this wave's copy of the head weights (LDS)
   // and the pages of its groups (lane l: the block id of group g0 + l).
-  const uint16_t* qb = (const uint16_t*)p.q + (size_t)t * (64 * 128);
+  const uint16_t* qsrc = MX ? (const uint16_t*)L.region : qb;
   bf16x8 a0[8], a1[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    a0[s] = *(const bf16x8*)(qb + col * 128 + half * 64 + 8 * s);
-    a1[s] = *(const bf16x8*)(qb + (32 + col) * 128 + half * 64 + 8 * s);
+    a0[s] = *(const bf16x8*)(qsrc + col * 128 + half * 64 + 8 * s);
+    a1[s] = *(const bf16x8*)(qsrc + (32 + col) * 128 + half * 64 + 8 * s);
   }
+  if constexpr (MX) __syncthreads();
   const float* lw = L.w + wave * 64;
   load_to_lds<4>(p.w + (size_t)t * 64, 4u * lane, lds_addr(lw));
   int gblk = 0;
@@ -283,19 +325,24 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
   // Group g's products: both 32-head chains of MFMAs over the key rows in slot sb.
   auto products = [&](const uint8_t* sb, f32x16& acc0, f32x16& acc1) {
     const uint8_t* rb = sb + col * ROWB;      // this lane's row
+    // MXFP8: this lane's two groups 2 half, 2 half + 1 (k steps 0..3, 4..7)
+    const uint32_t sw = MX ? *(const uint32_t*)(sb + GB + 4 * col) >> (16 * half) : 0u;
+    const float xs0 = MX ? mx_scale_f32(sw & 255u) : 1.0f;
+    const float xs1 = MX ? mx_scale_f32((sw >> 8) & 255u) : 1.0f;
     acc0 = f32x16{};
     acc1 = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       bf16x8 kb;
       if constexpr (FP8) {
+        const float xs = s < 4 ? xs0 : xs1;
         const u32x4 v = *(const u32x4*)(rb + 16 * ((4 * half + (s >> 1)) ^ (col & (CPR - 1))));
         const uint32_t lo = (s & 1) ? v.z : v.x;
         const uint32_t hi = (s & 1) ? v.w : v.y;
-        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, xs, false);
+        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, xs, true);
+        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, xs, false);
+        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, xs, true);
         kb = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       } else {
         kb = *(const bf16x8*)(rb + 16 * ((8 * half + s) ^ (col & (CPR - 1))));
@@ -321,7 +368,7 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
     }
     const float psum = (part[0] + part[1]) + (part[2] + part[3]);
     float tot = psum + __shfl_xor(psum, 32, 64);
-    if constexpr (FP8) tot *= scale;
+    if constexpr (FP8 && !MX) tot *= scale;
     const int off = g * 32 + col;
     if (half == 0 && off < len) {
       const uint32_t key = float_to_key(tot);
@@ -346,7 +393,7 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
     products(sb, acc0, acc1);
     // both chains are issued before any accumulator is read, so they interleave
     __builtin_amdgcn_sched_barrier(0);
-    finish(g, acc0, acc1, FP8 ? *(const float*)(sb + GB + 4 * col) : 1.f);
+    finish(g, acc0, acc1, FP8 && !MX ? *(const float*)(sb + GB + 4 * col) : 1.f);
   }
   wait_vmcnt<0>();                            // no load may still target the ring afterwards
 }
@@ -355,6 +402,11 @@ __device__ __forceinline__ float load_elem(const void* base, int dt, int64_t i) 
   if (dt == kDtF32) return ((const float*)base)[i];
   if (dt == kDtBF16) return bf16_bits_to_f32(((const uint16_t*)base)[i]);
   return fp8_e4m3_to_f32(((const uint8_t*)base)[i]);
+}
+// Value of an MXFP8 key element: code times 2^(byte - 127) of its group of 32 (fp64, exact).
+__device__ __forceinline__ double mx_key(const IndexerParams& p, int64_t row, int d) {
+  const int e = (int)((const uint8_t*)p.k_scale)[row * (p.D / 32) + (d >> 5)] - 127;
+  return ldexp((double)fp8_e4m3_to_f32(((const uint8_t*)p.k_pool)[row * p.D + d]), e);
 }
 
 // Reference scorer: one thread per position, fp64 accumulation (products of the stored
@@ -366,11 +418,13 @@ __device__ __forceinline__ void score_generic(const IndexerParams& p, int seq, i
   for (int i = threadIdx.x; i < len; i += NT) {
     const int64_t row = pool_row(p.L, seq, start + i);
     const double ks = (p.k_dtype == kDtFP8) ? (double)p.k_scale[row] : 1.0;
+    const bool mx = p.k_dtype == kDtMX;
     double S = 0.0;
     for (int h = 0; h < H; ++h) {
       double x = 0.0;
       for (int d = 0; d < D; ++d)
-        x = fma((double)gs.q[h * D + d], (double)load_elem(p.k_pool, p.k_dtype, row * D + d) * ks, x);
+        x = fma((double)gs.q[h * D + d],
+                mx ? mx_key(p, row, d) : (double)load_elem(p.k_pool, p.k_dtype, row * D + d) * ks, x);
       S = fma((double)gs.w[h], fmax(x, 0.0), S);
     }
     const uint32_t key = float_to_key((float)S);
@@ -395,8 +449,8 @@ __device__ __forceinline__ void score_split(const IndexerParams& p, int t, int s
     seq = __builtin_amdgcn_readfirstlane(seq);
     start = __builtin_amdgcn_readfirstlane(start);
     len = __builtin_amdgcn_readfirstlane(len);
-    if (p.L.bt) score_mfma<MODE == 2, true, MODE>(p, t, seq, start, len, L, kmin, kmax);
-    else score_mfma<MODE == 2, false, MODE>(p, t, seq, start, len, L, kmin, kmax);
+    if (p.L.bt) score_mfma<MODE >= 2, true, MODE>(p, t, seq, start, len, L, kmin, kmax);
+    else score_mfma<MODE >= 2, false, MODE>(p, t, seq, start, len, L, kmin, kmax);
   }
   kmin = wave_min(kmin);
   kmax = wave_max(kmax);
@@ -1379,6 +1433,19 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
     for (int i = threadIdx.x; i < HD; i += NT)
       gs.q[i] = load_elem(p.q, p.q_dtype, (int64_t)t * HD + i);
     for (int i = threadIdx.x; i < p.H; i += NT) gs.w[i] = p.w[(size_t)t * p.H + i];
+    if (p.k_dtype == kDtMX) {
+      // MXFP8 keys: the query is quantized too, per head and group of 32 dims (one group per
+      // thread), and replaced by its dequantized values (exact in fp32 down to 2^-149)
+      __syncthreads();
+      for (int g = threadIdx.x; g < HD / 32; g += NT) {
+        float amax = 0.f;
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(gs.q[32 * g + i]));
+        const uint32_t sb = mx_scale_byte(amax);
+        for (int i = 0; i < 32; ++i)
+          gs.q[32 * g + i] = (float)ldexp((double)fp8_e4m3_to_f32(f32_to_fp8_e4m3(gs.q[32 * g + i] * mx_inv_scale(sb))),
+                                          (int)sb - 127);
+      }
+    }
     gsp = &gs;
   }
   __syncthreads();
@@ -1532,6 +1599,7 @@ hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t st
   const dim3 grid(p.grid), block(NT);
   if (!fast_path) hipLaunchKernelGGL(indexer_topk_kernel<0>, grid, block, 0, stream, p);
   else if (p.k_dtype == kDtFP8) hipLaunchKernelGGL(indexer_topk_kernel<2>, grid, block, 0, stream, p);
+  else if (p.k_dtype == kDtMX) hipLaunchKernelGGL(indexer_topk_kernel<3>, grid, block, 0, stream, p);
   else hipLaunchKernelGGL(indexer_topk_kernel<1>, grid, block, 0, stream, p);
   return hipGetLastError();
 }

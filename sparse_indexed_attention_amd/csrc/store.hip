@@ -6,6 +6,12 @@
 // max|k| / 448 (1 for an all-zero token), code = e4m3(k / scale) rounded to nearest even and
 // saturated at +-448.  One wave per token.
 //
+// Index keys may also be stored in MXFP8 ("Day0 Adaptation and Performance Optimization for
+// Novel Long-Sequence Reasoning Models", section 4; "Optimizing and Deploying Ultra-Long
+// Sequence Inference Architectures", section II: groups of 32 elements share one scale), read
+// as the OCP microscaling format: per group of 32 dims an E8M0 byte (see mx_scale_byte) and
+// e4m3 codes of k * 2^(127 - byte), nearest even, saturated.
+//
 // The SFA latent cache may be stored in fp8-e4m3 per token and per tile of 128 columns ("Day0
 // Adaptation and Performance Optimization for Novel Long-Sequence Reasoning Models", section
 // 4; "Large Model Inference Acceleration: Day-0 Adaptation...", section 2.2): columns 0..511
@@ -17,26 +23,6 @@
 
 namespace dsa {
 namespace {
-
-// fp32 -> e4m3fn code, nearest value with ties to the even code, |x| >= 448 -> 448, NaN ->
-// 0x7F.  Within one binade the e4m3 values are evenly spaced and the code's low bit is the
-// mantissa's, so rounding the scaled mantissa to the nearest even integer is exactly "ties to
-// the even code"; a carry into the next binade lands on mantissa 0, also even.
-__device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float x) {
-  if (x != x) return 0x7fu;
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (a >= 448.f) return sign | 0x7eu;
-  if (a < 0.015625f) {                                   // below 2^-6: subnormal grid m*2^-9
-    const uint32_t n = (uint32_t)rintf(a * 512.f);       // exact scaling, then RNE; n <= 8
-    return sign | n;                                     // n == 8 is code 0x08 = 2^-6
-  }
-  int E = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;   // -6 .. 8
-  const float m = a * __uint_as_float((uint32_t)(127 - E) << 23);   // a / 2^E, exact, in [1,2)
-  uint32_t n = (uint32_t)rintf((m - 1.f) * 8.f);
-  if (n == 8u) { n = 0u; ++E; }
-  return sign | ((uint32_t)(E + 7) << 3) | n;
-}
 
 __global__ __launch_bounds__(64) void store_index_keys_kernel(const float* k_new, int D,
                                                               const int64_t* slot, void* pool,
@@ -51,6 +37,23 @@ __global__ __launch_bounds__(64) void store_index_keys_kernel(const float* k_new
   if (dt == kDtBF16) {
     for (int d = lane; d < D; d += 64)
       ((uint16_t*)pool)[row * D + d] = (uint16_t)f32_to_bf16_bits(src[d]);
+    return;
+  }
+  if (dt == kDtMX) {
+    // column d = d0 + lane: lanes 0..31 and 32..63 each hold one group of 32 (D % 32 == 0)
+    uint8_t* sbytes = (uint8_t*)k_scale + row * (D / 32);
+    for (int d0 = 0; d0 < D; d0 += 64) {
+      const int d = d0 + lane;
+      const float x = d < D ? src[d] : 0.f;
+      float amax = fabsf(x);
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      const uint32_t sb = mx_scale_byte(amax);
+      if (d < D) {
+        ((uint8_t*)pool)[row * D + d] = (uint8_t)f32_to_fp8_e4m3(x * mx_inv_scale(sb));
+        if ((lane & 31) == 0) sbytes[d >> 5] = (uint8_t)sb;
+      }
+    }
     return;
   }
   float amax = 0.f;

@@ -69,6 +69,8 @@ def test_indexer_validation(lib):
     assert _idx_call(lib, m, out=None) == 1
     assert _idx_call(lib, m, qd=2) == 3                       # fp8 queries not accepted
     assert _idx_call(lib, m, kd=9) == 3
+    assert _idx_call(lib, m, kd=3, ks=None) == 1              # MXFP8 keys need their scale bytes
+    assert _idx_call(lib, m, kd=3, D=136, H=32) == 2          # MXFP8: head_dim % 32
     assert _idx_call(lib, m, D=100) == 2                      # head_dim % 8
     assert _idx_call(lib, m, H=128, D=128) == 4               # above the reference limit
     assert _idx_call(lib, m, K=0) == 2
@@ -139,6 +141,8 @@ def test_store_validation(lib):
     assert lib.dsa_store_index_keys(A[0], 4, 128, A[1], A[2], 2, None, None) == 1
     assert lib.dsa_store_index_keys(A[0], 0, 128, A[1], A[2], 2, A[3], None) == 2
     assert lib.dsa_store_index_keys(A[0], 4, 128, A[1], A[2], 7, A[3], None) == 3
+    assert lib.dsa_store_index_keys(A[0], 4, 128, A[1], A[2], 3, None, None) == 1
+    assert lib.dsa_store_index_keys(A[0], 4, 120, A[1], A[2], 3, A[3], None) == 2
     assert lib.dsa_store_kv(A[0], 2, 4, 576, A[1], A[2], 1, None) == 3
     assert lib.dsa_store_kv(A[0], 1, 4, 576, A[1] + 8, A[2], 1, None) == 6
     assert lib.dsa_store_kv(A[0], 1, 4, 512, A[1], A[2], 2, None) == 4   # fp8 rows: d_qk 576 only
