@@ -236,6 +236,7 @@ def main():
         spec = dataclasses.replace(spec, kv_dtype="fp8", name=spec.name + "_fp8kv")
         inp = dataclasses.replace(inp, spec=spec, kv_pool=Fp8RowsOfBf16Pool(inp.kv_pool))
     V = [int(v) for v in inp.q_visible]
+    total_visible = sum(V)       # known to the host, as in a serving scheduler
     T = spec.num_queries
 
     step_bytes_idx = indexer_bytes(dataclasses.replace(spec, k_dtype="mxfp8") if mx_keys else spec, V)
@@ -300,7 +301,8 @@ def main():
         if which == "idx":
             ev[0].record()
         dsa.indexer_topk(d.q_idx, d.w, d.k_pool, d.k_scale, lay, d.q_seq, d.q_visible,
-                         d.max_visible, K, out_idx=idx, want_score=False, workspace=ws_i)
+                         d.max_visible, K, out_idx=idx, want_score=False, workspace=ws_i,
+                         total_visible=total_visible)
         if which == "idx":
             ev[1].record()
         if which == "sfa":

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 typedef enum {
   DSA_OK = 0,
@@ -81,12 +81,17 @@ typedef struct {
  * positions [0, q_visible[t]) of sequence q_seq[t]: causal, its own position included.  A
  * decode query sees its whole sequence; query i of a chunk of new tokens appended to a
  * prefix of P tokens sees P + i + 1.  max_visible (host) must be >= every q_visible[t]; it
- * sizes the launch so that the host never reads device memory. */
+ * sizes the launch so that the host never reads device memory.  total_visible (host,
+ * optional) is the sum of q_visible over the queries when the caller knows it, else 0; the
+ * indexer then sizes its context splits to the real total instead of T * max_visible.  It
+ * only steers the launch: a wrong value costs time, never correctness (it is clamped to
+ * [max_visible, T * max_visible]). */
 typedef struct {
   int32_t num_queries;          /* T >= 1                                                     */
   const int32_t* q_seq;         /* [T], 0 <= q_seq[t] < num_seqs                              */
   const int32_t* q_visible;     /* [T], 1 <= q_visible[t] <= max_visible                      */
   int32_t max_visible;          /* (host) 1 <= max_visible <= DSA_MAX_CONTEXT                 */
+  int64_t total_visible;        /* (host) sum of q_visible, or 0 if unknown                   */
 } dsa_queries;
 
 #define DSA_MAX_CONTEXT (1 << 22)  /* longest visible prefix a query may have (4M tokens)    */

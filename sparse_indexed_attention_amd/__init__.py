@@ -33,7 +33,8 @@ class DsaLayout(ctypes.Structure):
 
 class DsaQueries(ctypes.Structure):
     _fields_ = [("num_queries", ctypes.c_int32), ("q_seq", ctypes.c_void_p),
-                ("q_visible", ctypes.c_void_p), ("max_visible", ctypes.c_int32)]
+                ("q_visible", ctypes.c_void_p), ("max_visible", ctypes.c_int32),
+                ("total_visible", ctypes.c_int64)]
 
 
 class DsaError(RuntimeError):
@@ -128,9 +129,10 @@ def make_layout(block_table=None, block_size: int = 0, seq_stride: int = 0, num_
     return DsaLayout(0, 0, None, seq_stride, num_seqs, pool_rows)
 
 
-def make_queries(q_seq, q_visible=None, max_visible: int = 0) -> DsaQueries:
+def make_queries(q_seq, q_visible=None, max_visible: int = 0, total_visible: int = 0) -> DsaQueries:
     return DsaQueries(q_seq.shape[0], q_seq.data_ptr(),
-                      None if q_visible is None else q_visible.data_ptr(), max_visible)
+                      None if q_visible is None else q_visible.data_ptr(), max_visible,
+                      total_visible)
 
 
 def indexer_workspace_bytes(num_queries: int, max_visible: int, top_k: int) -> int:
@@ -148,13 +150,14 @@ def zeroed_workspace(nbytes: int, device):
 
 def indexer_topk(q, head_w, k_pool, k_scale, layout: DsaLayout, q_seq, q_visible,
                  max_visible: int, top_k: int, *, out_idx=None, out_score=None,
-                 want_score: bool = True, workspace=None, stream=None):
+                 want_score: bool = True, workspace=None, stream=None, total_visible: int = 0):
     """Fused lightning indexer + Top-K.  Shapes as in include/dsa.h:
     q [T, H_I, D_I] (float32 | bfloat16/int16 bits), head_w [T, H_I] float32,
     k_pool [rows, D_I] (float32 | bfloat16 bits | fp8 codes as uint8/float8_e4m3fn),
     k_scale [rows] float32 for fp8 keys, or uint8 [rows, D/32] E8M0 bytes for MXFP8 keys (the
     query is then quantized to MXFP8 inside the call).  Returns (idx [T, K] int32, score or
-    None)."""
+    None).  total_visible: the sum of q_visible if known on the host (sizes the launch), else
+    0."""
     torch = _torch()
     lib = load()
     T, H, D = q.shape
@@ -162,7 +165,7 @@ def indexer_topk(q, head_w, k_pool, k_scale, layout: DsaLayout, q_seq, q_visible
         out_idx = torch.empty((T, top_k), dtype=torch.int32, device=q.device)
     if out_score is None and want_score:
         out_score = torch.empty((T, top_k), dtype=torch.float32, device=q.device)
-    queries = make_queries(q_seq, q_visible, max_visible)
+    queries = make_queries(q_seq, q_visible, max_visible, total_visible)
     if workspace is None:
         workspace = zeroed_workspace(indexer_workspace_bytes(T, max_visible, top_k), q.device)
     st = lib.dsa_indexer_topk(_ptr(q), _dtype_code(q), _ptr(head_w), _ptr(k_pool),

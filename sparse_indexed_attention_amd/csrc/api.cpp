@@ -72,7 +72,7 @@ extern "C" {
 
 size_t dsa_indexer_topk_workspace_size(int32_t num_queries, int32_t max_visible, int32_t top_k) {
   if (num_queries < 1 || max_visible < 1 || max_visible > DSA_MAX_CONTEXT || top_k < 1) return 0;
-  return plan_indexer(num_queries, max_visible, top_k).bytes;
+  return indexer_workspace_bytes(num_queries, max_visible, top_k);
 }
 
 dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_w,
@@ -99,7 +99,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
       misaligned(out_idx) || misaligned(out_score) || misaligned(workspace))
     return DSA_ERR_ALIGN;
   const int32_t T = queries->num_queries;
-  const IndexerPlan pl = plan_indexer(T, queries->max_visible, top_k);
+  const IndexerPlan pl = plan_indexer(T, queries->max_visible, top_k, queries->total_visible);
   if (!workspace || workspace_bytes < pl.bytes) return DSA_ERR_WORKSPACE;
 
   IndexerParams p{};
@@ -122,6 +122,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
   p.nsplit_max = pl.nsplit_max;
   p.cap = pl.cap;
   p.rs = pl.rs;
+  p.compact = pl.compact;
   p.out_idx = out_idx;
   p.out_score = out_score;
   uint8_t* ws = static_cast<uint8_t*>(workspace);

@@ -16,6 +16,7 @@ constexpr int kNSplitMax = 2048;       // context splits per query
 constexpr int kMaxTopK = 2048;         // largest top_k
 constexpr int kMinFastBlock = 32;      // smallest page size of the MFMA path (one page per 32-position group)
 constexpr int kMinSplit = 512;         // shortest context split
+constexpr int kCompactMaxT = 64;       // most queries of a compact indexer launch
 constexpr int kGenericMaxHD = 8192;    // n_heads * head_dim on the reference path
 constexpr int kGenericMaxHeads = 256;
 
@@ -27,6 +28,7 @@ struct IndexerPlan {
   int32_t nsplit_max;   // splits of the longest visible prefix (header rows per query)
   int32_t cap;          // candidates per split at most = min(split, top_k)
   int32_t rs;           // candidate slots per split: cap rounded up to 4
+  int32_t compact;      // 1: the grid numbers only live splits (IndexerParams::compact)
   size_t off_counters, off_hdr, off_ckey, off_cpos, bytes;
 };
 
@@ -41,6 +43,7 @@ struct IndexerParams {
   int32_t T, H, D, K, max_visible;
   int32_t q_dtype, k_dtype;
   int32_t grid, split, nsplit_max, cap, rs;
+  int32_t compact;      // items numbered over the live splits only (see the kernel)
   int32_t* out_idx;
   float* out_score;
   uint32_t* counters;   // [T]                  split arrivals per query (self-resetting)
@@ -49,7 +52,9 @@ struct IndexerParams {
   int32_t* cand_pos;    // [T][nsplit_max][rs] ... and positions
 };
 
-IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k);
+IndexerPlan plan_indexer_split(int32_t T, int32_t max_visible, int32_t top_k, int32_t split);
+IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k, int64_t total_visible);
+size_t indexer_workspace_bytes(int32_t T, int32_t max_visible, int32_t top_k);
 hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream);
 
 // ------------------------------------------------------------------ sparse attention

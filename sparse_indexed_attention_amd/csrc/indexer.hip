@@ -1379,41 +1379,11 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
 // only the merging workgroup of a query whose split thresholds failed to certify comes back
 // to it, to re-score each failing split and take its exact local Top-K.
 // ---------------------------------------------------------------------------------------
+// One work item: split j of query t (scoring, candidate emission, and the merge when it is
+// the query's last split to arrive).  Every return is uniform over the workgroup.
 template <int MODE>
-__global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
-  constexpr int RB = region_bytes<MODE>();
-  static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kNSplitMax + 4, "shared region");
-  __shared__ __attribute__((aligned(16))) uint8_t s_region[RB];
-  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSplitMax];
-  __shared__ __attribute__((aligned(16))) float s_w[NWAVE * 64];
-  __shared__ int s_res[4], s_scan[2 * NWAVE + 2], s_wcnt[2 * NWAVE], s_bcast[4];
-  __shared__ uint32_t s_range[2 * NWAVE];
-  __shared__ __attribute__((aligned(16))) int s_psum[NT];
-  __shared__ uint32_t s_small[64];
-  Lds L;
-  L.keys = s_keys;
-  L.w = s_w;
-  L.region = s_region;
-  L.hist = (int*)s_region;                         // while selecting a split's candidates
-  L.sel_key = (uint32_t*)s_region;                 // while merging (hist then moves to s_keys)
-  L.sel_pos = (int32_t*)(s_region + kSelCap * 4);
-  L.flat = (uint32_t*)(s_region + kSelBytes);
-  L.res = s_res;
-  L.scan = s_scan;
-  L.wcnt = s_wcnt;
-  L.bcast = s_bcast;
-  L.range = s_range;
-  L.psum = s_psum;
-  L.small = s_small;
-  Lds Lm = L;
-  Lm.hist = (int*)s_keys;
-
-  // Workgroup -> (query t, split j).  Dispatch follows the linear index: the splits that exist
-  // for every query (small j) come first and the empty ones of short queries last, so the live
-  // workgroups spread over all the CUs, and within a block of T workgroups the queries are
-  // rotated by j so that each query's splits spread over the XCDs.
-  const int L0 = blockIdx.x;
-  const int j = L0 / p.T, t = (L0 - j * p.T + j) % p.T;
+__device__ __forceinline__ void run_item(const IndexerParams& p, int t, int j, const Lds& L,
+                                         const Lds& Lm) {
   const int split = p.split;
   const int cap = min(split, p.K);
   const int V = min(p.q_vis[t], p.max_visible);
@@ -1568,17 +1538,78 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   }
 }
 
+template <int MODE>
+__global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
+  constexpr int RB = region_bytes<MODE>();
+  static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kNSplitMax + 4, "shared region");
+  __shared__ __attribute__((aligned(16))) uint8_t s_region[RB];
+  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSplitMax];
+  __shared__ __attribute__((aligned(16))) float s_w[NWAVE * 64];
+  __shared__ int s_res[4], s_scan[2 * NWAVE + 2], s_wcnt[2 * NWAVE], s_bcast[4];
+  __shared__ uint32_t s_range[2 * NWAVE];
+  __shared__ __attribute__((aligned(16))) int s_psum[NT];
+  __shared__ uint32_t s_small[64];
+  Lds L;
+  L.keys = s_keys;
+  L.w = s_w;
+  L.region = s_region;
+  L.hist = (int*)s_region;                         // while selecting a split's candidates
+  L.sel_key = (uint32_t*)s_region;                 // while merging (hist then moves to s_keys)
+  L.sel_pos = (int32_t*)(s_region + kSelCap * 4);
+  L.flat = (uint32_t*)(s_region + kSelBytes);
+  L.res = s_res;
+  L.scan = s_scan;
+  L.wcnt = s_wcnt;
+  L.bcast = s_bcast;
+  L.range = s_range;
+  L.psum = s_psum;
+  L.small = s_small;
+  Lds Lm = L;
+  Lm.hist = (int*)s_keys;
+
+  // Work items (query t, split j).  Compact launch: the items, query-major, are numbered from
+  // the queries' split counts, and workgroup i takes items i, i + grid, ... so that a grid
+  // sized from the host's estimate covers every item even when the estimate is short.
+  // Otherwise one item per workgroup by the linear index: the splits that exist for every
+  // query (small j) come first and the empty ones of short queries last, so the live
+  // workgroups spread over all the CUs, and within a block of T workgroups the queries are
+  // rotated by j so that each query's splits spread over the XCDs.
+  __shared__ int s_pre[kCompactMaxT + 1];
+  int n_items = gridDim.x;
+  if (p.compact) {
+    if ((int)threadIdx.x < p.T) {
+      const int V = min(p.q_vis[threadIdx.x], p.max_visible);
+      s_pre[threadIdx.x + 1] = V <= 0 ? 1 : (V + p.split - 1) / p.split;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      s_pre[0] = 0;
+      for (int u = 0; u < p.T; ++u) s_pre[u + 1] += s_pre[u];
+    }
+    __syncthreads();
+    n_items = s_pre[p.T];
+  }
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    int t, j;
+    if (p.compact) {
+      t = 0;
+      while (s_pre[t + 1] <= item) ++t;
+      j = item - s_pre[t];
+    } else {
+      j = item / p.T;
+      t = (item - j * p.T + j) % p.T;
+    }
+    run_item<MODE>(p, t, j, L, Lm);
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
-IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
+// The layout and launch for one split length (a multiple of 64 in [kMinSplit, kSplitMax]).
+IndexerPlan plan_indexer_split(int32_t T, int32_t max_visible, int32_t top_k, int32_t split) {
   IndexerPlan pl{};
-  int64_t target_wg = 512;
-  if (const char* e = getenv("DSA_INDEXER_TARGET_WG")) target_wg = atoll(e) > 0 ? atoll(e) : 512;
-  int64_t split = ((int64_t)T * max_visible + target_wg - 1) / target_wg;
-  split = (split + 63) / 64 * 64;
-  if (split < kMinSplit) split = kMinSplit;
-  if (split > kSplitMax) split = kSplitMax;
-  pl.split = (int32_t)split;
+  pl.split = split;
   pl.nsplit_max = (int32_t)((max_visible + split - 1) / split);
   pl.cap = (int32_t)(split < top_k ? split : top_k);
   pl.rs = (pl.cap + 3) / 4 * 4;
@@ -1593,6 +1624,44 @@ IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k) {
   pl.off_cpos = off;     off = al(off + slots * 4);
   pl.bytes = off;
   return pl;
+}
+
+// Split length: the live workgroups (sum over queries of ceil(V_t / split)) should fill the
+// chip's 512 resident slots (256 CUs x 2) without exceeding them; a workgroup that has to wait
+// for a slot starts only when another ends and delays its query's merge by a whole split.
+// With the total visible length known, split = total / (512 - T) bounds the live count by
+// 512; without it, T * max_visible stands in for the total (fewer, longer splits).
+IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k, int64_t total_visible) {
+  int64_t target_wg = 512;
+  if (const char* e = getenv("DSA_INDEXER_TARGET_WG")) target_wg = atoll(e) > 0 ? atoll(e) : 512;
+  const int64_t tmax = (int64_t)T * max_visible;
+  int64_t total = tmax, slots = target_wg;
+  if (total_visible > 0) {
+    total = total_visible < max_visible ? max_visible : (total_visible > tmax ? tmax : total_visible);
+    if (T < target_wg / 2) slots = target_wg - T;
+  }
+  int64_t split = (total + slots - 1) / slots;
+  split = (split + 63) / 64 * 64;
+  if (split < kMinSplit) split = kMinSplit;
+  if (split > kSplitMax) split = kSplitMax;
+  IndexerPlan pl = plan_indexer_split(T, max_visible, top_k, (int32_t)split);
+  if (total_visible > 0 && T <= kCompactMaxT) {
+    // no empty workgroups: at most total / split + T items exist (one partial split a query)
+    const int64_t items = (total + split - 1) / split + T;
+    pl.compact = 1;
+    if (items < pl.grid) pl.grid = (int32_t)items;
+  }
+  return pl;
+}
+
+// Workspace large enough for every split length a plan can choose.
+size_t indexer_workspace_bytes(int32_t T, int32_t max_visible, int32_t top_k) {
+  size_t b = 0;
+  for (int32_t s = kMinSplit; s <= kSplitMax; s += 64) {
+    const size_t x = plan_indexer_split(T, max_visible, top_k, s).bytes;
+    b = x > b ? x : b;
+  }
+  return b;
 }
 
 hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream) {

@@ -16,13 +16,16 @@ def layout_of(m, d):
                          pool_rows=d.pool_rows)
 
 
-def run_indexer(m, inp, d=None, *, top_k=None, workspace=None):
-    """-> (idx int64 [T, K], score float32 [T, K]) as numpy."""
+def run_indexer(m, inp, d=None, *, top_k=None, workspace=None, total_visible="exact"):
+    """-> (idx int64 [T, K], score float32 [T, K]) as numpy.  total_visible: the launch hint,
+    by default the true sum of the visible lengths (as the benchmark passes it)."""
     import torch
     d = d or to_device(inp)
     K = top_k or inp.spec.top_k
+    tv = int(np.sum(inp.q_visible, dtype=np.int64)) if total_visible == "exact" else int(total_visible)
     idx, score = m.indexer_topk(d.q_idx, d.w, d.k_pool, d.k_scale, layout_of(m, d), d.q_seq,
-                                d.q_visible, d.max_visible, K, workspace=workspace)
+                                d.q_visible, d.max_visible, K, workspace=workspace,
+                                total_visible=tv)
     torch.cuda.synchronize()
     return idx.cpu().numpy().astype(np.int64), score.cpu().numpy()
 

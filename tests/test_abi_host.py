@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 2
+    assert lib.dsa_abi_version() == 3
     for s in range(8):
         assert lib.dsa_status_string(s).startswith(b"DSA_")
 

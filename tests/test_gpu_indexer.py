@@ -144,6 +144,23 @@ def test_layout_invariance_and_determinism(dsa):
     assert np.array_equal(i1, i3) and np.array_equal(s1.view(np.uint32), s3.view(np.uint32))
 
 
+def test_total_visible_hint_changes_the_launch_not_the_result(dsa):
+    """The host hint only picks the split length: no hint, the true total, one far too small
+    and one far too large give bit-identical outputs (every position's score is summed the
+    same way whatever split holds it, and the output is in position order)."""
+    spec = scaled_spec(workload(4), seq_lens=[70000, 9000, 120000, 2100])
+    inp = make_inputs(spec, seed=12, with_sfa=False)
+    d = to_device(inp)
+    ws = dsa.zeroed_workspace(dsa.indexer_workspace_bytes(spec.num_queries, d.max_visible,
+                                                          spec.top_k), "cuda")
+    outs = [run_indexer(dsa, inp, d, workspace=ws, total_visible=tv)
+            for tv in ("exact", 0, 1, 10 ** 12)]
+    check(inp, outs[0][0], outs[0][1])
+    for i, s in outs[1:]:
+        assert np.array_equal(i, outs[0][0])
+        assert np.array_equal(s.view(np.uint32), outs[0][1].view(np.uint32))
+
+
 def test_workspace_reuse_across_sizes(dsa):
     """One zero-initialised workspace serves a large call and then smaller ones."""
     big = scaled_spec(workload(2), seq_lens=[40000, 40000, 3000])
