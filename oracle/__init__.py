@@ -17,7 +17,8 @@ blocking, fusion or reordering:
   full sort;
 * Sparse Flash Attention is dense softmax attention restricted to the selected rows of the
   MLA latent cache, the value being the first d_v columns of each row ("Day0 Adaptation and
-  Sparse Attention Optimization for Long-Sequence LLM Inference", section 4).
+  Sparse Attention Optimization for Long-Sequence LLM Inference", section 4);
+* the zigzag head-tail sharding of a causal chunk (see zigzag.py).
 
 Every function is pinned by the CPU tests against something other than itself (closed
 forms, brute force, library routines); see tests/test_oracle_*.py.
@@ -31,6 +32,7 @@ from .indexer import (index_scores, to_fp32_score, topk_order, IndexerResult,
                       indexer_topk_query, indexer_topk)
 from .sfa import sfa_dense, sfa_query, sfa
 from .compare import TopkCheck, check_topk_row, check_topk, AttnCheck, check_attention
+from .zigzag import zigzag_segments, zigzag_shard, contiguous_shard, causal_cost
 
 __all__ = [
     "decode", "decode_bf16", "decode_fp8_e4m3", "fp8_e4m3_table", "encode_bf16_rne",
@@ -39,5 +41,6 @@ __all__ = [
     "decode_mxfp8", "logical_rows", "depage", "index_scores",
     "to_fp32_score", "topk_order", "IndexerResult", "indexer_topk_query", "indexer_topk",
     "sfa_dense", "sfa_query", "sfa", "TopkCheck", "check_topk_row", "check_topk",
-    "AttnCheck", "check_attention",
+    "AttnCheck", "check_attention", "zigzag_segments", "zigzag_shard", "contiguous_shard",
+    "causal_cost",
 ]
