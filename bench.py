@@ -17,12 +17,15 @@ recorded around it in every 16th step of the timed region; an event pair costs t
 microseconds, so the other steps run unbracketed) and the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--config 4] [--sfa-kv fp8]
+    python bench.py --config 6 --shards 4 [--layout zigzag|contiguous] --steps 5 --warmup 2
 
 --sfa-kv fp8 stores the latent cache as fp8 rows quantized per 128-column tile (written by
 dsa_store_kv on the GPU before timing) instead of bf16 rows.  --idx-keys mxfp8 stores the
 index keys in MXFP8 (e4m3 codes, one E8M0 scale byte per group of 32 dims, written by
 dsa_store_index_keys on the GPU from the same N(0,1) keys) instead of fp8 with per-token
-scales; the CPU baseline then reads the oracle's quantization of the same keys.
+scales; the CPU baseline then reads the oracle's quantization of the same keys.  --shards G
+times a chunk of queries cut into G shards (zigzag head-tail pairs or contiguous ranges), each
+shard's step on its own: the share one device of a context-parallel group would run.
 """
 from __future__ import annotations
 
@@ -183,12 +186,85 @@ def cpu_baseline(inp, budget_s=12.0):
                       f"{cores} available cores"}
 
 
+def shard_bench(args, dsa, torch, spec, inp, base, lay):
+    """The chunk's queries cut into --shards shards (zigzag head-tail pairs from
+    dsa_zigzag_ranges, or contiguous ranges); each shard's step (indexer + SFA over just its
+    queries) is timed on its own with HIP events, as the share one device of a context-parallel
+    group would run.  value = all queries / the sum of the shard times (this one GPU running
+    every shard); the per-shard times and their max/min show the balance."""
+    G, T, K = args.shards, spec.num_queries, spec.top_k
+    shards = []
+    for g in range(G):
+        if args.layout == "zigzag":
+            (b0, e0), (b1, e1) = dsa.zigzag_ranges(T, G, g)
+            rows = np.concatenate([np.arange(b0, e0), np.arange(b1, e1)])
+        else:
+            rows = np.arange(g * T // G, (g + 1) * T // G)
+        V = np.asarray(inp.q_visible)[rows]
+        o = torch.from_numpy(rows).cuda()
+        sub = {f: getattr(base, f)[o].contiguous() for f in ("q_idx", "w", "q_seq", "q_visible", "q_sfa")}
+        n = len(rows)
+        shards.append(dict(rows=rows, V=V, sub=sub, n=n,
+                           ws_i=dsa.zeroed_workspace(dsa.indexer_workspace_bytes(n, int(V.max()), K), "cuda"),
+                           ws_s=dsa.zeroed_workspace(dsa.sfa_workspace_bytes(n, spec.sfa_heads, K, spec.d_v), "cuda"),
+                           idx=torch.empty((n, K), dtype=torch.int32, device="cuda"),
+                           out=torch.empty((n, spec.sfa_heads, spec.d_v), dtype=base.q_sfa.dtype, device="cuda")))
+
+    def run(s, ev=None):
+        u = s["sub"]
+        if ev:
+            ev[0].record()
+        dsa.indexer_topk(u["q_idx"], u["w"], base.k_pool, base.k_scale, lay, u["q_seq"], u["q_visible"],
+                         int(s["V"].max()), K, out_idx=s["idx"], want_score=False, workspace=s["ws_i"],
+                         total_visible=int(s["V"].sum()))
+        if ev:
+            ev[1].record()
+        dsa.sparse_attn(u["q_sfa"], base.kv_pool, s["idx"], lay, u["q_seq"], spec.softmax_scale, spec.d_v,
+                        out=s["out"], want_lse=False, workspace=s["ws_s"])
+        if ev:
+            ev[2].record()
+
+    steps = max(1, args.steps)
+    idx_ms, step_ms = [], []
+    for s in shards:
+        for _ in range(args.warmup):
+            run(s)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in evs:
+            run(s, e)
+        torch.cuda.synchronize()
+        idx_ms.append(float(np.mean([e[0].elapsed_time(e[1]) for e in evs])))
+        step_ms.append(float(np.mean([e[0].elapsed_time(e[2]) for e in evs])))
+    total_ms = sum(step_ms)
+    V_all = [int(v) for v in inp.q_visible]
+    idx_tflops = indexer_flops(spec, V_all) / (sum(idx_ms) * 1e-3) / 1e12
+    print(f"bench: {G} {args.layout} shards, step ms per shard {[round(x, 3) for x in step_ms]}, "
+          f"max/min {max(step_ms) / min(step_ms):.3f}", file=sys.stderr, flush=True)
+    line = {
+        "metric": METRIC, "value": T / (total_ms * 1e-3), "unit": "queries/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": total_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.name, "queries_per_step": T, "top_k": K,
+                   "shards": G, "layout": args.layout,
+                   "shard_queries": [s["n"] for s in shards],
+                   "shard_causal_positions": [int(s["V"].sum()) for s in shards],
+                   "shard_step_ms": step_ms, "shard_indexer_ms": idx_ms,
+                   "shard_max_over_min": max(step_ms) / min(step_ms)},
+        "roofline": {"bound": "mfma", "kernel": "indexer_topk_kernel", "achieved": idx_tflops,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": idx_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=4, help="workload number (1-5)")
+    ap.add_argument("--config", type=int, default=4, help="workload number (1-6)")
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -197,6 +273,11 @@ def main():
                     help="latent cache storage read by SFA")
     ap.add_argument("--idx-keys", choices=("default", "mxfp8"), default="default",
                     help="index key storage (default: the workload's)")
+    ap.add_argument("--shards", type=int, default=0,
+                    help="time the workload cut into this many shards of queries, one after the "
+                         "other (each one device's share at its real shape)")
+    ap.add_argument("--layout", choices=("zigzag", "contiguous"), default="zigzag",
+                    help="how --shards cuts the chunk of queries")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel for scaling the HBM byte counters) and exit")
@@ -282,6 +363,9 @@ def main():
                dsa.make_layout(None, 0, seq_stride=d.seq_stride, num_seqs=spec.num_seqs,
                                pool_rows=d.pool_rows) for d in devs]
     K = spec.top_k
+    if args.shards:
+        shard_bench(args, dsa, torch, spec, inp, base, layouts[0])
+        return
     ws_i = dsa.zeroed_workspace(dsa.indexer_workspace_bytes(T, base.max_visible, K), "cuda")
     ws_s = dsa.zeroed_workspace(dsa.sfa_workspace_bytes(T, spec.sfa_heads, K, spec.d_v), "cuda")
     outs = []

@@ -215,6 +215,24 @@ dsa_status dsa_store_index_keys(const float* k_new, int32_t n_tokens, int32_t he
 dsa_status dsa_store_kv(const void* kv_new, dsa_dtype src_dtype, int32_t n_tokens, int32_t d_qk,
                         const int64_t* slot, void* kv_pool, dsa_dtype pool_dtype, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * dsa_zigzag_ranges: the token ranges of one shard of a causal chunk under the zigzag
+ * head-tail layout ("Day0 Adaptation and Performance Optimization for Novel Long-Sequence
+ * Reasoning Models", section 5; "Large Model Inference Acceleration: Day-0 Adaptation...",
+ * section 3.1; "Optimizing and Deploying Ultra-Long Sequence Inference Architectures",
+ * section 3.2).  A chunk of n_tokens new tokens (token i sees prefix + i + 1 positions, so
+ * later tokens cost more) is cut into 2 * n_shards segments, segment s being
+ * [floor(s * n_tokens / (2 n_shards)), floor((s + 1) * n_tokens / (2 n_shards))); shard g
+ * takes segment g (its head range) and segment 2 n_shards - 1 - g (its tail range), which
+ * pairs short and long histories.  Running each shard's queries (dsa_indexer_topk and
+ * dsa_sparse_attn over just those rows of q, head_w, q_seq and q_visible) and putting the
+ * rows back in token order gives the unsharded result.
+ *   ranges (host, 4 int64): written with {head_begin, head_end, tail_begin, tail_end}.
+ * Host-only arithmetic: no device is touched.  Errors: DSA_ERR_NULL (ranges NULL),
+ * DSA_ERR_SHAPE (n_tokens < 0, n_shards < 1, shard outside [0, n_shards)).
+ * --------------------------------------------------------------------------------------- */
+dsa_status dsa_zigzag_ranges(int64_t n_tokens, int32_t n_shards, int32_t shard, int64_t* ranges);
+
 /* Human-readable name of a status (static storage, never NULL). */
 const char* dsa_status_string(dsa_status status);
 

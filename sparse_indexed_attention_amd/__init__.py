@@ -80,6 +80,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dsa_status_string.restype = ctypes.c_char_p
     lib.dsa_abi_version.argtypes = []
     lib.dsa_abi_version.restype = _I32
+    lib.dsa_zigzag_ranges.argtypes = [ctypes.c_int64, _I32, _I32, _P]
+    lib.dsa_zigzag_ranges.restype = _I32
     _lib = lib
     return lib
 
@@ -133,6 +135,16 @@ def make_queries(q_seq, q_visible=None, max_visible: int = 0, total_visible: int
     return DsaQueries(q_seq.shape[0], q_seq.data_ptr(),
                       None if q_visible is None else q_visible.data_ptr(), max_visible,
                       total_visible)
+
+
+def zigzag_ranges(n_tokens: int, n_shards: int, shard: int):
+    """((head_begin, head_end), (tail_begin, tail_end)) of one zigzag shard of a causal chunk
+    (dsa_zigzag_ranges)."""
+    r = (ctypes.c_int64 * 4)()
+    st = load().dsa_zigzag_ranges(n_tokens, n_shards, shard, ctypes.cast(r, _P))
+    if st != 0:
+        raise DsaError("dsa_zigzag_ranges", st)
+    return (r[0], r[1]), (r[2], r[3])
 
 
 def indexer_workspace_bytes(num_queries: int, max_visible: int, top_k: int) -> int:

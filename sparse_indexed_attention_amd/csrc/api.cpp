@@ -244,4 +244,18 @@ const char* dsa_status_string(dsa_status s) {
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
 
+dsa_status dsa_zigzag_ranges(int64_t n_tokens, int32_t n_shards, int32_t shard, int64_t* ranges) {
+  if (!ranges) return DSA_ERR_NULL;
+  if (n_tokens < 0 || n_shards < 1 || shard < 0 || shard >= n_shards) return DSA_ERR_SHAPE;
+  // segment bounds floor(s * n / m) without overflow for n < 2^62: n = a * m + b
+  const int64_t m = 2 * (int64_t)n_shards, a = n_tokens / m, b = n_tokens % m;
+  auto bound = [&](int64_t s) { return s * a + s * b / m; };
+  const int64_t tail = m - 1 - shard;
+  ranges[0] = bound(shard);
+  ranges[1] = bound(shard + 1);
+  ranges[2] = bound(tail);
+  ranges[3] = bound(tail + 1);
+  return DSA_OK;
+}
+
 }  // extern "C"

@@ -109,12 +109,22 @@ def decode_fp8_1m() -> Spec:
     return _decode_spec("decode_fp8_1m", [1 << 20], k_dtype="fp8", k_std=1.0)
 
 
+def prefill_causal_16k() -> Spec:
+    """Causal prefill with no prefix: one sequence of 16384 new tokens, query i sees
+    positions [0, i + 1), so the first 2047 queries see fewer than K positions and later
+    queries cost more (the load the zigzag layout balances); bf16, Top-K 2048."""
+    n = 16384
+    return Spec(name="prefill_causal_16k", seq_lens=(n,), q_seq=(0,) * n,
+                q_visible=tuple(range(1, n + 1)))
+
+
 WORKLOADS = {
     1: tiny_decode_fp32,
     2: decode_bf16_32k,
     3: prefill_chunk_bf16,
     4: decode_fp8_128k,
     5: decode_fp8_1m,
+    6: prefill_causal_16k,
 }
 
 

@@ -33,6 +33,28 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), n
 
 
+@pytest.mark.parametrize("L,G", [(0, 1), (1, 1), (16, 2), (24, 4), (17, 2), (1000, 3), (4099, 8),
+                                 (5, 4), (16384, 8), (3 * 10 ** 12 + 7, 5)])
+def test_zigzag_ranges_match_the_oracle(L, G):
+    import sparse_indexed_attention_amd as m
+    import oracle
+    for g in range(G):
+        (b0, e0), (b1, e1) = m.zigzag_ranges(L, G, g)
+        seg = oracle.zigzag_segments(L, G)
+        assert (b0, e0) == seg[g] and (b1, e1) == seg[2 * G - 1 - g]
+
+
+def test_zigzag_ranges_reject_bad_arguments(lib):
+    import ctypes
+    r = (ctypes.c_int64 * 4)()
+    p = ctypes.cast(r, ctypes.c_void_p)
+    assert lib.dsa_zigzag_ranges(16, 2, 0, None) == 1
+    assert lib.dsa_zigzag_ranges(-1, 2, 0, p) == 2
+    assert lib.dsa_zigzag_ranges(16, 0, 0, p) == 2
+    assert lib.dsa_zigzag_ranges(16, 2, 2, p) == 2
+    assert lib.dsa_zigzag_ranges(16, 2, -1, p) == 2
+
+
 def test_version_and_status_strings(lib):
     assert lib.dsa_abi_version() == 3
     for s in range(8):
