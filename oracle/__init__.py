@@ -18,7 +18,8 @@ blocking, fusion or reordering:
 * Sparse Flash Attention is dense softmax attention restricted to the selected rows of the
   MLA latent cache, the value being the first d_v columns of each row ("Day0 Adaptation and
   Sparse Attention Optimization for Long-Sequence LLM Inference", section 4);
-* the zigzag head-tail sharding of a causal chunk (see zigzag.py).
+* the zigzag head-tail sharding of a causal chunk (see zigzag.py);
+* the indexer prolog: projections of the hidden vector and the key's RMSNorm (prolog.py).
 
 Every function is pinned by the CPU tests against something other than itself (closed
 forms, brute force, library routines); see tests/test_oracle_*.py.
@@ -33,6 +34,7 @@ from .indexer import (index_scores, to_fp32_score, topk_order, IndexerResult,
 from .sfa import sfa_dense, sfa_query, sfa
 from .compare import TopkCheck, check_topk_row, check_topk, AttnCheck, check_attention
 from .zigzag import zigzag_segments, zigzag_shard, contiguous_shard, causal_cost
+from .prolog import project, rms_norm, indexer_prolog
 
 __all__ = [
     "decode", "decode_bf16", "decode_fp8_e4m3", "fp8_e4m3_table", "encode_bf16_rne",
@@ -42,5 +44,5 @@ __all__ = [
     "to_fp32_score", "topk_order", "IndexerResult", "indexer_topk_query", "indexer_topk",
     "sfa_dense", "sfa_query", "sfa", "TopkCheck", "check_topk_row", "check_topk",
     "AttnCheck", "check_attention", "zigzag_segments", "zigzag_shard", "contiguous_shard",
-    "causal_cost",
+    "causal_cost", "project", "rms_norm", "indexer_prolog",
 ]
