@@ -259,6 +259,71 @@ def shard_bench(args, dsa, torch, spec, inp, base, lay):
     print(json.dumps(line), flush=True)
 
 
+def prolog_bench(args, dsa, torch, spec):
+    """dsa_indexer_prolog for the workload's T new tokens (hidden width --prolog-dx, the
+    indexer's H x D, keys stored in the workload's key format into a T-row pool), timed with
+    HIP events around each call.  Decode is bound by reading the weight matrix (d_x x
+    (H D + D + H) bf16); a prefill chunk by the GEMM's MFMA rate."""
+    from synth import make_prolog_inputs
+    T, H, D, dx = spec.num_queries, spec.idx_heads, spec.idx_dim, args.prolog_dx
+    N = H * D + D + H
+    pi = make_prolog_inputs(T, dx, H, D, seed=args.seed or 1)
+    x = torch.from_numpy(pi.x.view(np.int16)).cuda().view(torch.bfloat16)
+    W = torch.from_numpy(pi.w_proj.view(np.int16)).cuda().view(torch.bfloat16)
+    g = torch.from_numpy(pi.gain).cuda()
+    slot = torch.arange(T, dtype=torch.int64, device="cuda")
+    fmt = spec.k_dtype
+    if fmt == "fp8":
+        pool = torch.zeros((T, D), dtype=torch.uint8, device="cuda")
+        ks = torch.zeros((T,), dtype=torch.float32, device="cuda")
+        key_bytes = D + 4
+    else:
+        pool = torch.zeros((T, D), dtype=torch.bfloat16, device="cuda")
+        ks, key_bytes = None, 2 * D
+    ws = torch.empty(dsa.prolog_workspace_bytes(T, H, D), dtype=torch.uint8, device="cuda")
+    q = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    run = lambda: dsa.indexer_prolog(x, W, g, pi.eps, H, D, slot=slot, k_pool=pool, k_scale=ks,
+                                     q_out=q, w_out=w, workspace=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        run()
+        e[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    byts = dx * N * 2 + T * dx * 2 + T * (H * D * 2 + H * 4 + key_bytes) + D * 4
+    flops = 2.0 * T * dx * N
+    gbs, tfl = byts / (ms * 1e-3) / 1e9, flops / (ms * 1e-3) / 1e12
+    # a few tokens reuse no weight: the weight read bounds it; thousands of tokens: the MFMA rate
+    hbm = byts / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    roof = ({"bound": "hbm", "kernel": "indexer prolog (GEMM + epilogue)", "achieved": gbs,
+             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+            if hbm else
+            {"bound": "mfma", "kernel": "indexer prolog (GEMM + epilogue)", "achieved": tfl,
+             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tfl / MFMA_BF16_PEAK_TFLOPS,
+             "traffic": None})
+    print(f"bench: prolog T={T} d_x={dx} H={H} D={D} keys {fmt}: {ms * 1e3:.1f} us per call, "
+          f"{gbs:.0f} GB/s, {tfl:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    line = {
+        "metric": "indexer prolog tokens/sec (projections + key RMSNorm + key store)",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.name + "_prolog", "tokens": T, "d_x": dx, "heads": H,
+                   "head_dim": D, "key_format": fmt, "algorithmic_bytes": byts, "flops": flops,
+                   "wall_ms_per_call": wall * 1e3 / steps},
+        "roofline": roof, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +343,10 @@ def main():
                          "other (each one device's share at its real shape)")
     ap.add_argument("--layout", choices=("zigzag", "contiguous"), default="zigzag",
                     help="how --shards cuts the chunk of queries")
+    ap.add_argument("--prolog", action="store_true",
+                    help="time the indexer prolog (projections, key RMSNorm, query quantization, "
+                         "key store) for the workload's new tokens instead of the step")
+    ap.add_argument("--prolog-dx", type=int, default=7168, help="hidden width for --prolog")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel for scaling the HBM byte counters) and exit")
@@ -307,6 +376,9 @@ def main():
     dsa.load()
     torch.cuda.set_device(0)
     spec = workload(args.config)
+    if args.prolog:
+        prolog_bench(args, dsa, torch, spec)
+        return
     seed = args.seed or args.config
     print(f"bench: generating {spec.name} (seed {seed})", file=sys.stderr, flush=True)
     mx_keys = args.idx_keys == "mxfp8"

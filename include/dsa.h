@@ -51,7 +51,8 @@ typedef enum {
   DSA_ERR_UNSUPPORTED = 4, /* valid in principle, not built (e.g. head_dim or top_k too large) */
   DSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the *_workspace_size query      */
   DSA_ERR_ALIGN = 6,       /* a device pointer is not 16-byte aligned                       */
-  DSA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                    */
+  DSA_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed                    */
+  DSA_ERR_BLAS = 8         /* the library GEMM (rocBLAS) failed                             */
 } dsa_status;
 
 typedef enum {
@@ -214,6 +215,44 @@ dsa_status dsa_store_index_keys(const float* k_new, int32_t n_tokens, int32_t he
 
 dsa_status dsa_store_kv(const void* kv_new, dsa_dtype src_dtype, int32_t n_tokens, int32_t d_qk,
                         const int64_t* slot, void* kv_pool, dsa_dtype pool_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * dsa_indexer_prolog: the indexer's inputs for n_tokens new tokens, from their hidden vectors
+ * ("Day0 Adaptation and Performance Optimization for Novel Long-Sequence Reasoning Models",
+ * section 3; "Large Model Inference Acceleration: Day-0 Adaptation...", section 1.2;
+ * "Optimizing and Deploying Ultra-Long Sequence Inference Architectures", section I: query
+ * projection, key normalization, query quantization, head-weight projection), and the key's
+ * store into the paged key pool.  With H = n_heads, D = head_dim, N = H * D + D + H:
+ *     Y = x w_proj                          fp32 sums of bf16 products (one library GEMM)
+ *     q_out[t, h, d] = Y[t, h * D + d]      bf16, nearest even; for k_dtype MXFP8_E4M3 the
+ *                                           MXFP8 group-32 quantization of Y's query part
+ *                                           (defined under dsa_indexer_topk), dequantized
+ *     k[t, d]  = Y[t, H*D + d] / sqrt(mean_d Y[t, H*D + d]^2 + eps) * k_gain[d]
+ *     w_out[t, h] = Y[t, H*D + D + h]       fp32
+ * and k[t] is written to k_pool row slot[t] as dsa_store_index_keys writes it (k_dtype F32,
+ * BF16, FP8_E4M3 with k_scale, or MXFP8_E4M3 with its scale bytes in k_scale).
+ *   x:       [n_tokens, d_x] bf16 (device)
+ *   w_proj:  [d_x, N] bf16 row-major (device): columns [0, H*D) the query, head-major, then
+ *            D key columns, then H head-weight columns
+ *   k_gain:  [D] fp32 (device); eps >= 0
+ *   q_out:   [n_tokens, H, D] bf16; w_out: [n_tokens, H] fp32; k_out: [n_tokens, D] fp32 or
+ *            NULL (the normalized keys before their storage rounding)
+ *   slot, k_pool, k_scale: the store; slot and k_pool both NULL skips it
+ *   1 <= head_dim <= 1024 (% 32 == 0 for MXFP8_E4M3), n_heads >= 1, n_heads * head_dim <=
+ *   65534 * 2048, d_x >= 1, 1 <= n_tokens <= 2^20.  All buffers are the caller's and stay so.
+ * workspace: dsa_indexer_prolog_workspace_size(...) bytes (any contents).  The call
+ * enqueues the GEMM and one kernel on `stream` and returns; the library keeps one rocBLAS
+ * handle per device (created on first use) and serializes only the enqueueing of calls.
+ * Errors: DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_DTYPE, DSA_ERR_UNSUPPORTED (beyond those sizes),
+ * DSA_ERR_WORKSPACE, DSA_ERR_ALIGN, DSA_ERR_BLAS (rocBLAS refused or failed), DSA_ERR_HIP.
+ * --------------------------------------------------------------------------------------- */
+size_t dsa_indexer_prolog_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim);
+
+dsa_status dsa_indexer_prolog(const void* x, int32_t n_tokens, int32_t d_x, const void* w_proj,
+                              const float* k_gain, float eps, int32_t n_heads, int32_t head_dim,
+                              void* q_out, float* w_out, float* k_out, const int64_t* slot,
+                              void* k_pool, dsa_dtype k_dtype, void* k_scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * dsa_zigzag_ranges: the token ranges of one shard of a causal chunk under the zigzag

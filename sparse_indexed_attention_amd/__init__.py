@@ -82,6 +82,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dsa_abi_version.restype = _I32
     lib.dsa_zigzag_ranges.argtypes = [ctypes.c_int64, _I32, _I32, _P]
     lib.dsa_zigzag_ranges.restype = _I32
+    lib.dsa_indexer_prolog_workspace_size.argtypes = [_I32, _I32, _I32]
+    lib.dsa_indexer_prolog_workspace_size.restype = _SZ
+    lib.dsa_indexer_prolog.argtypes = [_P, _I32, _I32, _P, _P, ctypes.c_float, _I32, _I32,
+                                       _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]
+    lib.dsa_indexer_prolog.restype = _I32
     _lib = lib
     return lib
 
@@ -225,6 +230,43 @@ def store_index_keys(k_new, slot, k_pool, k_scale=None, stream=None):
                                      _stream(stream))
     if st != 0:
         raise DsaError("dsa_store_index_keys", st)
+
+
+_KEY_FORMATS = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3}
+
+
+def prolog_workspace_bytes(n_tokens: int, n_heads: int, head_dim: int) -> int:
+    return int(load().dsa_indexer_prolog_workspace_size(n_tokens, n_heads, head_dim))
+
+
+def indexer_prolog(x, w_proj, k_gain, eps: float, n_heads: int, head_dim: int, *, slot=None,
+                   k_pool=None, k_scale=None, key_format: str = "bf16", want_k: bool = False,
+                   q_out=None, w_out=None, k_out=None, workspace=None, stream=None):
+    """dsa_indexer_prolog: x [T, d_x] bf16, w_proj [d_x, H*D + D + H] bf16, k_gain [D] float32
+    -> (q [T, H, D] bf16, w [T, H] float32, k [T, D] float32 or None); with slot and k_pool
+    the keys are also stored (k_pool's dtype as in store_index_keys).  Without a pool,
+    key_format ("bf16", "fp8", "mxfp8", "f32") says which keys the query is made for (MXFP8
+    keys: the query is MXFP8-quantized)."""
+    torch = _torch()
+    lib = load()
+    T, d_x = x.shape
+    if q_out is None:
+        q_out = torch.empty((T, n_heads, head_dim), dtype=torch.bfloat16, device=x.device)
+    if w_out is None:
+        w_out = torch.empty((T, n_heads), dtype=torch.float32, device=x.device)
+    if k_out is None and want_k:
+        k_out = torch.empty((T, head_dim), dtype=torch.float32, device=x.device)
+    kd = _key_dtype(k_pool, k_scale) if k_pool is not None else _KEY_FORMATS[key_format]
+    if workspace is None:
+        workspace = torch.empty(max(prolog_workspace_bytes(T, n_heads, head_dim), 16),
+                                dtype=torch.uint8, device=x.device)
+    st = lib.dsa_indexer_prolog(_ptr(x), T, d_x, _ptr(w_proj), _ptr(k_gain), float(eps), n_heads,
+                                head_dim, _ptr(q_out), _ptr(w_out), _ptr(k_out), _ptr(slot),
+                                _ptr(k_pool), kd, _ptr(k_scale), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise DsaError("dsa_indexer_prolog", st)
+    return q_out, w_out, k_out
 
 
 def store_kv(kv_new, slot, kv_pool, stream=None):

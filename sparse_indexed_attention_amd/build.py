@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["api.cpp", "indexer.hip", "sfa.hip", "store.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "sfa.hip", "store.hip", "prolog.hip"]
+LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 ARCH = "gfx950"
 
 
@@ -35,7 +36,7 @@ def flags():
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc(), *flags(), *[os.path.join(CSRC, s) for s in SOURCES], *LIBS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -238,11 +238,65 @@ const char* dsa_status_string(dsa_status s) {
     case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
     case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: device pointer not 16-byte aligned";
     case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP runtime or launch failure";
+    case DSA_ERR_BLAS: return "DSA_ERR_BLAS: the library GEMM failed";
   }
   return "DSA_ERR_UNKNOWN";
 }
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+size_t dsa_indexer_prolog_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim) {
+  if (n_tokens < 1 || n_heads < 1 || head_dim < 1) return 0;
+  const int64_t N = (int64_t)n_heads * head_dim + head_dim + n_heads;
+  return (size_t)((n_tokens * N * 4 + 255) / 256 * 256);
+}
+
+dsa_status dsa_indexer_prolog(const void* x, int32_t n_tokens, int32_t d_x, const void* w_proj,
+                              const float* k_gain, float eps, int32_t n_heads, int32_t head_dim,
+                              void* q_out, float* w_out, float* k_out, const int64_t* slot,
+                              void* k_pool, dsa_dtype k_dtype, void* k_scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!x || !w_proj || !k_gain || !q_out || !w_out) return DSA_ERR_NULL;
+  if (!slot != !k_pool) return DSA_ERR_NULL;
+  if (k_dtype != DSA_F32 && k_dtype != DSA_BF16 && k_dtype != DSA_FP8_E4M3 &&
+      k_dtype != DSA_MXFP8_E4M3)
+    return DSA_ERR_DTYPE;
+  if (k_pool && (k_dtype == DSA_FP8_E4M3 || k_dtype == DSA_MXFP8_E4M3) && !k_scale)
+    return DSA_ERR_NULL;
+  if (n_tokens < 1 || n_tokens > (1 << 20) || d_x < 1 || n_heads < 1 || head_dim < 1 ||
+      !(eps >= 0.f) || eps == INFINITY)
+    return DSA_ERR_SHAPE;
+  if (k_dtype == DSA_MXFP8_E4M3 && head_dim % 32 != 0) return DSA_ERR_SHAPE;
+  const int64_t N = (int64_t)n_heads * head_dim + head_dim + n_heads;
+  if (N > (1 << 30)) return DSA_ERR_SHAPE;
+  if (head_dim > kPrologMaxD || (int64_t)n_heads * head_dim > (int64_t)65534 * 2048)
+    return DSA_ERR_UNSUPPORTED;   // the epilogue's grid takes 2048 query values a workgroup
+  const size_t need = dsa_indexer_prolog_workspace_size(n_tokens, n_heads, head_dim);
+  if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+  if (misaligned(x) || misaligned(w_proj) || misaligned(k_gain) || misaligned(q_out) ||
+      misaligned(w_out) || misaligned(k_out) || misaligned(slot) || misaligned(k_pool) ||
+      misaligned(k_scale) || misaligned(workspace))
+    return DSA_ERR_ALIGN;
+  PrologParams p{};
+  p.y = static_cast<const float*>(workspace);
+  p.N = (int32_t)N;
+  p.H = n_heads;
+  p.D = head_dim;
+  p.eps = eps;
+  p.gain = k_gain;
+  p.q_out = q_out;
+  p.q_mx = k_dtype == DSA_MXFP8_E4M3;
+  p.w_out = w_out;
+  p.k_out = k_out;
+  p.slot = slot;
+  p.pool = k_pool;
+  p.k_dt = k_dtype;
+  p.k_scale = static_cast<float*>(k_scale);
+  int blas = 0;
+  const hipError_t e = run_prolog(x, n_tokens, d_x, w_proj, p, static_cast<hipStream_t>(stream), &blas);
+  if (blas) return DSA_ERR_BLAS;
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
 
 dsa_status dsa_zigzag_ranges(int64_t n_tokens, int32_t n_shards, int32_t shard, int64_t* ranges) {
   if (!ranges) return DSA_ERR_NULL;

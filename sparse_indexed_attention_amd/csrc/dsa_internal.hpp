@@ -98,4 +98,27 @@ hipError_t launch_store_index_keys(const float* k_new, int32_t n, int32_t D, con
 hipError_t launch_store_kv(const void* kv_new, int32_t src_dtype, int32_t n, int32_t dqk,
                            const int64_t* slot, void* kv_pool, int32_t pool_dtype, hipStream_t s);
 
+// ------------------------------------------------------------------ indexer prolog
+constexpr int kPrologMaxD = 1024;      // longest key (head_dim) of the prolog
+constexpr int kMaxDevices = 64;
+
+struct PrologParams {
+  const float* y;         // [T, N] fp32 projections (workspace), N = H * D + D + H
+  int32_t N, H, D;
+  float eps;
+  const float* gain;      // [D] RMSNorm gain of the key
+  void* q_out;            // [T, H, D] bf16
+  int32_t q_mx;           // quantize the query to MXFP8 (for MXFP8 keys)
+  float* w_out;           // [T, H]
+  float* k_out;           // [T, D] or nullptr
+  const int64_t* slot;    // [T] key-pool rows, or nullptr with pool
+  void* pool;             // key pool or nullptr (no store)
+  int32_t k_dt;
+  float* k_scale;
+};
+
+// rocBLAS GEMM then the epilogue; *blas_status is the rocblas_status when that failed
+hipError_t run_prolog(const void* x, int32_t T, int32_t d_x, const void* w_proj,
+                      const PrologParams& p, hipStream_t stream, int* blas_status);
+
 }  // namespace dsa

@@ -19,7 +19,7 @@
 // magnitude at or below 448 (so no code saturates and x / scale is exact), the rope columns
 // 512..575 in bf16.  One workgroup of 128 threads per token, thread i owning columns 4i..4i+3.
 
-#include "dsa_internal.hpp"
+#include "store_row.hpp"
 
 namespace dsa {
 namespace {
@@ -27,43 +27,8 @@ namespace {
 __global__ __launch_bounds__(64) void store_index_keys_kernel(const float* k_new, int D,
                                                               const int64_t* slot, void* pool,
                                                               int dt, float* k_scale) {
-  const int i = blockIdx.x, lane = threadIdx.x;
-  const float* src = k_new + (size_t)i * D;
-  const int64_t row = slot[i];
-  if (dt == kDtF32) {
-    for (int d = lane; d < D; d += 64) ((float*)pool)[row * D + d] = src[d];
-    return;
-  }
-  if (dt == kDtBF16) {
-    for (int d = lane; d < D; d += 64)
-      ((uint16_t*)pool)[row * D + d] = (uint16_t)f32_to_bf16_bits(src[d]);
-    return;
-  }
-  if (dt == kDtMX) {
-    // column d = d0 + lane: lanes 0..31 and 32..63 each hold one group of 32 (D % 32 == 0)
-    uint8_t* sbytes = (uint8_t*)k_scale + row * (D / 32);
-    for (int d0 = 0; d0 < D; d0 += 64) {
-      const int d = d0 + lane;
-      const float x = d < D ? src[d] : 0.f;
-      float amax = fabsf(x);
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-      const uint32_t sb = mx_scale_byte(amax);
-      if (d < D) {
-        ((uint8_t*)pool)[row * D + d] = (uint8_t)f32_to_fp8_e4m3(x * mx_inv_scale(sb));
-        if ((lane & 31) == 0) sbytes[d >> 5] = (uint8_t)sb;
-      }
-    }
-    return;
-  }
-  float amax = 0.f;
-  for (int d = lane; d < D; d += 64) amax = fmaxf(amax, fabsf(src[d]));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  const float scale = amax == 0.f ? 1.f : amax / 448.f;
-  for (int d = lane; d < D; d += 64)
-    ((uint8_t*)pool)[row * D + d] = (uint8_t)f32_to_fp8_e4m3(src[d] / scale);
-  if (lane == 0) k_scale[row] = scale;
+  const int i = blockIdx.x;
+  store_key_row(k_new + (size_t)i * D, D, slot[i], pool, dt, k_scale, threadIdx.x);
 }
 
 __global__ __launch_bounds__(256) void store_kv_kernel(const void* src, int sdt, int dqk,

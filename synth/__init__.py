@@ -6,6 +6,7 @@ block table).  It holds none of the path's arithmetic: no scoring, no selection 
 attention.  Both the CPU oracle and the HIP path consume what it produces.
 """
 from .configs import Spec, WORKLOADS, workload, scaled_spec
-from .generate import Inputs, make_inputs
+from .generate import Inputs, make_inputs, PrologInputs, make_prolog_inputs
 
-__all__ = ["Spec", "WORKLOADS", "workload", "scaled_spec", "Inputs", "make_inputs"]
+__all__ = ["Spec", "WORKLOADS", "workload", "scaled_spec", "Inputs", "make_inputs",
+           "PrologInputs", "make_prolog_inputs"]

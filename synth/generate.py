@@ -16,6 +16,7 @@ Unused block-table columns point at a NaN block.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 from typing import Optional
 
@@ -183,3 +184,26 @@ def make_inputs(spec: Spec, seed: int, *, sfa_dist: str = "config",
     return Inputs(spec=spec, q_idx=q_idx, w=w, k_pool=k_pool, k_scale=k_scale,
                   q_sfa=q_sfa, kv_pool=kv_pool, block_table=bt, seq_stride=stride,
                   q_seq=q_seq, q_visible=q_vis, seed=seed)
+
+
+@dataclass
+class PrologInputs:
+    """Hidden vectors and weights of the indexer prolog (bf16 bits) and the key's gain."""
+    x: np.ndarray        # [T, d_x] uint16
+    w_proj: np.ndarray   # [d_x, H*D + D + H] uint16
+    gain: np.ndarray     # [D] float32
+    n_heads: int
+    head_dim: int
+    eps: float
+
+
+def make_prolog_inputs(n_tokens: int, d_x: int, n_heads: int, head_dim: int, seed: int,
+                       eps: float = 1e-6) -> PrologInputs:
+    """x ~ N(0, 1) and W ~ N(0, 1/d_x), so every projection is about N(0, 1); gain ~
+    U(0.5, 1.5)."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    N = n_heads * head_dim + head_dim + n_heads
+    x = to_bf16_bits(_f32_normal(rng, (n_tokens, d_x), 1.0))
+    w = to_bf16_bits(_f32_normal(rng, (d_x, N), 1.0 / math.sqrt(d_x)))
+    gain = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
+    return PrologInputs(x, w, gain, n_heads, head_dim, eps)

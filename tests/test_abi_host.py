@@ -55,9 +55,33 @@ def test_zigzag_ranges_reject_bad_arguments(lib):
     assert lib.dsa_zigzag_ranges(16, 2, -1, p) == 2
 
 
+def test_prolog_rejects_bad_arguments(lib):
+    import sparse_indexed_attention_amd as m
+    P = lambda i: ctypes.c_void_p(A[i])
+    ws_ok = m.prolog_workspace_bytes(8, 64, 128)
+
+    def call(x=P(0), T=8, dx=7168, W=P(1), g=P(2), eps=1e-6, H=64, D=128, q=P(3), w=P(4), k=None,
+             slot=P(5), pool=P(6), kd=2, ks=P(7), ws=P(8), wsb=ws_ok):
+        return lib.dsa_indexer_prolog(x, T, dx, W, g, eps, H, D, q, w, k, slot, pool, kd, ks, ws,
+                                      wsb, None)
+    assert call(x=None) == 1
+    assert call(slot=None) == 1                      # a pool without slots
+    assert call(ks=None) == 1                        # fp8 keys need their scales
+    assert call(kd=7) == 3
+    assert call(T=0) == 2
+    assert call(eps=-1.0) == 2
+    assert call(eps=float("nan")) == 2
+    assert call(kd=3, D=40, H=2) == 2                # MXFP8 keys: head_dim % 32
+    assert call(D=2048, H=1, wsb=1 << 30) == 4
+    assert call(wsb=ws_ok - 1) == 5
+    assert call(ws=None) == 5
+    assert call(x=ctypes.c_void_p(A[0] + 2)) == 6
+    assert m.prolog_workspace_bytes(8, 64, 128) >= 8 * (64 * 128 + 128 + 64) * 4
+
+
 def test_version_and_status_strings(lib):
     assert lib.dsa_abi_version() == 3
-    for s in range(8):
+    for s in range(9):
         assert lib.dsa_status_string(s).startswith(b"DSA_")
 
 
