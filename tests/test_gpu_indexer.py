@@ -45,6 +45,9 @@ CASES = {
     # MFMA path, fp8 keys with per-token scales
     "fp8_mixed": lambda: scaled_spec(workload(4), seq_lens=[20000, 3333, 2049, 65, 1]),
     "fp8_k256": lambda: scaled_spec(workload(4), seq_lens=[30000, 70000], top_k=256),
+    # degenerate Top-K sizes on the fast path: K = 1, and K >= V (every position selected)
+    "fp8_k1": lambda: scaled_spec(workload(4), seq_lens=[5000, 1, 70, 2049], top_k=1),
+    "bf16_k_all": lambda: scaled_spec(workload(2), seq_lens=[100, 2048, 700, 1]),
     # reference path with mixed formats
     "ref_bf16q_fp8k": lambda: scaled_spec(workload(4), seq_lens=[3000, 5000], idx_heads=16,
                                           idx_dim=64, top_k=300),
@@ -210,3 +213,13 @@ def test_full_chunked_prefill_sampled(dsa):
     # causal: no query selects a position it cannot see
     V = inp.q_visible
     assert np.all((idx < V[:, None]) | (idx == -1))
+
+
+@pytest.mark.slow
+def test_max_context_single_query(dsa):
+    """The longest context a query may have (DSA_MAX_CONTEXT = 4M positions): 2048 splits of
+    2048 positions, the most a query can have, all merged by one workgroup."""
+    spec = scaled_spec(workload(5), seq_lens=[1 << 22])
+    inp = make_inputs(spec, seed=22, with_sfa=False)
+    idx, score = run_indexer(dsa, inp)
+    check(inp, idx, score)
