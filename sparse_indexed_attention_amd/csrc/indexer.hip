@@ -54,7 +54,15 @@ constexpr int kBins = 2048;               // radix bins per pass
 template <int MODE> struct Ring { static constexpr int D = 1, SLOT = 0; };
 template <> struct Ring<1> { static constexpr int D = 2, SLOT = 8192; };          // bf16 keys
 template <> struct Ring<2> { static constexpr int D = 4, SLOT = 4096 + 256; };    // fp8 keys + scales
-template <> struct Ring<3> : Ring<2> {};                                           // MXFP8 keys + scale bytes
+template <> struct Ring<3> : Ring<2> {};
+constexpr int kMqQ = 4;        // queries of a multi-query workgroup (one per wave)
+constexpr int kMqRing = 4;     // its shared ring of 8 KB bf16 key groups
+// Where a multi-query workgroup keeps things in the shared region while it scores: the
+// histogram the split selection uses stays at its start, the scores of queries 1.. follow
+// (query 0's are in the key array), and the ring takes the upper half.
+constexpr int kMqKeysOff = kBins * 4;
+constexpr int kMqRingOff = 32768;
+constexpr int kMqMinT = 256;   // fewest queries for multi-query workgroups                                           // MXFP8 keys + scale bytes
 
 // Bytes of the kernel's shared region: the scorer's ring while scoring, then the selection
 // arrays.
@@ -396,6 +404,126 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
     finish(g, acc0, acc1, FP8 && !MX ? *(const float*)(sb + GB + 4 * col) : 1.f);
   }
   wait_vmcnt<0>();                            // no load may still target the ring afterwards
+}
+
+// Multi-query scoring (bf16 keys, kMqQ queries of one sequence over one split, as in a
+// prefill chunk whose queries share the cached context).  Scoring one query per workgroup
+// re-reads the split's keys for every query through a two-slot ring per wave, and is then
+// bound by the latency of those loads.  Here the waves share one ring of kMqRing key groups
+// (kMqRing - 1 in flight) filled once for all the queries: every wave issues two of a
+// group's eight direct-to-LDS loads, and one barrier per group makes the group visible to all
+// waves and frees the slot of the previous one.  Wave w then scores query w with the same
+// MFMA steps as score_mfma, into its own key array.  Waves without a query (nq < kMqQ) still
+// load and pass the barriers.  Group indices past the split are clamped onto its last group,
+// so that every step issues the same loads and the waits stay exact.
+template <bool PAGED>
+__device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)[kMqQ], int nq,
+                                         int seq, int start, int lenmax, const int (&lens)[kMqQ],
+                                         uint32_t* const (&keys)[kMqQ], const Lds& L,
+                                         uint32_t* range) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  constexpr int ROWB = 256, CPR = 16, RPI = 4, LPR = 16;
+  constexpr int D = kMqRing, SLOT = 8192;
+  static_assert(kMqRingOff + D * SLOT <= region_bytes<1>(), "ring size");
+  static_assert(kMqKeysOff + (kMqQ - 1) * kSplitMax * 4 <= kMqRingOff, "scores below the ring");
+  static_assert(kSplitMax / 32 <= 64, "one lane per group of the split");
+  seq = __builtin_amdgcn_readfirstlane(seq);
+  start = __builtin_amdgcn_readfirstlane(start);
+  lenmax = __builtin_amdgcn_readfirstlane(lenmax);
+  const int ng = (lenmax + 31) >> 5;
+  const bool act = wave < nq;
+  const int t = __builtin_amdgcn_readfirstlane(act ? tq[wave] : tq[0]);
+  const int len = __builtin_amdgcn_readfirstlane(act ? lens[wave] : 0);
+  uint32_t* const kout = keys[act ? wave : 0];
+
+  const uint16_t* qb = (const uint16_t*)p.q + (size_t)t * (64 * 128);
+  bf16x8 a0[8], a1[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    a0[s] = *(const bf16x8*)(qb + col * 128 + half * 64 + 8 * s);
+    a1[s] = *(const bf16x8*)(qb + (32 + col) * 128 + half * 64 + 8 * s);
+  }
+  const float* lw = L.w + wave * 64;
+  load_to_lds<4>(p.w + (size_t)t * 64, 4u * lane, lds_addr(lw));
+  int gblk = 0;
+  if constexpr (PAGED)
+    gblk = p.L.bt[(int64_t)seq * p.L.bt_stride + ((start + 32 * min(lane, ng - 1)) >> p.L.bs_log2)];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  const int bsl = PAGED ? p.L.bs_log2 : 0;
+  const int64_t cbase = PAGED ? 0 : (int64_t)seq * p.L.seq_stride;
+  const uint8_t* kbytes = (const uint8_t*)p.k_pool;
+  const int cpos = lane % LPR;
+  auto slot_of = [&](int g) { return L.region + kMqRingOff + (g & (D - 1)) * SLOT; };
+  auto issue = [&](int g) {
+    uint8_t* sb = slot_of(g);
+    g = min(g, ng - 1);
+    const int gpos = start + 32 * g;
+    const int last = lenmax - 1 - 32 * g;
+    int64_t row0;
+    if constexpr (PAGED) {
+      const int blk = __builtin_amdgcn_readlane(gblk, g);
+      row0 = ((int64_t)blk << bsl) | (gpos & ((1 << bsl) - 1));
+    }
+    else row0 = cbase + gpos;
+    const uint8_t* gbase = kbytes + row0 * ROWB;
+    const uint32_t lb = lds_addr(sb);
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * wave + ii;
+      const int r = RPI * i + lane / LPR;
+      const uint32_t off = (uint32_t)(min(r, last) * ROWB + 16 * (cpos ^ (r & (CPR - 1))));
+      load_to_lds<16>(gbase, off, lb + 1024 * i);
+    }
+  };
+  wait_vmcnt<0>();                            // query and head weights
+  for (int g = 0; g < D - 1; ++g) issue(g);
+#pragma unroll 1
+  for (int g = 0; g < ng; ++g) {
+    wait_vmcnt<2 * (D - 2)>();                // this wave's loads of group g have landed
+    __syncthreads();                          // ... and every wave's; group g - 1 is consumed
+    issue(g + D - 1);                         // into group g - 1's slot
+    if (act) {
+      const uint8_t* rb = slot_of(g) + col * ROWB;
+      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 kb = *(const bf16x8*)(rb + 16 * ((8 * half + s) ^ (col & (CPR - 1))));
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], kb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], kb, acc1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 w0 = *(const f32x4*)(lw + 8 * rg + 4 * half);
+        const f32x4 w1 = *(const f32x4*)(lw + 32 + 8 * rg + 4 * half);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          part[u] = fmaf(w0[u], relu(acc0[4 * rg + u]), part[u]);
+          part[u] = fmaf(w1[u], relu(acc1[4 * rg + u]), part[u]);
+        }
+      }
+      const float psum = (part[0] + part[1]) + (part[2] + part[3]);
+      const float tot = psum + __shfl_xor(psum, 32, 64);
+      const int off = g * 32 + col;
+      if (half == 0 && off < len) {
+        const uint32_t key = float_to_key(tot);
+        kout[off] = key;
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+    }
+  }
+  wait_vmcnt<0>();                            // no load may still target the ring afterwards
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if (lane == 0) {
+    range[2 * wave] = kmin;
+    range[2 * wave + 1] = kmax;
+  }
+  __syncthreads();
 }
 
 __device__ __forceinline__ float load_elem(const void* base, int dt, int64_t i) {
@@ -1380,19 +1508,23 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
 // to it, to re-score each failing split and take its exact local Top-K.
 // ---------------------------------------------------------------------------------------
 // One work item: split j of query t (scoring, candidate emission, and the merge when it is
-// the query's last split to arrive).  Every return is uniform over the workgroup.
+// the query's last split to arrive).  With prescored the split's scores are already in
+// L.keys, klo0 and khi0 their smallest and largest key.  phase 1 stops after the arrival and
+// returns whether this workgroup must merge; phase 2 then does that merge (and the re-scoring
+// it may need); phase 0 does everything.  Every return is uniform over the workgroup.
 template <int MODE>
-__device__ __forceinline__ void run_item(const IndexerParams& p, int t, int j, const Lds& L,
-                                         const Lds& Lm) {
+__device__ __forceinline__ bool run_item(const IndexerParams& p, int t, int j, const Lds& L,
+                                         const Lds& Lm, bool prescored = false,
+                                         uint32_t klo0 = 0u, uint32_t khi0 = 0u, int phase = 0) {
   const int split = p.split;
   const int cap = min(split, p.K);
   const int V = min(p.q_vis[t], p.max_visible);
   if (V <= 0) {
     if (j == 0) pad_output(p, t, 0);
-    return;
+    return false;
   }
   const int nsplit = (V + split - 1) / split;
-  if (j >= nsplit) return;
+  if (j >= nsplit) return false;
   const int seq = p.q_seq[t];
   const int K_eff = min(p.K, V);
 
@@ -1425,10 +1557,32 @@ __device__ __forceinline__ void run_item(const IndexerParams& p, int t, int j, c
   uint32_t T = 0u;
   int gt = 0;
   bool enough = false;
+  // The next split that fails the merge's threshold after split `from`, or -1.  The headers
+  // are read again from the workspace: their LDS copy shares memory with the scorer's ring.
+  auto next_failing = [&](int from) {
+    int nxt = -1;
+    for (int jj = from + 1; jj < nsplit && nxt < 0; ++jj) {
+      const uint32_t tau = ld_agent(p.hdr + ((size_t)t * p.nsplit_max + jj) * kHdrWords + 1);
+      if (enough ? (tau > T) : (tau != 0u)) nxt = jj;
+    }
+    nxt = __builtin_amdgcn_readfirstlane(nxt);   // same value in every lane
+    wait_all_memory();
+    __syncthreads();
+    return nxt;
+  };
+  if (phase == 2) {
+    if (merge<MODE>(p, t, K_eff, nsplit, Lm, T, gt, enough)) return false;
+    refill = true;
+    cur = next_failing(-1);
+    if (cur < 0) {
+      merge<MODE>(p, t, K_eff, nsplit, Lm, T, gt, enough);   // certified
+      return false;
+    }
+  }
   for (;;) {
     const int start = cur * split, len = min(split, V - start);
-    uint32_t klo, khi;
-    score_split<MODE>(p, t, seq, start, len, L, gsp, klo, khi);
+    uint32_t klo = klo0, khi = khi0;
+    if (!prescored || refill) score_split<MODE>(p, t, seq, start, len, L, gsp, klo, khi);
 
     if (!refill) {
       if (nsplit == 1) {
@@ -1442,7 +1596,7 @@ __device__ __forceinline__ void run_item(const IndexerParams& p, int t, int j, c
                  },
                  L);
         pad_output(p, t, K_eff);
-        return;
+        return false;
       }
       // candidates of this split: every key at or above a threshold chosen so that a little
       // more than the split's expected share e of the Top-K survives
@@ -1494,8 +1648,9 @@ __device__ __forceinline__ void run_item(const IndexerParams& p, int t, int j, c
       if (threadIdx.x == 0)
         L.bcast[0] = add_agent(p.counters + t, 1u) == (uint32_t)(nsplit - 1);
       __syncthreads();
-      if (!L.bcast[0]) return;
-      if (merge<MODE>(p, t, K_eff, nsplit, Lm, T, gt, enough)) return;
+      if (!L.bcast[0]) return false;
+      if (phase == 1) return true;
+      if (merge<MODE>(p, t, K_eff, nsplit, Lm, T, gt, enough)) return false;
       refill = true;
       cur = -1;
     } else {
@@ -1520,25 +1675,80 @@ __device__ __forceinline__ void run_item(const IndexerParams& p, int t, int j, c
         st_agent(h + 4, khi);
       }
     }
-    // Next failing split, judged against the threshold the merge found.  The headers are
-    // read again from the workspace: their LDS copy shares memory with the scorer's ring.
-    int nxt = -1;
-    for (int jj = cur + 1; jj < nsplit && nxt < 0; ++jj) {
-      const uint32_t tau = ld_agent(p.hdr + ((size_t)t * p.nsplit_max + jj) * kHdrWords + 1);
-      if (enough ? (tau > T) : (tau != 0u)) nxt = jj;
-    }
-    nxt = __builtin_amdgcn_readfirstlane(nxt);   // same value in every lane
-    wait_all_memory();
-    __syncthreads();
+    // Next failing split, judged against the threshold the merge found.
+    const int nxt = next_failing(cur);
     if (nxt < 0) {
       merge<MODE>(p, t, K_eff, nsplit, Lm, T, gt, enough);   // certified
-      return;
+      return false;
     }
     cur = nxt;
   }
 }
 
+// Work item (tile b of kMqQ consecutive queries, split j).  When two or more of the tile's
+// queries have a split j and all of those read one sequence, score_mq scores them together
+// and each then takes the rest of its split's steps in turn from its own scores; otherwise
+// (and for queries without split j, which only pad their output or return) every query takes
+// the single-query path.
 template <int MODE>
+__device__ __forceinline__ void run_tile(const IndexerParams& p, int b, int j, const Lds& L,
+                                         const Lds& Lm, uint32_t* keys_mq, uint32_t* range_mq) {
+  const int split = p.split, start = j * split;
+  int tq[kMqQ], lens[kMqQ];
+  int nq = 0, seq = -1, lenmax = 0;
+  bool same = true;
+  for (int i = 0; i < kMqQ; ++i) {
+    const int t = kMqQ * b + i;
+    if (t >= p.T) break;
+    const int V = min(p.q_vis[t], p.max_visible);
+    if (V <= start) continue;                 // no split j (or nothing visible)
+    const int s = p.q_seq[t];
+    if (nq > 0 && s != seq) same = false;
+    seq = s;
+    tq[nq] = t;
+    lens[nq] = min(split, V - start);
+    lenmax = max(lenmax, lens[nq]);
+    ++nq;
+  }
+  for (int i = nq; i < kMqQ; ++i) tq[i] = lens[i] = 0;
+  if (same && nq >= 2) {
+    uint32_t* const keys[kMqQ] = {L.keys, keys_mq, keys_mq + kSplitMax, keys_mq + 2 * kSplitMax};
+    if (p.L.bt) score_mq<true>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
+    else score_mq<false>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
+    // every query's selection and emission first: a merge (and its re-scoring) takes the
+    // whole region, where the other queries' scores are
+    bool must_merge[kMqQ];
+    for (int i = 0; i < nq; ++i) {
+      Lds Lq = L;
+      Lq.keys = keys[i];
+      must_merge[i] = run_item<MODE>(p, tq[i], j, Lq, Lm, true, range_mq[2 * i],
+                                     range_mq[2 * i + 1], 1);
+      __syncthreads();
+    }
+    for (int i = 0; i < nq; ++i)
+      if (must_merge[i]) {
+        run_item<MODE>(p, tq[i], j, L, Lm, false, 0u, 0u, 2);
+        __syncthreads();
+      }
+    for (int i = 0; i < kMqQ; ++i) {          // queries without split j
+      const int t = kMqQ * b + i;
+      if (t < p.T && min(p.q_vis[t], p.max_visible) <= start) {
+        run_item<MODE>(p, t, j, L, Lm);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+  for (int i = 0; i < kMqQ; ++i) {
+    const int t = kMqQ * b + i;
+    if (t < p.T) {
+      run_item<MODE>(p, t, j, L, Lm);
+      __syncthreads();
+    }
+  }
+}
+
+template <int MODE, int QT = 1>
 __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   constexpr int RB = region_bytes<MODE>();
   static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kNSplitMax + 4, "shared region");
@@ -1566,6 +1776,18 @@ __global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
   L.small = s_small;
   Lds Lm = L;
   Lm.hist = (int*)s_keys;
+  if constexpr (QT > 1) {
+    // one item (tile of QT queries, split j) per workgroup, j-major with the tiles rotated
+    // by j as the queries are below
+    static_assert(QT == kMqQ && QT == NWAVE && MODE == 1, "multi-query tiles: bf16 keys");
+    uint32_t* const s_keys_mq = (uint32_t*)(s_region + kMqKeysOff);
+    __shared__ uint32_t s_range_mq[2 * QT];
+    const int ntiles = (p.T + QT - 1) / QT;
+    const int item = blockIdx.x;
+    const int j = item / ntiles, b = (item - j * ntiles + j) % ntiles;
+    run_tile<MODE>(p, b, j, L, Lm, s_keys_mq, s_range_mq);
+    return;
+  }
 
   // Work items (query t, split j).  Compact launch: the items, query-major, are numbered from
   // the queries' split counts, and workgroup i takes items i, i + grid, ... so that a grid
@@ -1664,11 +1886,23 @@ size_t indexer_workspace_bytes(int32_t T, int32_t max_visible, int32_t top_k) {
   return b;
 }
 
+// Multi-query tiles for many queries with bf16 keys (chunked prefill: thousands of queries
+// over one cached context); DSA_INDEXER_MQ=0 turns them off for measurement.
+bool indexer_multi_query(const IndexerParams& p) {
+  if (p.k_dtype != kDtBF16 || p.compact || p.T < kMqMinT) return false;
+  const char* e = getenv("DSA_INDEXER_MQ");
+  return !(e && atoi(e) == 0);
+}
+
 hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream) {
   const dim3 grid(p.grid), block(NT);
   if (!fast_path) hipLaunchKernelGGL(indexer_topk_kernel<0>, grid, block, 0, stream, p);
   else if (p.k_dtype == kDtFP8) hipLaunchKernelGGL(indexer_topk_kernel<2>, grid, block, 0, stream, p);
   else if (p.k_dtype == kDtMX) hipLaunchKernelGGL(indexer_topk_kernel<3>, grid, block, 0, stream, p);
+  else if (indexer_multi_query(p)) {
+    const dim3 g(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
+    hipLaunchKernelGGL((indexer_topk_kernel<1, kMqQ>), g, block, 0, stream, p);
+  }
   else hipLaunchKernelGGL(indexer_topk_kernel<1>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
