@@ -353,9 +353,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(sharding across GPUs is described in DESIGN.md, not implemented).",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (a causal chunk "
+              "can be sharded across devices with dsa_zigzag_ranges; --shards times each "
+              "shard's share on this GPU).", file=sys.stderr)
         sys.exit(2)
 
     import torch
