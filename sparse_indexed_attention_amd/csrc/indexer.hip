@@ -1135,7 +1135,7 @@ __device__ __forceinline__ int run_slot(const uint32_t* pre, int nsplit, int rs,
 
 // Copies the virtual list (n entries, a multiple of 4) into LDS: keys to lk and, when lp is not
 // null, positions to lp, with agent-scope direct-to-LDS loads of 16 bytes per lane.  Every run
-// takes whole 4-entry chunks.  Long runs (64 entries or more on average) are copied one run
+// takes whole 4-entry chunks.  Long runs (48 entries or more on average) are copied one run
 // per load (lane l: chunk l of the run; wave w copies runs w, w + 4, ...).  Short runs would
 // leave most lanes of such a load idle, so then a load fills 64 consecutive chunks of the list
 // instead, each lane finding its chunk's run by binary search.
@@ -1152,7 +1152,7 @@ __device__ __forceinline__ void stage_runs(const uint32_t* gk, const int32_t* gp
       issued = 40;
     }
   };
-  if (n >= 64 * nsplit) {
+  if (n >= 48 * nsplit) {
     for (int r0 = wave; r0 < nsplit; r0 += 64 * NWAVE) {
       // lane l: the bounds of run r0 + 4 l
       const int rl = min(r0 + NWAVE * lane, nsplit - 1);
