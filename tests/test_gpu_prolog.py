@@ -110,3 +110,57 @@ def test_prolog_matches_oracle(dsa, case):
             sc = ks.cpu().numpy()
             assert np.array_equal(sc[slot_np], s)
             assert np.all(sc[others] == SENTINEL) and np.all(pool_np[others] == SENTINEL)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8"])
+def test_prolog_feeds_the_indexer(dsa, fmt):
+    """A prefill chunk end to end: the prolog projects the chunk's hidden vectors and writes
+    their keys into the paged cache after a prefix, then the indexer scores the chunk's
+    queries (the prolog's q and head weights) causally over prefix and chunk.  The oracle
+    gets the same cache by quantizing the keys the prolog returned (its bytes must equal the
+    GPU's) and the same q and w, and its Top-K must match the indexer's."""
+    import dataclasses
+    import torch
+    from synth import make_inputs
+    from synth.configs import Spec
+    from synth.device import bits_of, to_device
+    from tests.gpu_util import run_indexer, score_error
+    from tests.helpers import rows_of
+    P, L, H, D = 6000, 300, 64, 128
+    spec = Spec(name=f"prolog_chunk_{fmt}", seq_lens=(P + L,), q_seq=(0,) * L,
+                q_visible=tuple(P + i + 1 for i in range(L)),
+                k_dtype="fp8" if fmt == "fp8" else "f32", k_std=1.0)
+    inp = make_inputs(spec, seed=61, with_sfa=False)
+    if fmt == "mxfp8":
+        with np.errstate(invalid="ignore"):
+            codes, sb = oracle.quantize_mxfp8(inp.k_pool)
+        inp = dataclasses.replace(inp, spec=dataclasses.replace(spec, k_dtype="mxfp8"),
+                                  k_pool=codes, k_scale=sb)
+    d = to_device(inp)
+    pi = make_prolog_inputs(L, 1024, H, D, seed=62)
+    x = torch.from_numpy(pi.x.view(np.int16)).cuda().view(torch.bfloat16)
+    W = torch.from_numpy(pi.w_proj.view(np.int16)).cuda().view(torch.bfloat16)
+    g = torch.from_numpy(pi.gain).cuda()
+    slots = rows_of(inp, 0, np.arange(P, P + L)).astype(np.int64)
+    q, w, k = dsa.indexer_prolog(x, W, g, pi.eps, H, D, slot=torch.from_numpy(slots).cuda(),
+                                 k_pool=d.k_pool, k_scale=d.k_scale, want_k=True)
+    torch.cuda.synchronize()
+    k_np = k.cpu().numpy()
+    if fmt == "fp8":
+        c, s = oracle.quantize_fp8_per_token(k_np)
+    else:
+        c, s = oracle.quantize_mxfp8(k_np)
+    assert np.array_equal(d.k_pool.cpu().numpy()[slots], c)
+    assert np.array_equal(d.k_scale.cpu().numpy()[slots].view(np.uint8), s.view(np.uint8))
+    inp.k_pool[slots], inp.k_scale[slots] = c, s
+    inp.q_idx[...] = bits_of(q)
+    inp.w[...] = w.cpu().numpy()
+    d.q_idx, d.w = q, w
+    idx, score = run_indexer(dsa, inp, d)
+    sample = [0, 1, 150, 298, 299]
+    refs = oracle.indexer_topk(inp, sample)
+    res = oracle.check_topk(idx, refs)
+    err = max(score_error(score[r.t], idx[r.t], r) for r in refs)
+    log(f"  prolog -> indexer ({fmt}): score err {err:.2e}")
+    assert res.ok, res.msgs[:5]
+    assert err <= 2e-6
