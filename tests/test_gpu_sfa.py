@@ -123,7 +123,7 @@ def test_end_to_end_indexer_then_sfa(dsa):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("n", [2, 4])
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
 def test_full_size_end_to_end_sampled(dsa, n):
     inp = make_inputs(workload(n), seed=n)
     idx, score = run_indexer(dsa, inp)
