@@ -1748,8 +1748,10 @@ __device__ __forceinline__ void run_tile(const IndexerParams& p, int b, int j, c
   }
 }
 
+// The reference path (MODE 0) keeps its fp32 query in LDS and fits one workgroup per CU; the
+// MFMA paths fit two.
 template <int MODE, int QT = 1>
-__global__ __launch_bounds__(NT, 2) void indexer_topk_kernel(IndexerParams p) {
+__global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(IndexerParams p) {
   constexpr int RB = region_bytes<MODE>();
   static_assert(RB >= kBins * 4 && flat_words<MODE>() >= kNSplitMax + 4, "shared region");
   __shared__ __attribute__((aligned(16))) uint8_t s_region[RB];
