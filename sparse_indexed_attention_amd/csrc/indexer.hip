@@ -1510,8 +1510,9 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
 // One work item: split j of query t (scoring, candidate emission, and the merge when it is
 // the query's last split to arrive).  With prescored the split's scores are already in
 // L.keys, klo0 and khi0 their smallest and largest key.  phase 1 stops after the arrival and
-// returns whether this workgroup must merge; phase 2 then does that merge (and the re-scoring
-// it may need); phase 0 does everything.  Every return is uniform over the workgroup.
+// returns whether this workgroup must merge; phase 3 stops before it (the caller drains the
+// stores and arrives); phase 2 does the merge (and the re-scoring it may need); phase 0 does
+// everything.  Every return is uniform over the workgroup.
 template <int MODE>
 __device__ __forceinline__ bool run_item(const IndexerParams& p, int t, int j, const Lds& L,
                                          const Lds& Lm, bool prescored = false,
@@ -1643,6 +1644,7 @@ __device__ __forceinline__ bool run_item(const IndexerParams& p, int t, int j, c
         }
       }
       // arrival: the last split of this query to arrive merges
+      if (phase == 3) return false;
       wait_all_memory();
       __syncthreads();
       if (threadIdx.x == 0)
@@ -1716,15 +1718,27 @@ __device__ __forceinline__ void run_tile(const IndexerParams& p, int b, int j, c
     if (p.L.bt) score_mq<true>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
     else score_mq<false>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
     // every query's selection and emission first: a merge (and its re-scoring) takes the
-    // whole region, where the other queries' scores are
-    bool must_merge[kMqQ];
+    // whole region, where the other queries' scores are.  The candidate stores of all of them
+    // are drained once, then the queries arrive together.
     for (int i = 0; i < nq; ++i) {
       Lds Lq = L;
       Lq.keys = keys[i];
-      must_merge[i] = run_item<MODE>(p, tq[i], j, Lq, Lm, true, range_mq[2 * i],
-                                     range_mq[2 * i + 1], 1);
+      run_item<MODE>(p, tq[i], j, Lq, Lm, true, range_mq[2 * i], range_mq[2 * i + 1], 3);
       __syncthreads();
     }
+    wait_all_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int i = 0; i < nq; ++i) {
+        const int V = min(p.q_vis[tq[i]], p.max_visible);
+        const int ns = (V + split - 1) / split;
+        L.bcast[i] = ns > 1 && add_agent(p.counters + tq[i], 1u) == (uint32_t)(ns - 1);
+      }
+    }
+    __syncthreads();
+    bool must_merge[kMqQ];
+    for (int i = 0; i < kMqQ; ++i) must_merge[i] = i < nq && L.bcast[i];
+    __syncthreads();
     for (int i = 0; i < nq; ++i)
       if (must_merge[i]) {
         run_item<MODE>(p, tq[i], j, L, Lm, false, 0u, 0u, 2);
