@@ -406,17 +406,18 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
   wait_vmcnt<0>();                            // no load may still target the ring afterwards
 }
 
-// Multi-query scoring (bf16 keys, kMqQ queries of one sequence over one split, as in a
+// Multi-query scoring (bf16 or fp8 keys, kMqQ queries of one sequence over one split, as in a
 // prefill chunk whose queries share the cached context).  Scoring one query per workgroup
 // re-reads the split's keys for every query through a two-slot ring per wave, and is then
 // bound by the latency of those loads.  Here the waves share one ring of kMqRing key groups
-// (kMqRing - 1 in flight) filled once for all the queries: every wave issues two of a
-// group's eight direct-to-LDS loads, and one barrier per group makes the group visible to all
-// waves and frees the slot of the previous one.  Wave w then scores query w with the same
+// (kMqRing - 1 in flight) filled once for all the queries: every wave issues two of a bf16
+// group's eight direct-to-LDS loads (fp8: one of four, plus a copy of the group's 32 token
+// scales, the same bytes from every wave), and one barrier per group makes the group visible
+// to all waves and frees the slot of the previous one.  Wave w then scores query w with the same
 // MFMA steps as score_mfma, into its own key array.  Waves without a query (nq < kMqQ) still
 // load and pass the barriers.  Group indices past the split are clamped onto its last group,
 // so that every step issues the same loads and the waits stay exact.
-template <bool PAGED>
+template <bool FP8, bool PAGED>
 __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)[kMqQ], int nq,
                                          int seq, int start, int lenmax, const int (&lens)[kMqQ],
                                          uint32_t* const (&keys)[kMqQ], const Lds& L,
@@ -424,9 +425,17 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
-  constexpr int ROWB = 256, CPR = 16, RPI = 4, LPR = 16;
+  constexpr int ROWB = FP8 ? 128 : 256;       // bytes per key row
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;            // rows per load instruction
+  constexpr int LPR = 64 / RPI;               // lanes per row in a load instruction
+  constexpr int GB = 32 * ROWB;               // key bytes per group
+  constexpr int KPW = GB / 1024 / NWAVE;      // key loads per wave and group
+  constexpr int LPW = KPW + (FP8 ? 1 : 0);    // loads per wave and group
   constexpr int D = kMqRing, SLOT = 8192;
-  static_assert(kMqRingOff + D * SLOT <= region_bytes<1>(), "ring size");
+  static_assert(GB + (FP8 ? 256 : 0) <= SLOT && KPW >= 1, "slot size");
+  static_assert(kMqRingOff + D * SLOT <= region_bytes<1>() &&
+                kMqRingOff + D * SLOT <= region_bytes<2>(), "ring size");
   static_assert(kMqKeysOff + (kMqQ - 1) * kSplitMax * 4 <= kMqRingOff, "scores below the ring");
   static_assert(kSplitMax / 32 <= 64, "one lane per group of the split");
   seq = __builtin_amdgcn_readfirstlane(seq);
@@ -470,26 +479,40 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
     const uint8_t* gbase = kbytes + row0 * ROWB;
     const uint32_t lb = lds_addr(sb);
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * wave + ii;
+    for (int ii = 0; ii < KPW; ++ii) {
+      const int i = KPW * wave + ii;
       const int r = RPI * i + lane / LPR;
       const uint32_t off = (uint32_t)(min(r, last) * ROWB + 16 * (cpos ^ (r & (CPR - 1))));
       load_to_lds<16>(gbase, off, lb + 1024 * i);
     }
+    if constexpr (FP8) load_to_lds<4>(p.k_scale + row0, 4u * (uint32_t)min(col, last), lb + GB);
   };
   wait_vmcnt<0>();                            // query and head weights
   for (int g = 0; g < D - 1; ++g) issue(g);
 #pragma unroll 1
   for (int g = 0; g < ng; ++g) {
-    wait_vmcnt<2 * (D - 2)>();                // this wave's loads of group g have landed
+    wait_vmcnt<LPW * (D - 2)>();              // this wave's loads of group g have landed
     __syncthreads();                          // ... and every wave's; group g - 1 is consumed
     issue(g + D - 1);                         // into group g - 1's slot
     if (act) {
-      const uint8_t* rb = slot_of(g) + col * ROWB;
+      const uint8_t* sb = slot_of(g);
+      const uint8_t* rb = sb + col * ROWB;
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 kb = *(const bf16x8*)(rb + 16 * ((8 * half + s) ^ (col & (CPR - 1))));
+        bf16x8 kb;
+        if constexpr (FP8) {
+          const u32x4 v = *(const u32x4*)(rb + 16 * ((4 * half + (s >> 1)) ^ (col & (CPR - 1))));
+          const uint32_t lo = (s & 1) ? v.z : v.x;
+          const uint32_t hi = (s & 1) ? v.w : v.y;
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+          kb = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        } else {
+          kb = *(const bf16x8*)(rb + 16 * ((8 * half + s) ^ (col & (CPR - 1))));
+        }
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], kb, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], kb, acc1, 0, 0, 0);
       }
@@ -506,7 +529,8 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
         }
       }
       const float psum = (part[0] + part[1]) + (part[2] + part[3]);
-      const float tot = psum + __shfl_xor(psum, 32, 64);
+      float tot = psum + __shfl_xor(psum, 32, 64);
+      if constexpr (FP8) tot *= *(const float*)(sb + GB + 4 * col);
       const int off = g * 32 + col;
       if (half == 0 && off < len) {
         const uint32_t key = float_to_key(tot);
@@ -1715,8 +1739,8 @@ __device__ __forceinline__ void run_tile(const IndexerParams& p, int b, int j, c
   for (int i = nq; i < kMqQ; ++i) tq[i] = lens[i] = 0;
   if (same && nq >= 2) {
     uint32_t* const keys[kMqQ] = {L.keys, keys_mq, keys_mq + kSplitMax, keys_mq + 2 * kSplitMax};
-    if (p.L.bt) score_mq<true>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
-    else score_mq<false>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
+    if (p.L.bt) score_mq<MODE == 2, true>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
+    else score_mq<MODE == 2, false>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
     // every query's selection and emission first: a merge (and its re-scoring) takes the
     // whole region, where the other queries' scores are.  The candidate stores of all of them
     // are drained once, then the queries arrive together.
@@ -1795,7 +1819,8 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(Ind
   if constexpr (QT > 1) {
     // one item (tile of QT queries, split j) per workgroup, j-major with the tiles rotated
     // by j as the queries are below
-    static_assert(QT == kMqQ && QT == NWAVE && MODE == 1, "multi-query tiles: bf16 keys");
+    static_assert(QT == kMqQ && QT == NWAVE && (MODE == 1 || MODE == 2),
+                  "multi-query tiles: bf16 or fp8 keys");
     uint32_t* const s_keys_mq = (uint32_t*)(s_region + kMqKeysOff);
     __shared__ uint32_t s_range_mq[2 * QT];
     const int ntiles = (p.T + QT - 1) / QT;
@@ -1902,10 +1927,10 @@ size_t indexer_workspace_bytes(int32_t T, int32_t max_visible, int32_t top_k) {
   return b;
 }
 
-// Multi-query tiles for many queries with bf16 keys (chunked prefill: thousands of queries
-// over one cached context); DSA_INDEXER_MQ=0 turns them off for measurement.
+// Multi-query tiles for many queries with bf16 or fp8 keys (chunked prefill: thousands of
+// queries over one cached context); DSA_INDEXER_MQ=0 turns them off for measurement.
 bool indexer_multi_query(const IndexerParams& p) {
-  if (p.k_dtype != kDtBF16 || p.compact || p.T < kMqMinT) return false;
+  if ((p.k_dtype != kDtBF16 && p.k_dtype != kDtFP8) || p.compact || p.T < kMqMinT) return false;
   const char* e = getenv("DSA_INDEXER_MQ");
   return !(e && atoi(e) == 0);
 }
@@ -1913,7 +1938,14 @@ bool indexer_multi_query(const IndexerParams& p) {
 hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream) {
   const dim3 grid(p.grid), block(NT);
   if (!fast_path) hipLaunchKernelGGL(indexer_topk_kernel<0>, grid, block, 0, stream, p);
-  else if (p.k_dtype == kDtFP8) hipLaunchKernelGGL(indexer_topk_kernel<2>, grid, block, 0, stream, p);
+  else if (p.k_dtype == kDtFP8) {
+    if (indexer_multi_query(p)) {
+      const dim3 g(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
+      hipLaunchKernelGGL((indexer_topk_kernel<2, kMqQ>), g, block, 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(indexer_topk_kernel<2>, grid, block, 0, stream, p);
+    }
+  }
   else if (p.k_dtype == kDtMX) hipLaunchKernelGGL(indexer_topk_kernel<3>, grid, block, 0, stream, p);
   else if (indexer_multi_query(p)) {
     const dim3 g(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));

@@ -1,6 +1,6 @@
-"""GPU parity of the indexer's multi-query workgroups (many queries with bf16 keys, as in a
-chunked prefill: four queries of one sequence scored together over each split), through the
-C ABI.  Same tolerance as the single-query suites; and the multi-query launch must give
+"""GPU parity of the indexer's multi-query workgroups (many queries with bf16 or fp8 keys, as
+in a chunked prefill: four queries of one sequence scored together over each split), through
+the C ABI.  Same tolerance as the single-query suites; and the multi-query launch must give
 bit-identical results to the single-query one (DSA_INDEXER_MQ=0), since every score is the
 same MFMA sum whichever workgroup computes it."""
 import os
@@ -23,7 +23,7 @@ def chunk(L, P, **kw):
                 q_visible=tuple(P + i + 1 for i in range(L)), **kw)
 
 
-def mixed(n_seqs, per_seq, lens):
+def mixed(n_seqs, per_seq, lens, **kw):
     """Queries interleaved over sequences (q_seq = i % n_seqs), so tiles mix sequences."""
     q_seq, q_vis = [], []
     for i in range(n_seqs * per_seq):
@@ -40,6 +40,10 @@ CASES = {
     "contiguous_chunk": lambda: chunk(300, 5000, block_size=0, permute=False, extra_blocks=0),
     "bs32_chunk": lambda: chunk(280, 4100, block_size=32),
     "mixed_sequences": lambda: mixed(7, 40, [5000, 3000, 8000, 700, 64, 2049, 4500]),
+    # fp8 keys with per-token scales (the quantized prefill path)
+    "fp8_causal_chunk_600": lambda: chunk(600, 7000, k_dtype="fp8", k_std=1.0),
+    "fp8_no_prefix_523": lambda: chunk(523, 0, k_dtype="fp8", k_std=1.0),
+    "fp8_bs32_chunk": lambda: chunk(300, 3000, k_dtype="fp8", k_std=1.0, block_size=32),
 }
 
 
