@@ -44,6 +44,8 @@ CASES = {
     "fp8_causal_chunk_600": lambda: chunk(600, 7000, k_dtype="fp8", k_std=1.0),
     "fp8_no_prefix_523": lambda: chunk(523, 0, k_dtype="fp8", k_std=1.0),
     "fp8_bs32_chunk": lambda: chunk(300, 3000, k_dtype="fp8", k_std=1.0, block_size=32),
+    "fp8_contiguous_chunk": lambda: chunk(260, 4000, k_dtype="fp8", k_std=1.0, block_size=0,
+                                          permute=False, extra_blocks=0),
 }
 
 
