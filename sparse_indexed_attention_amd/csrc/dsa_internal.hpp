@@ -23,7 +23,7 @@ constexpr int kGenericMaxHeads = 256;
 enum { kDtF32 = 0, kDtBF16 = 1, kDtFP8 = 2, kDtMX = 3 };
 
 struct IndexerPlan {
-  int32_t grid;         // workgroups of the launch
+  int32_t grid;         // workgroups of the launch (a multi-query launch takes nsplit_max * ceil(T / 4))
   int32_t split;        // positions per context split (multiple of 64)
   int32_t nsplit_max;   // splits of the longest visible prefix (header rows per query)
   int32_t cap;          // candidates per split at most = min(split, top_k)

@@ -10,7 +10,11 @@
 // scores never leave the registers and the per-position scores stay in LDS.
 //
 // Work decomposition (MI355X: 256 CUs in 8 XCDs, wave64, 160 KB LDS per CU):
-//   * one workgroup of 4 waves per (query, context split of `split` positions);
+//   * one workgroup of 4 waves per (query, context split of `split` positions), two per CU.
+//     With the host's total of the visible lengths and at most 64 queries the splits are
+//     sized so that the live items fit the resident slots and the grid numbers only live
+//     items; with many queries and bf16 or fp8 keys (chunked prefill) a workgroup takes four
+//     queries of one sequence over one split instead (see score_mq);
 //   * scoring: each wave takes a contiguous run of 32-position groups.  Key bytes travel
 //     HBM -> LDS with fully coalesced direct-to-LDS loads into a per-wave ring of groups.  Per
 //     group, one v_mfma_f32_32x32x16_bf16 chain per 32-head half computes x[head, position]
