@@ -45,6 +45,11 @@ CASES = {
     # MFMA path, fp8 keys with per-token scales
     "fp8_mixed": lambda: scaled_spec(workload(4), seq_lens=[20000, 3333, 2049, 65, 1]),
     "fp8_k256": lambda: scaled_spec(workload(4), seq_lens=[30000, 70000], top_k=256),
+    # 65..255 queries: the rectangular launch even with the host's total (no compact, no tiles)
+    "bf16_T100_ragged": lambda: scaled_spec(workload(2), seq_lens=[int(x) for x in
+                                            np.random.default_rng(100).integers(1, 9000, 100)]),
+    "fp8_T200_ragged": lambda: scaled_spec(workload(4), seq_lens=[int(x) for x in
+                                           np.random.default_rng(200).integers(1, 5000, 200)]),
     # degenerate Top-K sizes on the fast path: K = 1, and K >= V (every position selected)
     "fp8_k1": lambda: scaled_spec(workload(4), seq_lens=[5000, 1, 70, 2049], top_k=1),
     "bf16_k_all": lambda: scaled_spec(workload(2), seq_lens=[100, 2048, 700, 1]),
