@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from synth import make_inputs, scaled_spec, workload
+from synth.configs import Spec
 from synth.device import to_device
 from tests.gpu_util import log, run_indexer, score_error
 from tests.helpers import rows_of
@@ -93,6 +94,10 @@ CASES = {
     "ref_f32q": lambda: scaled_spec(workload(4), seq_lens=[3000], k_dtype="f32", q_dtype="f32"),
     "ref_h8_d64": lambda: scaled_spec(workload(4), seq_lens=[2000, 900], k_dtype="f32",
                                       idx_heads=8, idx_dim=64, top_k=100),
+    # a chunk of 300 new queries over a 6000-token prefix (many queries, one sequence)
+    "prefill_chunk_300": lambda: Spec(name="mx_chunk", seq_lens=(6300,), q_seq=(0,) * 300,
+                                      q_visible=tuple(6000 + i + 1 for i in range(300)),
+                                      k_dtype="f32", k_std=1.0),
 }
 
 
