@@ -410,7 +410,7 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
   wait_vmcnt<0>();                            // no load may still target the ring afterwards
 }
 
-// Multi-query scoring (bf16 or fp8 keys, kMqQ queries of one sequence over one split, as in a
+// Multi-query scoring (bf16, fp8 or MXFP8 keys, kMqQ queries of one sequence over one split, as in a
 // prefill chunk whose queries share the cached context).  Scoring one query per workgroup
 // re-reads the split's keys for every query through a two-slot ring per wave, and is then
 // bound by the latency of those loads.  Here the waves share one ring of kMqRing key groups
@@ -420,8 +420,11 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
 // to all waves and frees the slot of the previous one.  Wave w then scores query w with the same
 // MFMA steps as score_mfma, into its own key array.  Waves without a query (nq < kMqQ) still
 // load and pass the barriers.  Group indices past the split are clamped onto its last group,
-// so that every step issues the same loads and the waits stay exact.
-template <bool FP8, bool PAGED>
+// so that every step issues the same loads and the waits stay exact.  MXFP8 keys (MX) move
+// like fp8 keys with their rows' scale bytes, are widened with their group's power-of-two
+// scale, and the workgroup first quantizes all the tile's queries to MXFP8 into the free
+// region, from which each wave loads its own dequantized query.
+template <bool FP8, bool PAGED, bool MX = false>
 __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)[kMqQ], int nq,
                                          int seq, int start, int lenmax, const int (&lens)[kMqQ],
                                          uint32_t* const (&keys)[kMqQ], const Lds& L,
@@ -439,7 +442,9 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
   constexpr int D = kMqRing, SLOT = 8192;
   static_assert(GB + (FP8 ? 256 : 0) <= SLOT && KPW >= 1, "slot size");
   static_assert(kMqRingOff + D * SLOT <= region_bytes<1>() &&
-                kMqRingOff + D * SLOT <= region_bytes<2>(), "ring size");
+                kMqRingOff + D * SLOT <= region_bytes<2>() &&
+                kMqRingOff + D * SLOT <= region_bytes<3>(), "ring size");
+  static_assert(kMqQ * 64 * 128 * 2 <= region_bytes<3>(), "the tile's MXFP8 queries fit the region");
   static_assert(kMqKeysOff + (kMqQ - 1) * kSplitMax * 4 <= kMqRingOff, "scores below the ring");
   static_assert(kSplitMax / 32 <= 64, "one lane per group of the split");
   seq = __builtin_amdgcn_readfirstlane(seq);
@@ -452,12 +457,45 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
   uint32_t* const kout = keys[act ? wave : 0];
 
   const uint16_t* qb = (const uint16_t*)p.q + (size_t)t * (64 * 128);
+  if constexpr (MX) {
+    // query i's group g (head g / 4, dims 32 (g % 4) ..) is quantized by thread g of round i
+    // and stored dequantized (exact in bf16 for scale bytes >= 3) at region + 16 KB i
+    static_assert(NT == 64 * 4, "one thread per group of a query");
+    for (int i = 0; i < kMqQ; ++i) {
+      const int ti = i < nq ? tq[i] : tq[0];
+      const uint16_t* src = (const uint16_t*)p.q + (size_t)ti * (64 * 128) +
+                            (threadIdx.x >> 2) * 128 + 32 * (threadIdx.x & 3);
+      uint16_t* dst = (uint16_t*)(L.region + 16384 * i) + (threadIdx.x >> 2) * 128 +
+                      32 * (threadIdx.x & 3);
+      bf16x8 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *(const bf16x8*)(src + 8 * u);
+      float amax = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[u][e]));
+      const uint32_t sbyte = mx_scale_byte(amax);
+      const float inv = mx_inv_scale(sbyte), sc = mx_scale_f32(sbyte);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bf16x8 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          r[e] = (__bf16)(fp8_e4m3_to_f32(f32_to_fp8_e4m3_nb((float)v[u][e] * inv)) * sc);
+        *(bf16x8*)(dst + 8 * u) = r;
+      }
+    }
+    __syncthreads();
+  }
+  const uint16_t* qsrc = MX ? (const uint16_t*)(L.region + 16384 * (act ? wave : 0)) : qb;
   bf16x8 a0[8], a1[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    a0[s] = *(const bf16x8*)(qb + col * 128 + half * 64 + 8 * s);
-    a1[s] = *(const bf16x8*)(qb + (32 + col) * 128 + half * 64 + 8 * s);
+    a0[s] = *(const bf16x8*)(qsrc + col * 128 + half * 64 + 8 * s);
+    a1[s] = *(const bf16x8*)(qsrc + (32 + col) * 128 + half * 64 + 8 * s);
   }
+  if constexpr (MX) __syncthreads();          // every wave holds its query; the ring may start
   const float* lw = L.w + wave * 64;
   load_to_lds<4>(p.w + (size_t)t * 64, 4u * lane, lds_addr(lw));
   int gblk = 0;
@@ -501,18 +539,23 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
     if (act) {
       const uint8_t* sb = slot_of(g);
       const uint8_t* rb = sb + col * ROWB;
+      // MXFP8: this lane's two groups 2 half, 2 half + 1 (k steps 0..3, 4..7)
+      const uint32_t sw = MX ? *(const uint32_t*)(sb + GB + 4 * col) >> (16 * half) : 0u;
+      const float xs0 = MX ? mx_scale_f32(sw & 255u) : 1.0f;
+      const float xs1 = MX ? mx_scale_f32((sw >> 8) & 255u) : 1.0f;
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         bf16x8 kb;
         if constexpr (FP8) {
+          const float xs = s < 4 ? xs0 : xs1;
           const u32x4 v = *(const u32x4*)(rb + 16 * ((4 * half + (s >> 1)) ^ (col & (CPR - 1))));
           const uint32_t lo = (s & 1) ? v.z : v.x;
           const uint32_t hi = (s & 1) ? v.w : v.y;
-          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, xs, false);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, xs, true);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, xs, false);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, xs, true);
           kb = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
         } else {
           kb = *(const bf16x8*)(rb + 16 * ((8 * half + s) ^ (col & (CPR - 1))));
@@ -534,7 +577,7 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
       }
       const float psum = (part[0] + part[1]) + (part[2] + part[3]);
       float tot = psum + __shfl_xor(psum, 32, 64);
-      if constexpr (FP8) tot *= *(const float*)(sb + GB + 4 * col);
+      if constexpr (FP8 && !MX) tot *= *(const float*)(sb + GB + 4 * col);
       const int off = g * 32 + col;
       if (half == 0 && off < len) {
         const uint32_t key = float_to_key(tot);
@@ -1743,8 +1786,9 @@ __device__ __forceinline__ void run_tile(const IndexerParams& p, int b, int j, c
   for (int i = nq; i < kMqQ; ++i) tq[i] = lens[i] = 0;
   if (same && nq >= 2) {
     uint32_t* const keys[kMqQ] = {L.keys, keys_mq, keys_mq + kSplitMax, keys_mq + 2 * kSplitMax};
-    if (p.L.bt) score_mq<MODE == 2, true>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
-    else score_mq<MODE == 2, false>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
+    constexpr bool F8 = MODE >= 2, MXK = MODE == 3;
+    if (p.L.bt) score_mq<F8, true, MXK>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
+    else score_mq<F8, false, MXK>(p, tq, nq, seq, start, lenmax, lens, keys, L, range_mq);
     // every query's selection and emission first: a merge (and its re-scoring) takes the
     // whole region, where the other queries' scores are.  The candidate stores of all of them
     // are drained once, then the queries arrive together.
@@ -1823,8 +1867,7 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(Ind
   if constexpr (QT > 1) {
     // one item (tile of QT queries, split j) per workgroup, j-major with the tiles rotated
     // by j as the queries are below
-    static_assert(QT == kMqQ && QT == NWAVE && (MODE == 1 || MODE == 2),
-                  "multi-query tiles: bf16 or fp8 keys");
+    static_assert(QT == kMqQ && QT == NWAVE && MODE >= 1, "multi-query tiles: MFMA paths");
     uint32_t* const s_keys_mq = (uint32_t*)(s_region + kMqKeysOff);
     __shared__ uint32_t s_range_mq[2 * QT];
     const int ntiles = (p.T + QT - 1) / QT;
@@ -1931,10 +1974,10 @@ size_t indexer_workspace_bytes(int32_t T, int32_t max_visible, int32_t top_k) {
   return b;
 }
 
-// Multi-query tiles for many queries with bf16 or fp8 keys (chunked prefill: thousands of
-// queries over one cached context); DSA_INDEXER_MQ=0 turns them off for measurement.
+// Multi-query tiles for many queries on the MFMA paths (chunked prefill: thousands of queries
+// over one cached context); DSA_INDEXER_MQ=0 turns them off for measurement.
 bool indexer_multi_query(const IndexerParams& p) {
-  if ((p.k_dtype != kDtBF16 && p.k_dtype != kDtFP8) || p.compact || p.T < kMqMinT) return false;
+  if (p.compact || p.T < kMqMinT) return false;
   const char* e = getenv("DSA_INDEXER_MQ");
   return !(e && atoi(e) == 0);
 }
@@ -1950,7 +1993,14 @@ hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t st
       hipLaunchKernelGGL(indexer_topk_kernel<2>, grid, block, 0, stream, p);
     }
   }
-  else if (p.k_dtype == kDtMX) hipLaunchKernelGGL(indexer_topk_kernel<3>, grid, block, 0, stream, p);
+  else if (p.k_dtype == kDtMX) {
+    if (indexer_multi_query(p)) {
+      const dim3 g(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
+      hipLaunchKernelGGL((indexer_topk_kernel<3, kMqQ>), g, block, 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(indexer_topk_kernel<3>, grid, block, 0, stream, p);
+    }
+  }
   else if (indexer_multi_query(p)) {
     const dim3 g(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
     hipLaunchKernelGGL((indexer_topk_kernel<1, kMqQ>), g, block, 0, stream, p);

@@ -93,3 +93,25 @@ def test_multi_query_fallback(dsa):
     inp.k_pool[rows] = oracle.encode_bf16_rne(k.astype(np.float32))
     idx, score = run_both(dsa, inp)
     check(inp, idx, score, [0, 1, 2, 3, 150, 299])
+
+
+MX_CASES = {
+    "mx_causal_chunk_600": lambda: chunk(600, 7000, k_dtype="f32", k_std=1.0),
+    "mx_no_prefix_523": lambda: chunk(523, 0, k_dtype="f32", k_std=1.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MX_CASES))
+def test_multi_query_mxfp8(dsa, case):
+    """MXFP8 keys (the oracle's quantization of the same fp32 keys) and queries quantized
+    inside the call, per workgroup for the tile's four queries."""
+    import dataclasses
+    spec = MX_CASES[case]()
+    inp = make_inputs(spec, seed=len(case) * 17, with_sfa=False)
+    with np.errstate(invalid="ignore"):
+        codes, sb = oracle.quantize_mxfp8(inp.k_pool)
+    inp = dataclasses.replace(inp, spec=dataclasses.replace(spec, k_dtype="mxfp8"),
+                              k_pool=codes, k_scale=sb)
+    idx, score = run_both(dsa, inp)
+    T = spec.num_queries
+    check(inp, idx, score, sorted(set(range(0, T, max(1, T // 30))) | {T - 1}))
