@@ -11,10 +11,15 @@ The working set of one step (~125 MB) fits the 256 MB Infinity Cache, so the tim
 rotates over `--copies` independent device copies of all pools, tables and queries: a copy
 is reused only after ~1 GB of other copies has been touched.
 
-Prints one JSON line (see the keys below), including the roofline of the dominant kernel
-(the indexer, HBM-bound: algorithmic bytes per launch / its mean launch time from HIP events
-recorded around it in every 16th step of the timed region; an event pair costs the GPU a few
-microseconds, so the other steps run unbracketed) and the CPU oracle timed on a bounded sample.
+Prints one JSON line (see the keys below).  `value` is queries / second over exactly --steps
+steps between two synchronizations.  After that region each call is timed alone: launched back
+to back over the rotating copies behind a GPU sleep that keeps the queue full while the host
+enqueues, with HIP events between batches of calls on the stream the library launches on
+(samples, median, min, p10/p90 in the line).  The roofline of the dominant kernel (the
+indexer, HBM-bound in decode) is its algorithmic bytes per launch / that mean call time; the
+attention call gets its own.  `traffic` comes from the committed rocprofv3 counter summary
+(profiles/decode_counters.json, written by profile_counters.py) while its source digest
+matches the kernels.  The CPU oracle is timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--config 4] [--sfa-kv fp8]
     python bench.py --config 6 --shards 4 [--layout zigzag|contiguous] --steps 5 --warmup 2
@@ -48,7 +53,7 @@ METRIC = "decode queries/sec (indexer+TopK+SFA) at 128K ctx; % peak HBM BW / MFM
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "indexer_counters.json")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
 
 
 def indexer_bytes(spec, V):
@@ -132,15 +137,16 @@ def indexer_flops(spec, V):
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("indexer.hip", "dsa_common.hpp", "dsa_internal.hpp"):
+    for f in ("indexer.hip", "sfa.hip", "dsa_common.hpp", "dsa_internal.hpp"):
         with open(os.path.join(ROOT, "sparse_indexed_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
-    """HBM bytes per indexer launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
+def counter_traffic(call="indexer"):
+    """HBM bytes per launch of one call ("indexer" or "sparse_attn", the latter summing its
+    kernels) from the committed rocprofv3 counter summary, if it was taken on the current
+    kernel sources; else None."""
     try:
         with open(PROFILE_COUNTERS) as f:
             c = json.load(f)
@@ -148,7 +154,8 @@ def counter_traffic():
         return None, None
     if c.get("source_digest") != source_digest() or c.get("workload") is None:
         return None, c.get("workload")
-    return c.get("hbm_bytes_per_launch"), c.get("workload")
+    e = c.get("calls", {}).get(call)
+    return (e.get("hbm_bytes_per_launch") if e else None), c.get("workload")
 
 
 def cpu_baseline(inp, budget_s=12.0):
@@ -442,62 +449,95 @@ def main():
     ws_s = dsa.zeroed_workspace(dsa.sfa_workspace_bytes(T, spec.sfa_heads, K, spec.d_v), "cuda")
     outs = []
     for d in devs:
-        idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        # valid index lists from the start (position 0 repeated), so that the attention call can
+        # be timed on every copy before the indexer has written it
+        idx = torch.zeros((T, K), dtype=torch.int32, device="cuda")
         o = torch.empty((T, spec.sfa_heads, spec.d_v), dtype=d.q_sfa.dtype, device="cuda")
         outs.append((idx, o))
 
-    # An event pair costs a few microseconds of GPU time, so only every SAMPLE-th step of the
-    # timed region brackets a kernel call with events: the indexer in some, the sparse
-    # attention call in others.
-    SAMPLE = 8
+    def call_idx(i):
+        d, lay = devs[i % copies], layouts[i % copies]
+        dsa.indexer_topk(d.q_idx, d.w, d.k_pool, d.k_scale, lay, d.q_seq, d.q_visible,
+                         d.max_visible, K, out_idx=outs[i % copies][0], want_score=False,
+                         workspace=ws_i, total_visible=total_visible)
 
-    def step(i, ev=None, which=None):
+    def call_sfa(i):
         d, lay = devs[i % copies], layouts[i % copies]
         idx, o = outs[i % copies]
-        if which == "idx":
-            ev[0].record()
-        dsa.indexer_topk(d.q_idx, d.w, d.k_pool, d.k_scale, lay, d.q_seq, d.q_visible,
-                         d.max_visible, K, out_idx=idx, want_score=False, workspace=ws_i,
-                         total_visible=total_visible)
-        if which == "idx":
-            ev[1].record()
-        if which == "sfa":
-            ev[0].record()
         dsa.sparse_attn(d.q_sfa, d.kv_pool, idx, lay, d.q_seq, spec.softmax_scale, spec.d_v,
                         out=o, want_lse=False, workspace=ws_s)
-        if which == "sfa":
-            ev[1].record()
+
+    def step(i):
+        call_idx(i)
+        call_sfa(i)
 
     print(f"bench: {copies} rotating copies, warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    kinds = [("idx" if (i // SAMPLE) % 2 == 0 else "sfa") if i % SAMPLE == 0 else None
-             for i in range(args.steps)]
-    kinds[0] = "idx"
-    if args.steps > 1 and "sfa" not in kinds:
-        kinds[-1] = "sfa"
+    # The timed region: exactly --steps steps between two synchronizations, nothing else.
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i], kinds[i])
+        step(args.warmup + i)
+    t_host = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    idx_ms = [e[0].elapsed_time(e[1]) for e, k in zip(evs, kinds) if k == "idx"]
-    sfa_ms = [e[0].elapsed_time(e[1]) for e, k in zip(evs, kinds) if k == "sfa"] or [float("nan")]
     step_ms = wall * 1e3 / args.steps
     qps = T * args.steps / wall
-    idx_mean = float(np.mean(idx_ms))
-    sfa_mean = float(np.mean(sfa_ms))
+
+    # Per-call times, after the timed region: each call alone, launched back to back over the
+    # rotating copies.  A GPU sleep queued first keeps the device busy while the host enqueues
+    # every launch, so the events see a full queue (never an idle GPU waiting for the host);
+    # one event between batches of BATCH calls gives BATCHES samples of the mean call time.
+    BATCHES, BATCH = (60, 8) if step_ms < 1.0 else (12, 1)
+
+    def per_call_us(fn):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(BATCHES + 1)]
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(int(2.4e9 * 0.05))   # ~50 ms at 2.4 GHz, longer than the enqueueing
+        except (AttributeError, RuntimeError):
+            print("bench: no GPU sleep available; per-call times may include host gaps",
+                  file=sys.stderr, flush=True)
+        evs[0].record()
+        n = 0
+        for b in range(BATCHES):
+            for _ in range(BATCH):
+                fn(n)
+                n += 1
+            evs[b + 1].record()
+        torch.cuda.synchronize()
+        return np.array([evs[b].elapsed_time(evs[b + 1]) * 1e3 / BATCH for b in range(BATCHES)])
+
+    idx_us = per_call_us(call_idx)
+    sfa_us = per_call_us(call_sfa)
+
+    def stats(us):
+        return {"mean": float(us.mean()), "median": float(np.median(us)), "min": float(us.min()),
+                "p10": float(np.percentile(us, 10)), "p90": float(np.percentile(us, 90)),
+                "samples": int(us.size), "calls_per_sample": BATCH}
+
+    idx_mean = float(idx_us.mean()) * 1e-3          # ms
+    sfa_mean = float(sfa_us.mean()) * 1e-3
+    # the two calls run back to back in a step, so their separate times cannot exceed it
+    # (5% allowed for run-to-run noise between the two measurements)
+    consistent = idx_mean + sfa_mean <= step_ms * 1.05
     achieved = step_bytes_idx / (idx_mean * 1e-3) / 1e9
-    traffic, prof_wl = counter_traffic()
-    print(f"bench: step {step_ms * 1e3:.1f} us (indexer {idx_mean * 1e3:.1f} us median "
-          f"{np.median(idx_ms) * 1e3:.1f}, SFA {sfa_mean * 1e3:.1f} us); indexer {achieved:.0f} GB/s; "
-          f"SFA {step_bytes_sfa / (sfa_mean * 1e-3) / 1e9:.0f} GB/s, "
+    traffic, prof_wl = counter_traffic("indexer")
+    sfa_traffic, _ = counter_traffic("sparse_attn")
+    print(f"bench: step {step_ms * 1e3:.1f} us (host enqueue {t_host * 1e6 / args.steps:.1f} us); "
+          f"indexer {idx_mean * 1e3:.1f} us (median {np.median(idx_us):.1f}, p10 "
+          f"{np.percentile(idx_us, 10):.1f}, p90 {np.percentile(idx_us, 90):.1f}), "
+          f"{achieved:.0f} GB/s; SFA {sfa_mean * 1e3:.1f} us, "
+          f"{step_bytes_sfa / (sfa_mean * 1e-3) / 1e9:.0f} GB/s, "
           f"{sfa_flops(spec, V) / (sfa_mean * 1e-3) / 1e12:.1f} TFLOP/s; whole step "
           f"{(step_bytes_idx + step_bytes_sfa) / (step_ms * 1e-3) / 1e9:.0f} GB/s",
           file=sys.stderr, flush=True)
+    if not consistent:
+        print(f"bench: ERROR: indexer {idx_mean * 1e3:.1f} us + SFA {sfa_mean * 1e3:.1f} us exceed "
+              f"the step's {step_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        sys.exit(3)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -507,15 +547,31 @@ def main():
     # The indexer is the dominant kernel.  Decode streams every key once (HBM-bound); in chunked
     # prefill thousands of queries share one cached context, so the key bytes are reused from
     # the caches and the bound is the MFMA rate on its 2*H*D flops per visible position.
-    if spec.name.startswith("prefill"):
+    prefill = spec.name.startswith("prefill")
+    sfa_tflops = sfa_flops(spec, V) / (sfa_mean * 1e-3) / 1e12
+    if prefill:
         idx_tflops = indexer_flops(spec, V) / (idx_mean * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": "indexer_topk_kernel", "achieved": idx_tflops,
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": idx_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        sfa_roof = {"bound": "mfma", "kernel": "sfa (attention + fixup)", "achieved": sfa_tflops,
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": sfa_tflops / MFMA_BF16_PEAK_TFLOPS}
     else:
         roofline = {"bound": "hbm", "kernel": "indexer_topk_kernel", "achieved": achieved,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                     "traffic": traffic}
+        sfa_gbs = step_bytes_sfa / (sfa_mean * 1e-3) / 1e9
+        sfa_roof = {"bound": "hbm", "kernel": "sfa (attention + combine)", "achieved": sfa_gbs,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sfa_gbs / HBM_PEAK_GBS,
+                    "traffic": sfa_traffic, "tflops": sfa_tflops}
+    step_cfg = {}
+    if not prefill:
+        # a decode step streams its bytes from HBM; a prefill chunk reuses its cached context
+        # from the caches, so there the byte count is not an HBM figure
+        step_cfg = {"step_algorithmic_bytes": step_bytes_idx + step_bytes_sfa,
+                    "step_hbm_frac": (step_bytes_idx + step_bytes_sfa) / (step_ms * 1e-3) / 1e9
+                    / HBM_PEAK_GBS}
     line = {
         "metric": METRIC,
         "value": qps,
@@ -538,10 +594,10 @@ def main():
             "sfa": f"{spec.sfa_heads} heads {spec.d_qk}/{spec.d_v} {spec.kv_dtype}",
             "block_size": spec.block_size,
             "rotating_copies": copies,
-            "step_algorithmic_bytes": step_bytes_idx + step_bytes_sfa,
-            "step_hbm_frac": (step_bytes_idx + step_bytes_sfa) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "sfa_mean_us": sfa_mean * 1e3,
-            "indexer_mean_us": idx_mean * 1e3,
+            **step_cfg,
+            "indexer_us": stats(idx_us),
+            "sfa_us": stats(sfa_us),
+            "sfa_roofline": sfa_roof,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

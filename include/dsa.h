@@ -28,7 +28,11 @@
  *     checked on the device.
  *   - Every device pointer must be 16-byte aligned (DSA_ERR_ALIGN otherwise).  Pool rows are
  *     dense (row stride = row width).
- *   - The library keeps no device memory and no mutable global state.
+ *   - The library keeps no device memory.  Its only process-wide state is set once and never
+ *     changed afterwards: the planners' measurement overrides, read from the environment at
+ *     the first planned call (DSA_INDEXER_TARGET_WG, DSA_INDEXER_MQ, DSA_SFA_HPW,
+ *     DSA_SFA_SPLITS; unset means the planners' own choice), and for dsa_indexer_prolog one
+ *     rocBLAS handle per device, created at that device's first call under a lock.
  *   - Two calls that share a workspace must not run concurrently.
  */
 #ifndef DSA_H_

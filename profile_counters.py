@@ -1,0 +1,197 @@
+"""Hardware-counter summaries of the hot path's kernels, taken with rocprofv3 on an MI355X.
+
+    python profile_counters.py hbm  [--config 4] [--out DIR]   # FETCH_SIZE / WRITE_SIZE
+    python profile_counters.py mfma [--config 3] [--out DIR]   # MFMA busy cycles and ops
+
+Each counter pass is its own `rocprofv3 --pmc ... -- python3 bench.py ...` child process (the
+profiler's library must start with the program, so this script never touches the GPU
+itself), run from /tmp with TMPDIR=/tmp and a time limit.
+
+hbm: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of every kernel of the step, each scaled by
+what the same counter reads for a plain 256 MiB device-to-device copy of known size, give HBM
+bytes per launch of the indexer call and of the attention call (its kernels summed).  The
+result goes to profiles/decode_counters.json, tied to the kernel sources by the digest
+bench.py computes (bench.py reports `traffic` only while it matches), and a Markdown table is
+printed.
+
+mfma: SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16 per
+dispatch.  Utilisation = busy cycles / (GUI-active cycles x 1024 SIMDs), the profiler's own
+MfmaUtil definition; flops = MOPS x 512; the durations come from a kernel-trace pass of the
+same command.  A Markdown table is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+SIMDS = 256 * 4
+
+
+def run_prof(out_dir, tag, prof_args, bench_args, limit=240):
+    d = os.path.join(out_dir, tag)
+    cmd = ["rocprofv3", *prof_args, "--output-format", "csv", "-d", d, "-o", tag, "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *bench_args]
+    print("profile_counters: " + " ".join(cmd), flush=True)
+    env = dict(os.environ, TMPDIR="/tmp")
+    r = subprocess.run(["timeout", "-s", "KILL", str(limit), *cmd], cwd="/tmp", env=env)
+    if r.returncode != 0:
+        # rocprofv3 may end with a segmentation fault after a complete run; the caller checks
+        # that the result files exist
+        print(f"profile_counters: {tag} exited {r.returncode}", flush=True)
+    return d, " ".join(cmd[:cmd.index("-d")] + cmd[cmd.index("--"):]).replace(ROOT, "$ROOT")
+
+
+def read_csv(d, suffix):
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"profile_counters: no *{suffix}.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def short(name):
+    n = name.replace("(anonymous namespace)::", "").replace("dsa::", "").strip()
+    if n.startswith("void "):
+        n = n[5:]
+    return n.split("(")[0].strip()
+
+
+def counters_per_kernel(d):
+    """{kernel: {counter: mean value per dispatch}} from a --pmc pass."""
+    acc = defaultdict(lambda: defaultdict(float))
+    disp = defaultdict(set)
+    for r in read_csv(d, "counter_collection"):
+        k = short(r["Kernel_Name"])
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    return {k: {c: v / len(disp[k]) for c, v in cs.items()} for k, cs in acc.items()}, \
+        {k: len(v) for k, v in disp.items()}
+
+
+def durations(d):
+    """{kernel: (calls, mean us)} from a --kernel-trace pass."""
+    acc = defaultdict(list)
+    for r in read_csv(d, "kernel_trace"):
+        acc[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: (len(v), sum(v) / len(v)) for k, v in acc.items()}
+
+
+def call_of(kernel):
+    if kernel.startswith("indexer_topk_kernel"):
+        return "indexer"
+    if kernel.startswith("sfa_"):
+        return "sparse_attn"
+    return None
+
+
+def hbm(args):
+    sys.path.insert(0, ROOT)
+    import bench
+    ba = ["--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--config", str(args.config)]
+    cmds, res = [], {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        d, c = run_prof(args.out, f"pmc_{ctr.lower()}", ["--pmc", ctr], ba)
+        res[ctr], n = counters_per_kernel(d)
+        cmds.append(c)
+        d, c = run_prof(args.out, f"pmc_copy_{ctr.lower()}", ["--pmc", ctr], ["--calibrate-copy", "256"])
+        cal, _ = counters_per_kernel(d)
+        cmds.append(c)
+        copy_k = [k for k in cal if "copy" in k.lower()]
+        res["copy_" + ctr] = cal[copy_k[0]][ctr]
+    moved_kib = 256 * 1024.0
+    ff = moved_kib / res["copy_FETCH_SIZE"]
+    wf = moved_kib / res["copy_WRITE_SIZE"]
+    kernels = sorted(k for k in res["FETCH_SIZE"] if call_of(k))
+    calls = {}
+    table = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
+             "|---|---:|---:|---:|---:|"]
+    for k in kernels:
+        f = res["FETCH_SIZE"][k]["FETCH_SIZE"]
+        w = res["WRITE_SIZE"].get(k, {}).get("WRITE_SIZE", 0.0)
+        rb, wb = f * 1024 * ff, w * 1024 * wf
+        table.append(f"| `{k}` | {f:.0f} | {w:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+        e = calls.setdefault(call_of(k), {"kernels": [], "hbm_bytes_per_launch": 0.0,
+                                          "read_bytes": 0.0, "write_bytes": 0.0})
+        e["kernels"].append(k)
+        e["hbm_bytes_per_launch"] += rb + wb
+        e["read_bytes"] += rb
+        e["write_bytes"] += wb
+    out = {"workload": bench_workload(args.config), "source_digest": bench.source_digest(),
+           "calls": calls,
+           "calibration": {"kernel": "device-to-device copy (bench.py --calibrate-copy 256)",
+                           "bytes": 256 << 20, "fetch_kib": res["copy_FETCH_SIZE"],
+                           "write_kib": res["copy_WRITE_SIZE"], "fetch_factor": ff,
+                           "write_factor": wf},
+           "commands": cmds}
+    path = os.path.join(ROOT, "profiles", "decode_counters.json") if args.write else \
+        os.path.join(args.out, "decode_counters.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"profile_counters: wrote {path}")
+    print(f"copy calibration: fetch factor {ff:.3f}, write factor {wf:.3f}")
+    print("\n".join(table))
+    for c, e in calls.items():
+        print(f"{c}: {e['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch "
+              f"(read {e['read_bytes'] / 1e6:.1f}, write {e['write_bytes'] / 1e6:.1f})")
+    print("commands:\n" + "\n".join("    cd /tmp && export TMPDIR=/tmp && " + c for c in cmds))
+
+
+def bench_workload(cfg):
+    sys.path.insert(0, ROOT)
+    from synth import workload
+    return workload(cfg).name
+
+
+def mfma(args):
+    ba = ["--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--config", str(args.config)]
+    d, c1 = run_prof(args.out, "mfma_busy",
+                     ["--pmc", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16"], ba, 600)
+    ctr, n = counters_per_kernel(d)
+    d, c2 = run_prof(args.out, "mfma_util", ["--pmc", "MfmaUtil"], ba, 600)
+    util_d, _ = counters_per_kernel(d)
+    d, c3 = run_prof(args.out, "mfma_trace", ["--kernel-trace"], ba, 600)
+    dur = durations(d)
+    print(f"workload {bench_workload(args.config)}")
+    print("| kernel | dispatches | mean us | MfmaUtil % | busy / (GUI x 1024) | bf16 MFMA TFLOP/s (MOPS x 512 / time) | of 2500 |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for k in sorted(ctr):
+        if not call_of(k):
+            continue
+        cs = ctr[k]
+        raw = cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (cs["GRBM_GUI_ACTIVE"] * SIMDS) if cs.get("GRBM_GUI_ACTIVE") else float("nan")
+        mu = util_d.get(k, {}).get("MfmaUtil", float("nan"))
+        flops = cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        us = dur.get(k, (0, float("nan")))[1]
+        tf = flops / (us * 1e-6) / 1e12 if us == us and us > 0 else float("nan")
+        print(f"| `{k}` | {n[k]} | {us:.1f} | {mu:.1f} | {raw:.3f} | {tf:.0f} | {tf / 2500:.3f} |")
+        print(f"<!-- {k}: busy {cs['SQ_VALU_MFMA_BUSY_CYCLES']:.4g}, gui {cs['GRBM_GUI_ACTIVE']:.4g}, "
+              f"mops_bf16 {cs.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0):.4g} -->")
+    print("commands:\n" + "\n".join("    cd /tmp && export TMPDIR=/tmp && " + c for c in (c1, c2, c3)))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("mode", choices=("hbm", "mfma"))
+    ap.add_argument("--config", type=int, default=None)
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "counters"))
+    ap.add_argument("--write", action="store_true",
+                    help="hbm: write profiles/decode_counters.json (else into --out)")
+    args = ap.parse_args()
+    if args.config is None:
+        args.config = 4 if args.mode == "hbm" else 3
+    os.makedirs(args.out, exist_ok=True)
+    hbm(args) if args.mode == "hbm" else mfma(args)
+
+
+if __name__ == "__main__":
+    main()

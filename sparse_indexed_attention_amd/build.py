@@ -12,7 +12,11 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["api.cpp", "indexer.hip", "sfa.hip", "store.hip", "prolog.hip"]
+# (source, object, extra flags): the indexer compiles as four parts, one per group of its
+# kernel's instantiations, so that they build in parallel
+SOURCES = [("api.cpp", "api", []), ("sfa.hip", "sfa", []), ("store.hip", "store", []),
+           ("prolog.hip", "prolog", [])] + \
+          [("indexer.hip", f"indexer_p{k}", [f"-DDSA_INDEXER_PART={k}"]) for k in range(4)]
 LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 ARCH = "gfx950"
 
@@ -26,7 +30,7 @@ def hipcc() -> str:
 
 def flags():
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
@@ -34,19 +38,45 @@ def flags():
     ]
 
 
+def _compile(cc, src, obj, extra, verbose):
+    cmd = [cc, *flags(), *extra, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def _quiet(stderr: str) -> str:
+    # hipcc's host pass does not know the packed-fp32 feature name and says so; not an error
+    return "\n".join(l for l in stderr.splitlines()
+                     if "packed-fp32-ops" not in l or "error" in l.lower())
+
+
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (build/ next to this file), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+    cc = hipcc()
+    objdir = os.path.join(HERE, "build")
+    os.makedirs(objdir, exist_ok=True)
+    jobs = []
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1, 16)) as ex:
+        for s, o, extra in SOURCES:
+            obj = os.path.join(objdir, o + ".o")
+            jobs.append((o, ex.submit(_compile, cc, os.path.join(CSRC, s), obj, extra, verbose)))
+    for s, j in jobs:
+        res = j.result()
+        err = _quiet(res.stderr)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {s} ({res.returncode}):\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), *[os.path.join(CSRC, s) for s in SOURCES], *LIBS, "-o", tmp]
+    objs = [os.path.join(objdir, o + ".o") for _, o, _ in SOURCES]
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LIBS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature name and says so; not an error
-    err = "\n".join(l for l in res.stderr.splitlines()
-                    if "packed-fp32-ops" not in l or "error" in l.lower())
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{_quiet(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

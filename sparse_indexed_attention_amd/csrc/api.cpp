@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 
 #include "../../include/dsa.h"
 #include "dsa_internal.hpp"
@@ -67,6 +68,25 @@ bool sfa_fast(dsa_dtype dtype, int32_t H, int32_t dqk, int32_t dv) {
 }
 
 }  // namespace
+
+namespace dsa {
+const PlanOverrides& plan_overrides() {
+  static const PlanOverrides o = [] {
+    PlanOverrides v{};
+    auto num = [](const char* name) -> int64_t {
+      const char* e = std::getenv(name);
+      return e ? std::atoll(e) : 0;
+    };
+    v.indexer_target_wg = num("DSA_INDEXER_TARGET_WG");
+    const char* mq = std::getenv("DSA_INDEXER_MQ");
+    v.indexer_mq_off = mq && std::atoi(mq) == 0;
+    v.sfa_hpw = (int32_t)num("DSA_SFA_HPW");
+    v.sfa_splits = num("DSA_SFA_SPLITS");
+    return v;
+  }();
+  return o;
+}
+}  // namespace dsa
 
 extern "C" {
 

@@ -9,6 +9,18 @@
 
 namespace dsa {
 
+// Measurement overrides of the launch planners, read from the environment once per process
+// (at the first call that plans a launch) and constant afterwards; 0 means "planner's choice".
+//   DSA_INDEXER_TARGET_WG  indexer workgroups aimed for         DSA_INDEXER_MQ=0  no multi-query tiles
+//   DSA_SFA_HPW            heads per attention workgroup        DSA_SFA_SPLITS    index-list slices
+struct PlanOverrides {
+  int64_t indexer_target_wg;
+  int32_t indexer_mq_off;
+  int32_t sfa_hpw;
+  int64_t sfa_splits;
+};
+const PlanOverrides& plan_overrides();
+
 // ------------------------------------------------------------------ indexer + Top-K
 constexpr int kIdxThreads = 256;
 constexpr int kSplitMax = 2048;        // context positions scored by one workgroup

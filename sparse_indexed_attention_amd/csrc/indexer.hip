@@ -1916,6 +1916,38 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(Ind
 
 }  // namespace
 
+// The build compiles this file once per part (DSA_INDEXER_PART = 0 .. 3) so that the kernel's
+// instantiations compile in parallel; part 0 also holds the host planners and the dispatcher.
+// Without the macro every part is in one translation unit.
+#ifndef DSA_INDEXER_PART
+#define DSA_INDEXER_PART -1
+#endif
+#define DSA_PART(n) (DSA_INDEXER_PART < 0 || DSA_INDEXER_PART == (n))
+
+template <int MODE, int QT>
+void launch_instance(dim3 grid, hipStream_t stream, const IndexerParams& p);
+#define DSA_INSTANCE(part, MODE, QT)                                                         \
+  template <>                                                                                \
+  void launch_instance<MODE, QT>(dim3 grid, hipStream_t stream, const IndexerParams& p) {    \
+    hipLaunchKernelGGL((indexer_topk_kernel<MODE, QT>), grid, dim3(NT), 0, stream, p);       \
+  }
+#if DSA_PART(0)
+DSA_INSTANCE(0, 0, 1)
+DSA_INSTANCE(0, 1, 1)
+#endif
+#if DSA_PART(1)
+DSA_INSTANCE(1, 2, 1)
+DSA_INSTANCE(1, 1, kMqQ)
+#endif
+#if DSA_PART(2)
+DSA_INSTANCE(2, 3, 1)
+DSA_INSTANCE(2, 2, kMqQ)
+#endif
+#if DSA_PART(3)
+DSA_INSTANCE(3, 3, kMqQ)
+#endif
+
+#if DSA_PART(0)
 // The layout and launch for one split length (a multiple of 64 in [kMinSplit, kSplitMax]).
 IndexerPlan plan_indexer_split(int32_t T, int32_t max_visible, int32_t top_k, int32_t split) {
   IndexerPlan pl{};
@@ -1942,8 +1974,7 @@ IndexerPlan plan_indexer_split(int32_t T, int32_t max_visible, int32_t top_k, in
 // With the total visible length known, split = total / (512 - T) bounds the live count by
 // 512; without it, T * max_visible stands in for the total (fewer, longer splits).
 IndexerPlan plan_indexer(int32_t T, int32_t max_visible, int32_t top_k, int64_t total_visible) {
-  int64_t target_wg = 512;
-  if (const char* e = getenv("DSA_INDEXER_TARGET_WG")) target_wg = atoll(e) > 0 ? atoll(e) : 512;
+  const int64_t target_wg = plan_overrides().indexer_target_wg > 0 ? plan_overrides().indexer_target_wg : 512;
   const int64_t tmax = (int64_t)T * max_visible;
   int64_t total = tmax, slots = target_wg;
   if (total_visible > 0) {
@@ -1978,35 +2009,19 @@ size_t indexer_workspace_bytes(int32_t T, int32_t max_visible, int32_t top_k) {
 // over one cached context); DSA_INDEXER_MQ=0 turns them off for measurement.
 bool indexer_multi_query(const IndexerParams& p) {
   if (p.compact || p.T < kMqMinT) return false;
-  const char* e = getenv("DSA_INDEXER_MQ");
-  return !(e && atoi(e) == 0);
+  return !plan_overrides().indexer_mq_off;
 }
 
 hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t stream) {
-  const dim3 grid(p.grid), block(NT);
-  if (!fast_path) hipLaunchKernelGGL(indexer_topk_kernel<0>, grid, block, 0, stream, p);
-  else if (p.k_dtype == kDtFP8) {
-    if (indexer_multi_query(p)) {
-      const dim3 g(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
-      hipLaunchKernelGGL((indexer_topk_kernel<2, kMqQ>), g, block, 0, stream, p);
-    } else {
-      hipLaunchKernelGGL(indexer_topk_kernel<2>, grid, block, 0, stream, p);
-    }
-  }
-  else if (p.k_dtype == kDtMX) {
-    if (indexer_multi_query(p)) {
-      const dim3 g(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
-      hipLaunchKernelGGL((indexer_topk_kernel<3, kMqQ>), g, block, 0, stream, p);
-    } else {
-      hipLaunchKernelGGL(indexer_topk_kernel<3>, grid, block, 0, stream, p);
-    }
-  }
-  else if (indexer_multi_query(p)) {
-    const dim3 g(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
-    hipLaunchKernelGGL((indexer_topk_kernel<1, kMqQ>), g, block, 0, stream, p);
-  }
-  else hipLaunchKernelGGL(indexer_topk_kernel<1>, grid, block, 0, stream, p);
+  const dim3 grid(p.grid);
+  const bool mq = fast_path && indexer_multi_query(p);
+  const dim3 gmq(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
+  if (!fast_path) launch_instance<0, 1>(grid, stream, p);
+  else if (p.k_dtype == kDtFP8) mq ? launch_instance<2, kMqQ>(gmq, stream, p) : launch_instance<2, 1>(grid, stream, p);
+  else if (p.k_dtype == kDtMX) mq ? launch_instance<3, kMqQ>(gmq, stream, p) : launch_instance<3, 1>(grid, stream, p);
+  else mq ? launch_instance<1, kMqQ>(gmq, stream, p) : launch_instance<1, 1>(grid, stream, p);
   return hipGetLastError();
 }
+#endif  // DSA_PART(0)
 
 }  // namespace dsa

@@ -11,15 +11,17 @@
 // Fast path (bf16 storage, d_qk = 576, d_v = 512, heads a multiple of 32): a workgroup owns
 // (query, group of 32*NW heads, slice of the index list); every selected row is read once per
 // workgroup and serves all of its heads.
-//   * Gather: tiles of 32 rows land in LDS through direct-to-LDS loads, double-buffered (tile
-//     i+1 streams in while tile i is computed).  LDS rows are 73 sixteen-byte chunks (one of
+//   * Gather: tiles of 32 rows land in LDS through direct-to-LDS loads into three buffers (tiles
+//     i+1 and i+2 stream in while tile i is computed).  LDS rows are 73 sixteen-byte chunks (one of
 //     padding): with that odd stride both the MFMA reads of 16 rows at one column and the
 //     transposing reads of 4 rows x 2 chunks touch distinct banks.  The pool rows of the slice
 //     are resolved once, into LDS.
 //   * Each wave holds 32 heads.  S^T = R . Q^T on v_mfma_f32_32x32x16_bf16: tile rows are the
 //     A operand and the wave's queries (registers) the B operand, so a lane column is a head.
-//   * Online softmax in the exp2 domain; the output accumulators are rescaled only when a
-//     head's running maximum moves.
+//   * Softmax in the exp2 domain without rescaling: a head's exponent reference is set by its
+//     first live tile and never moved, so the output accumulators are never rescaled; a head
+//     whose scores climb more than 64 above that reference is flagged and recomputed by the
+//     reference method (fp32) after the attention kernel.
 //   * O += P . V on the same MFMA: the probabilities, in the S^T accumulator layout, are the
 //     A operand as they stand (the k order of the contraction is permuted to the rows each
 //     lane holds), and the V operand comes straight from the row-major tile through the
@@ -718,17 +720,15 @@ SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path) {
     // slices (at most 1024 rows each) until about one workgroup per CU runs.
     const bool wide = (int64_t)T * (H / 128) >= 256;
     pl.heads_per_wg = (H % 128 == 0) ? 128 : (H % 64 == 0) ? 64 : 32;
-    if (const char* e = getenv("DSA_SFA_HPW")) {
-      const int v = atoi(e);
-      if ((v == 32 || v == 64 || v == 128) && H % v == 0) pl.heads_per_wg = v;
-    }
+    if (const int v = plan_overrides().sfa_hpw; (v == 32 || v == 64 || v == 128) && H % v == 0)
+      pl.heads_per_wg = v;
     pl.n_hg = H / pl.heads_per_wg;
     const int64_t max_ns = (K + kTileRows - 1) / kTileRows;
     int64_t ns = 1;
     if (!wide) {
       const int64_t want = 256;
       ns = (want + (int64_t)T * pl.n_hg - 1) / ((int64_t)T * pl.n_hg);
-      if (const char* e = getenv("DSA_SFA_SPLITS")) ns = atoll(e) > 0 ? atoll(e) : ns;
+      if (plan_overrides().sfa_splits > 0) ns = plan_overrides().sfa_splits;
       const int64_t min_ns = (K + 1023) / 1024;
       if (ns < min_ns) ns = min_ns;
     }

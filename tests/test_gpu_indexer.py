@@ -209,15 +209,32 @@ def test_full_decode_fp8_1m_with_planted_ties(dsa):
     assert [p in sel for p in bnd.tolist()] == [True] + [False] * (len(bnd) - 1)
 
 
+def prefill_sample(T, n=64):
+    """n evenly spaced queries of a chunk, shifted so that every position inside a four-query
+    tile occurs (query 64i + i % 4), plus the last query."""
+    step = T // n
+    return sorted({step * i + i % 4 for i in range(n)} | {T - 1})
+
+
+def check_structure(inp, idx):
+    """Cheap invariants of every row: K_eff strictly increasing positions in [0, V) (the output
+    is in ascending position order), then -1."""
+    K = inp.spec.top_k
+    for t in range(inp.spec.num_queries):
+        V = int(inp.q_visible[t])
+        k = min(K, V)
+        head, tail = idx[t, :k], idx[t, k:]
+        assert np.all(tail == -1), f"query {t}: tail not -1"
+        assert head[0] >= 0 and head[-1] < V, f"query {t}: positions outside [0, {V})"
+        assert np.all(np.diff(head) > 0), f"query {t}: not strictly increasing"
+
+
 @pytest.mark.slow
 def test_full_chunked_prefill_sampled(dsa):
     inp = make_inputs(workload(3), seed=3, with_sfa=False)
     idx, score = run_indexer(dsa, inp)
-    sample = [0, 1, 777, 2048, 4094, 4095]
-    check(inp, idx, score, queries=sample)
-    # causal: no query selects a position it cannot see
-    V = inp.q_visible
-    assert np.all((idx < V[:, None]) | (idx == -1))
+    check_structure(inp, idx)
+    check(inp, idx, score, queries=prefill_sample(inp.spec.num_queries))
 
 
 @pytest.mark.slow
