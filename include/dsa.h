@@ -163,6 +163,30 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * dsa_indexer_topk_noalloc: dsa_indexer_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * arguments, results and errors are those of dsa_indexer_topk without the workspace: the call
+ * uses a scratch array of DSA_NOALLOC_SCRATCH_BYTES bytes that the library holds in device
+ * memory (one per device, from the device's first use of the library until the process
+ * ends) and calls no allocator.
+ *   - A call whose plan needs more scratch than that returns DSA_ERR_WORKSPACE and launches
+ *     nothing (decode batches fit: 8 queries of 128K, 32 of 32K or one of 4M positions need
+ *     under 9 MB; a prefill chunk of thousands of queries does not: use dsa_indexer_topk).
+ *   - The first call on a device looks up the array's device address and enqueues a kernel
+ *     that zeroes it on `stream` before the indexer (a failure there returns DSA_ERR_HIP).
+ *   - Every call on one device shares the array: calls that overlap on one device (other
+ *     streams, other host threads) race and must be serialized by the caller.
+ * --------------------------------------------------------------------------------------- */
+#define DSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+dsa_status dsa_indexer_topk_noalloc(const void* q, dsa_dtype q_dtype, const float* head_w,
+                                    const void* k_pool, dsa_dtype k_dtype, const float* k_scale,
+                                    int32_t n_heads, int32_t head_dim,
+                                    const dsa_layout* layout, const dsa_queries* queries,
+                                    int32_t top_k, int32_t* out_idx, float* out_score,
+                                    void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Sparse Flash Attention over the selected rows of the MLA latent cache
  *
  * For query t (sequence b = q_seq[t]) let J be the entries of idx[t, 0 .. top_k) that are

@@ -66,6 +66,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                      ctypes.POINTER(DsaLayout), ctypes.POINTER(DsaQueries),
                                      _I32, _P, _P, _P, _SZ, _P]
     lib.dsa_indexer_topk.restype = _I32
+    lib.dsa_indexer_topk_noalloc.argtypes = [_P, _I32, _P, _P, _I32, _P, _I32, _I32,
+                                             ctypes.POINTER(DsaLayout), ctypes.POINTER(DsaQueries),
+                                             _I32, _P, _P, _P]
+    lib.dsa_indexer_topk_noalloc.restype = _I32
     lib.dsa_sparse_attn_workspace_size.argtypes = [_I32, _I32, _I32, _I32]
     lib.dsa_sparse_attn_workspace_size.restype = _SZ
     lib.dsa_sparse_attn.argtypes = [_P, _I32, _P, _I32, _I32, _I32, _I32, ctypes.c_float,
@@ -192,6 +196,24 @@ def indexer_topk(q, head_w, k_pool, k_scale, layout: DsaLayout, q_seq, q_visible
                               _stream(stream))
     if st != 0:
         raise DsaError("dsa_indexer_topk", st)
+    return out_idx, out_score
+
+
+def indexer_topk_noalloc(q, head_w, k_pool, k_scale, layout: DsaLayout, q_seq, q_visible,
+                         max_visible: int, top_k: int, *, out_idx, out_score=None, stream=None,
+                         total_visible: int = 0):
+    """dsa_indexer_topk_noalloc: indexer_topk with the library's own device scratch array as
+    the workspace (nothing is allocated by the call; out_idx, and out_score if wanted, are the
+    caller's).  Returns (out_idx, out_score)."""
+    lib = load()
+    T, H, D = q.shape
+    queries = make_queries(q_seq, q_visible, max_visible, total_visible)
+    st = lib.dsa_indexer_topk_noalloc(_ptr(q), _dtype_code(q), _ptr(head_w), _ptr(k_pool),
+                                      _key_dtype(k_pool, k_scale), _ptr(k_scale), H, D,
+                                      ctypes.byref(layout), ctypes.byref(queries), top_k,
+                                      _ptr(out_idx), _ptr(out_score), _stream(stream))
+    if st != 0:
+        raise DsaError("dsa_indexer_topk_noalloc", st)
     return out_idx, out_score
 
 

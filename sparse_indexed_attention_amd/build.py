@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libdsa.so")
 # (source, object, extra flags): the indexer compiles as four parts, one per group of its
 # kernel's instantiations, so that they build in parallel
 SOURCES = [("api.cpp", "api", []), ("sfa.hip", "sfa", []), ("store.hip", "store", []),
-           ("prolog.hip", "prolog", [])] + \
+           ("prolog.hip", "prolog", []), ("noalloc.hip", "noalloc", [])] + \
           [("indexer.hip", f"indexer_p{k}", [f"-DDSA_INDEXER_PART={k}"]) for k in range(4)]
 LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 ARCH = "gfx950"

@@ -192,3 +192,34 @@ def test_store_validation(lib):
     assert lib.dsa_store_kv(A[0], 2, 4, 576, A[1], A[2], 1, None) == 3
     assert lib.dsa_store_kv(A[0], 1, 4, 576, A[1] + 8, A[2], 1, None) == 6
     assert lib.dsa_store_kv(A[0], 1, 4, 512, A[1], A[2], 2, None) == 4   # fp8 rows: d_qk 576 only
+
+
+def _noalloc_call(lib, m, layout=None, queries=None, **kw):
+    args = dict(q=A[0], qd=1, w=A[1], k=A[2], kd=2, ks=A[3], H=64, D=128, K=2048,
+                out=A[4], sc=A[5])
+    args.update(kw)
+    if layout is None:
+        layout, queries = _lq(m)
+    return lib.dsa_indexer_topk_noalloc(args["q"], args["qd"], args["w"], args["k"], args["kd"],
+                                        args["ks"], args["H"], args["D"], ctypes.byref(layout),
+                                        ctypes.byref(queries), args["K"], args["out"], args["sc"],
+                                        None)
+
+
+def test_indexer_noalloc_validation(lib):
+    """Argument errors and plans larger than the scratch array return before any device call."""
+    import sparse_indexed_attention_amd as m
+    assert _noalloc_call(lib, m, q=None) == 1
+    assert _noalloc_call(lib, m, ks=None) == 1
+    assert _noalloc_call(lib, m, qd=2) == 3
+    assert _noalloc_call(lib, m, K=4096) == 4
+    assert _noalloc_call(lib, m, out=A[4] + 4) == 6
+    lay, qs = _lq(m, maxb=3, maxv=200)
+    assert _noalloc_call(lib, m, layout=lay, queries=qs) == 2
+    # a chunked-prefill launch (4096 queries over a 69632-token context) needs far more
+    # candidate space than the scratch array holds
+    need = lib.dsa_indexer_topk_workspace_size(4096, 69632, 2048)
+    assert need > 32 << 20
+    lay = m.DsaLayout(64, 1088, A[8], 0, 1, 69632)
+    qs = m.DsaQueries(4096, A[9], A[10], 69632, 0)
+    assert _noalloc_call(lib, m, layout=lay, queries=qs) == 5
