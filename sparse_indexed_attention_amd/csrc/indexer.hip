@@ -1529,6 +1529,178 @@ __device__ __forceinline__ bool merge_select(const IndexerParams& p, int t, int 
   return true;
 }
 
+// ---------------------------------------------------------------------------------------
+// Selection over a list in LDS read four entries per lane (one 16-byte read), for the merge:
+// keys[0, n) with n a multiple of 4 and keys 16-byte aligned; key 0 marks padding and lies
+// below every real key.  Each pass issues one LDS read per four entries, so the merge's
+// passes cost a quarter of the instructions of one-entry-per-lane loops.
+// ---------------------------------------------------------------------------------------
+// rank_bin over the list (base >= 1, so padding never counts).
+__device__ __forceinline__ BinPick lst_rank_bin(const uint32_t* keys, int n, uint32_t base,
+                                                uint32_t width, int sh, int r, const Lds& L) {
+  int* hist = L.hist;
+  __syncthreads();   // earlier readers of the histogram are done
+  for (int i = threadIdx.x; i < kBins / 4; i += NT) *(int4*)(hist + 4 * i) = int4{0, 0, 0, 0};
+  __syncthreads();
+  const int nc = n >> 2;
+#pragma unroll 2
+  for (int c = threadIdx.x; c < nc; c += NT) {
+    const u32x4 k = *(const u32x4*)(keys + 4 * c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t o = k[u] - base;
+      if (o <= width) atomicAdd(&hist[o >> sh], 1);
+    }
+  }
+  __syncthreads();
+  return find_in_hist(r, L);
+}
+
+// The k-th largest key of the list, as radix_kth (every real key in [lo, hi], lo >= 1).
+__device__ __forceinline__ Kth lst_kth(const uint32_t* keys, int n, int k, uint32_t lo,
+                                       uint32_t hi, const Lds& L) {
+  uint32_t base = lo, width = hi - lo;
+  int above = 0;
+  const int lane = threadIdx.x & 63, nc = n >> 2;
+  for (;;) {
+    const int sh = range_shift(width);
+    const BinPick bp = lst_rank_bin(keys, n, base, width, sh, k - above, L);
+    base += (uint32_t)bp.d << sh;
+    if (sh == 0) return Kth{base, above + bp.above, above + bp.above + bp.c};
+    width = (1u << sh) - 1u;
+    if (bp.c > 64) {
+      above += bp.above;
+      continue;
+    }
+    // the c <= 64 keys of the bin, gathered into L.small and ranked within one wave
+    if (threadIdx.x == 0) L.bcast[3] = 0;
+    __syncthreads();
+    for (int c = threadIdx.x; c < nc; c += NT) {
+      const u32x4 kk = *(const u32x4*)(keys + 4 * c);
+      int m = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m += kk[u] - base <= width;
+      if (m) {
+        int at = atomicAdd(&L.bcast[3], m);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (kk[u] - base <= width) L.small[at++] = kk[u];
+      }
+    }
+    __syncthreads();
+    const int c = bp.c, r = k - above - bp.above;
+    const uint32_t v = lane < c ? L.small[lane] : 0u;
+    int gt = 0, ge = 0;
+    for (int j = 0; j < c; ++j) {
+      const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+      gt += w > v;
+      ge += w >= v;
+    }
+    const uint64_t hit = __ballot(lane < c && gt < r && r <= ge);
+    const int l = __builtin_ctzll(hit);
+    const int a = above + bp.above;
+    return Kth{(uint32_t)__builtin_amdgcn_readlane((int)v, l),
+               a + __builtin_amdgcn_readlane(gt, l), a + __builtin_amdgcn_readlane(ge, l)};
+  }
+}
+
+// Stable selection of the list in index order: entry i is taken if its key is above T, or
+// equal to T and fewer than `need` earlier entries equal to T were taken; taken entry number
+// s (in index order) writes pos[i] to out[s] (s < limit).  Wave w owns a contiguous range of
+// 4-entry chunks; within one step of 64 chunks a packed exclusive scan of the per-lane
+// (taken above T, equal to T) counts gives every lane its slots.
+__device__ __forceinline__ void lst_emit(const uint32_t* keys, const int32_t* pos, int n,
+                                         uint32_t T, int need, int32_t* out, float* out_score,
+                                         int limit, const Lds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nc = n >> 2;
+  const int cpw = (nc + NWAVE - 1) / NWAVE;
+  const int c0 = min(nc, wave * cpw), c1 = min(nc, c0 + cpw);
+  int g = 0, e = 0;
+  for (int c = c0 + lane; c < c1; c += 64) {
+    const u32x4 k = *(const u32x4*)(keys + 4 * c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      g += k[u] > T;
+      e += k[u] == T;
+    }
+  }
+  g = wave_scan_add(g);
+  e = wave_scan_add(e);
+  if (lane == 63) {
+    L.wcnt[wave] = g;
+    L.wcnt[NWAVE + wave] = e;
+  }
+  __syncthreads();
+  int slot = 0, eq = 0;   // taken entries and ties before this wave's range
+  for (int w = 0; w < wave; ++w) {
+    const int ew = L.wcnt[NWAVE + w];
+    slot += L.wcnt[w] + max(0, min(ew, need - eq));
+    eq += ew;
+  }
+  __syncthreads();
+  for (int cb = c0; cb < c1; cb += 64) {
+    const int c = cb + lane;
+    u32x4 k = {0u, 0u, 0u, 0u};
+    if (c < c1) k = *(const u32x4*)(keys + 4 * c);
+    int gl = 0, el = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      gl += k[u] > T;
+      el += k[u] == T;
+    }
+    // exclusive prefix of (above T, equal to T) over the lanes, packed 16:16 (<= 256 each)
+    const int incl = wave_scan_add(gl | (el << 16));
+    const int excl = incl - (gl | (el << 16));
+    const int tot = __builtin_amdgcn_readlane(incl, 63);
+    int gb = excl & 0xffff, eb = eq + (excl >> 16);
+    int s = slot + gb + max(0, min(eb - eq, need - eq));
+    if (gl | el) {
+      const i32x4 ps = *(const i32x4*)(pos + 4 * c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bool take = k[u] > T;
+        if (k[u] == T) take = eb++ < need;
+        if (take) {
+          if (s < limit) {
+            out[s] = ps[u];
+            if (out_score) out_score[s] = key_to_float(k[u]);
+          }
+          ++s;
+        }
+      }
+    }
+    slot += (tot & 0xffff) + max(0, min(tot >> 16, need - eq));
+    eq += tot >> 16;
+  }
+}
+
+// Selection over the staged list (keys fk, positions fp, in list order = position order),
+// with the LDS-resident, ballot-based routines of the single-split path: radix_kth finds the
+// exact K_eff-th key T with the counts above it (gt) and at or above it (ge); when every
+// split's threshold is at or below T the candidates provably hold the answer, and emit_sel
+// takes, in list order, every key above T and the first K_eff - gt keys equal to T, which
+// are the lowest positions among the tied ones.  The emission order is the output order.
+// Padding entries (key 0) lie below every real key and are never taken.  Returns 1 when the
+// output is written, 0 when a split's threshold lies above T (the caller re-scores), -1 when
+// the list does not qualify.
+__device__ __forceinline__ int merge_fast(const IndexerParams& p, int t, int K_eff,
+                                          const MergeHdr& mh, const uint32_t* fk,
+                                          const int32_t* fp, const Lds& L, uint32_t& T, int& gt,
+                                          bool& enough) {
+  enough = mh.n_real >= K_eff;
+  if (!enough) return -1;
+  const Kth kt = lst_kth(fk, mh.n, K_eff, mh.lo, mh.hi, L);
+  T = kt.T;
+  gt = kt.gt;
+  if (mh.max_tau > T) return 0;
+  lst_emit(fk, fp, mh.n, T, K_eff - gt, p.out_idx + (size_t)t * p.K,
+           p.out_score ? p.out_score + (size_t)t * p.K : nullptr, K_eff, L);
+  pad_output(p, t, K_eff);
+  if (threadIdx.x == 0) st_agent(p.counters + t, 0u);
+  return 1;
+}
+
 // Run starts from the headers, then the virtual list staged in LDS when it fits (keys;
 // positions too when there is room), then the selection.  T, gt and enough are kept for the
 // re-scoring of failing splits.
@@ -1562,6 +1734,10 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
   stage_runs(gk, gp, rs, nsplit, n, pre, fk, pos_in ? fp : nullptr);
   __syncthreads();
   auto lkey = [&](int v) { return fk[v]; };
+  if (pos_in) {
+    const int r = merge_fast(p, t, K_eff, mh, fk, fp, L, T, gt, enough);
+    if (r >= 0) return r == 1;
+  }
   if (pos_in) {
     auto lpos = [&](int v) { return fp[v]; };
     auto lpos_batch = [&](const int (&v)[kGatherU], int32_t (&ps)[kGatherU]) {
