@@ -159,7 +159,10 @@ size_t dsa_sparse_attn_workspace_size(int32_t num_queries, int32_t n_heads, int3
                                       int32_t d_v) {
   if (num_queries < 1 || n_heads < 1 || top_k < 1 || d_v < 1) return 0;
   // sized for the fast path, which needs at least as much as the reference path
-  return plan_sfa(num_queries, n_heads, top_k, d_v, n_heads % 32 == 0).bytes;
+  // the larger of the bf16-row and fp8-row plans (they may split the index list differently)
+  const size_t a = plan_sfa(num_queries, n_heads, top_k, d_v, n_heads % 32 == 0, false).bytes;
+  const size_t b = plan_sfa(num_queries, n_heads, top_k, d_v, n_heads % 32 == 0, true).bytes;
+  return a > b ? a : b;
 }
 
 dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool,
@@ -185,7 +188,7 @@ dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool,
     return DSA_ERR_ALIGN;
   const int32_t T = queries->num_queries;
   const bool fast = sfa_fast(dtype, n_heads, d_qk, d_v);
-  const SfaPlan pl = plan_sfa(T, n_heads, top_k, d_v, fast);
+  const SfaPlan pl = plan_sfa(T, n_heads, top_k, d_v, fast, kv_dtype == DSA_FP8_E4M3);
   if (!workspace || workspace_bytes < pl.bytes) return DSA_ERR_WORKSPACE;
 
   SfaParams p{};
@@ -203,6 +206,8 @@ dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool,
   p.dtype = dtype;
   p.kv_dtype = kv_dtype;
   p.heads_per_wg = pl.heads_per_wg;
+  p.decode64 = pl.decode64;
+  p.dim_waves = pl.dim_waves;
   p.n_hg = pl.n_hg;
   p.rows_per_split = pl.rows_per_split;
   p.nsplit = pl.nsplit;

@@ -76,6 +76,8 @@ constexpr int kSfaRowF8 = 656;        // fp8 latent row: 512 codes, 64 bf16, 4 f
 
 struct SfaPlan {
   int32_t heads_per_wg;   // heads handled by one workgroup (fast path)
+  int32_t decode64;       // 1: the 64-head, four-wave decode kernel
+  int32_t dim_waves;      // waves of an attention workgroup, each owning d_v / dim_waves dims
   int32_t n_hg;           // head groups
   int32_t rows_per_split; // selected rows per split (multiple of 32)
   int32_t nsplit;         // splits of top_k
@@ -93,6 +95,7 @@ struct SfaParams {
   int32_t dtype;
   int32_t kv_dtype;       // dtype, or kDtFP8 for the tile-quantized latent rows
   int32_t heads_per_wg, n_hg, rows_per_split, nsplit;
+  int32_t decode64, dim_waves;   // as in SfaPlan
   void* out;              // [T, H, d_v]
   float* lse;             // [T, H] or nullptr
   const void* zero;       // 16 zero bytes (source of the rows of absent positions)
@@ -101,7 +104,7 @@ struct SfaParams {
   float* part_ml;         // [T][H][nsplit][2] exponent reference (exp2 domain), sum
 };
 
-SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path);
+SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path, bool kv_fp8);
 hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream);
 
 // ------------------------------------------------------------------ cache writers

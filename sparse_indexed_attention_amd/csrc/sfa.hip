@@ -142,17 +142,10 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   const int nrows = min(p.K, j0 + p.rows_per_split) - j0;
   const int ntiles = (nrows + kTileRows - 1) / kTileRows;
 
-  // queries of this wave's 32 heads (lane holds head c, dims 16s + 8hh .. +7), loaded first:
-  // their latency overlaps that of the index and block-table reads below
-  bf16x8 qk[36];
-  {
-    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)t * p.H + h0 + c) * kSfaDqk + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qb + 16 * s);
-  }
-  // Pool rows of the slice.  The positions, and the sequence's whole block-table row when it
-  // fits in LDS, are requested together with the queries, so the lookup costs one memory round
-  // trip instead of two chained ones.
+  // Pool rows of the slice.  The positions and the sequence's whole block-table row (when it
+  // fits in LDS) are requested together, so the lookup costs one memory round trip; the first
+  // tiles are issued right after it, and the queries after those, so that the query reads
+  // overlap the row gather.
   constexpr int UI = kMaxTopK / NTS;                 // slice entries per thread (at most)
   int32_t posr[UI];
   {
@@ -190,6 +183,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   }
   __syncthreads();
 
+  // queries of this wave's 32 heads (lane holds head c, dims 16s + 8hh .. +7).  Issued after
+  // the first tiles: the first read of them waits for every load issued before, which by
+  // then are only the first tiles the attention step needs anyway.
+  bf16x8 qk[36];
+  auto load_queries = [&]() {
+    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)t * p.H + h0 + c) * kSfaDqk + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qb + 16 * s);
+  };
   const uint8_t* kv = (const uint8_t*)p.kv;
   const uint8_t* zero = (const uint8_t*)p.zero;
   // This wave's share of tile `tile`: loads I = wave, wave + NW, ...; lane l of load I fills
@@ -381,6 +383,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     // bf16 tile, which frees its staging buffer for the tile kStageBufs later
     static_assert(kStageBufs == 4 && 3 * LPW_MIN < 64, "waits below");
     for (int i = 0; i < kStageBufs && i < ntiles; ++i) issue(i, i);
+    load_queries();
     int buf = 0;
     for (int tile = 0; tile < ntiles; ++tile) {
       const int ahead = min(ntiles - 1 - tile, kStageBufs - 1);   // later tiles in flight
@@ -403,6 +406,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   if (ntiles > 0) issue(0, 0);
   if (ntiles > 1) issue(1, 1);
   if (ntiles > 2) issue(2, 2);
+  load_queries();
   int buf = 0;
   for (int tile = 0; tile < ntiles; ++tile) {
     const int ahead = min(ntiles - 1 - tile, kTileBufs - 1);   // later tiles in flight
@@ -475,6 +479,295 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     }
   }
   if (lane == 0) p.flags[((size_t)t * (p.H / 32) + hw) * p.nsplit + r] = flagword;
+}
+
+// Decode variant: a workgroup owns (query, group of 64 heads, slice of the index list) with
+// four waves, so a decode batch needs half the slices (and half the partial outputs) of the
+// 128-head workgroup for the same number of workgroups, and each reads half the queries.
+//   * Tiles are taken in pairs.  QK^T: wave w scores tile (w >> 1) of the pair for heads
+//     32 (w & 1) .. +31 of the group, exactly as above (tile rows the A operand, the wave's
+//     queries the B operand).  The two waves of a head half exchange their tile maxima through
+//     LDS, so both use the same exponent reference for the head (set by the first pair with a
+//     live row, never moved; heads that climb more than 64 above it are flagged).
+//   * P.V: wave w owns output dims 128 w .. +127 of all 64 heads over the pair's 64 rows
+//     (probabilities from the shared P tile, values through the transposing LDS read).
+//   * Four tile buffers: two pairs in flight.  The sequence's block-table row is staged in the
+//     last buffer before any tile is loaded.
+//   * Slices write O / l in fp16 in the record format of the 128-head kernel with two head
+//     blocks per wave (16 KB per wave), and (m, l) per head; the combine kernel merges them.
+constexpr int kRows64 = 512;                           // most slice entries of the decode variant
+constexpr int kPStride64 = 144;                        // bytes per head row of its P tile (64 rows)
+__global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
+  constexpr int NW = 4, NTS = 256;
+  constexpr int LPW = (kTileLoads + NW - 1) / NW, LPW_MIN = kTileLoads / NW;
+  constexpr int kBufs = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kBufs][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t plds[64 * kPStride64];
+  __shared__ int32_t rows[kRows64];
+  __shared__ float xmax[NW][32], xsum[NW][32];
+  __shared__ uint32_t xover[NW];
+  __shared__ __attribute__((aligned(16))) float hv[64];
+  static_assert(kBufs * kTileBytes + 64 * kPStride64 + 4 * kRows64 + 2 * NW * 32 * 4 + 16 + 256 <= 163840,
+                "LDS");
+
+  // workgroup -> (query, head group, slice): the head groups of one (query, slice) are 8
+  // apart, so consecutive workgroup numbers place them on one XCD, sharing its L2 for the rows
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7, qq = wg >> 3;
+  const int hg = qq % p.n_hg;
+  const int cc = (qq / p.n_hg) * 8 + xcd;
+  if (cc >= p.T * p.nsplit) return;
+  const int t = cc / p.nsplit, r = cc - t * p.nsplit;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, c = lane & 31;
+  const int hq = wave & 1, par = wave >> 1;        // QK^T: head half, tile of the pair
+  const int h0 = hg * 64 + hq * 32;                // first of this wave's QK^T heads
+  const int seq = p.q_seq[t];
+  const int j0 = r * p.rows_per_split;
+  const int nrows = min(p.K, j0 + p.rows_per_split) - j0;
+  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
+  const int npairs = (ntiles + 1) >> 1;
+
+  // pool rows of the slice (one memory round trip: positions and the block-table row together)
+  int32_t posr[kRows64 / NTS];
+  {
+    const int32_t* idx = p.idx + (size_t)t * p.K + j0;
+#pragma unroll
+    for (int u = 0; u < kRows64 / NTS; ++u) {
+      const int i = tid + u * NTS;
+      posr[u] = i < nrows ? idx[i] : -1;
+    }
+  }
+  int32_t* bt_lds = (int32_t*)tiles[kBufs - 1];
+  const bool stage_bt = p.L.bt != nullptr && p.L.bt_stride <= kBtLds;
+  if (stage_bt) {
+    const int32_t* btrow = p.L.bt + (size_t)seq * p.L.bt_stride;
+    for (int c0 = 64 * wave; c0 < p.L.bt_stride; c0 += NTS)
+      if (c0 + lane < p.L.bt_stride) load4_to_lds(btrow + c0 + lane, lds_u32(bt_lds + c0));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kRows64 / NTS; ++u) {
+    const int i = tid + u * NTS;
+    if (i < 2 * npairs * kTileRows) {
+      const int pos = posr[u];
+      int32_t row = -1;
+      if (pos >= 0) {
+        if (stage_bt) {
+          const int sh = p.L.bs_log2;
+          row = (bt_lds[pos >> sh] << sh) | (pos & ((1 << sh) - 1));
+        } else {
+          row = (int32_t)pool_row(p.L, seq, pos);
+        }
+      }
+      rows[i] = row;
+    }
+  }
+  __syncthreads();                                 // rows ready; the staged block table is free
+
+  const uint8_t* kv = (const uint8_t*)p.kv;
+  const uint8_t* zero = (const uint8_t*)p.zero;
+  // this wave's share of tile `tile` (see the 128-head kernel): rows without a position load
+  // from a zeroed chunk, so every wave issues the same number of loads per tile
+  auto issue = [&](int tile, int buf) {
+    uint8_t* tb = tiles[buf];
+    int z0 = 0;
+    asm volatile("" : "+v"(z0));
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int I = wave + NW * u;
+      if (LPW != LPW_MIN && I >= kTileLoads) break;
+      const int P = 64 * I + lane + z0;
+      const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
+      if (P < kTileSlots && ch < kRowChunks) {
+        const int row = rows[tile * kTileRows + rr];
+        load16_to_lds(row >= 0 ? kv + (size_t)row * kRowBytes + 16 * ch : zero, lds_u32(tb + 1024 * I));
+      }
+    }
+  };
+  auto issue_pair = [&](int pr) {
+    issue(2 * pr, 2 * (pr & 1));
+    issue(2 * pr + 1, 2 * (pr & 1) + 1);
+  };
+  issue_pair(0);
+  if (npairs > 1) issue_pair(1);
+  // queries of this wave's 32 heads, after the first tiles (their first use waits for every
+  // load issued before them)
+  bf16x8 qk[36];
+  {
+    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)t * p.H + h0 + c) * kSfaDqk + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qb + 16 * s);
+  }
+
+  const float scale2 = p.scale * kLog2e;
+  float m2 = -INFINITY, l = 0.f;
+  bool over = false;
+  f32x16 o[2][4];                                  // [head block][32-dim block of this wave]
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) o[hb][nb] = f32x16{};
+  const int vi = c & 15;
+  const int vrow = 4 * hh + (vi >> 2);
+  const int vdim = 16 * (c >> 4) + 4 * (vi & 3);
+
+  for (int pr = 0; pr < npairs; ++pr) {
+    const int b0 = 2 * (pr & 1);
+    if (pr + 1 < npairs) wait_vmcnt<(2 * LPW_MIN < 63 ? 2 * LPW_MIN : 63)>();   // the next pair may fly
+    else wait_vmcnt<0>();
+    __syncthreads();                               // every wave's loads of pair pr have landed
+    // S^T for tile 2 pr + par, heads h0 .. h0 + 31
+    const int tile = 2 * pr + par;
+    const uint8_t* tb = tiles[b0 + par];
+    const uint32_t valid = (uint32_t)__ballot(rows[tile * kTileRows + c] >= 0);
+    float z[16];
+    {
+      f32x16 sa = {};
+      const uint8_t* ra = tb + tile_off(c, hh);
+      bf16x8 a[2][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[0][u] = *(const bf16x8*)(ra + 32 * u);
+#pragma unroll
+      for (int g = 0; g < 9; ++g) {
+        if (g + 1 < 9) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) a[(g + 1) & 1][u] = *(const bf16x8*)(ra + 32 * (4 * (g + 1) + u));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[g & 1][u], qk[4 * g + u], sa, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint32_t mh = valid >> (4 * hh);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        z[e] = (mh >> (8 * (e >> 2) + (e & 3))) & 1u ? sa[e] * scale2 : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, z[e]);
+    mx = xhalf_max(mx);
+    if (hh == 0) xmax[wave][c] = mx;
+    __syncthreads();                               // both tiles' maxima of every head
+    mx = fmaxf(mx, xmax[wave ^ 2][c]);
+    if (m2 == -INFINITY) m2 = mx;                  // first pair with a live row of this head
+    over |= mx > m2 + 64.f;
+    const bool live = m2 != -INFINITY;
+    {
+      bf16x8 pw[2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float e0 = live ? __builtin_amdgcn_exp2f(z[u] - m2) : 0.f;
+        const float e1 = live ? __builtin_amdgcn_exp2f(z[8 + u] - m2) : 0.f;
+        l += e0 + e1;
+        pw[0][u] = (__bf16)e0;
+        pw[1][u] = (__bf16)e1;
+      }
+      // head row 32 hq + c, k steps 2 par and 2 par + 1 (this tile's rows)
+      uint8_t* prow = plds + (32 * hq + c) * kPStride64 + 64 * par + 16 * hh;
+      *(bf16x8*)prow = pw[0];
+      *(bf16x8*)(prow + 32) = pw[1];
+    }
+    __syncthreads();                               // every head's P of both tiles is in place
+    bf16x8 pa[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        pa[hb][kk] = *(const bf16x8*)(plds + (32 * hb + c) * kPStride64 + 32 * kk + 16 * hh);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int dim = 128 * wave + 32 * nb + vdim;
+      const int cho = tile_off(0, dim >> 3) + 2 * (dim & 7);
+      bf16x8 b[4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        s16x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(tiles[b0 + tt] + tile_off(8 * q + vrow, 0) + cho));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          b[2 * tt + kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[2 * kk], v[2 * kk + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          o[hb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb][kk], b[kk], o[hb][nb], 0, 0, 0);
+    }
+    __syncthreads();                               // the pair's buffers and the P tile are free
+    if (pr + 2 < npairs) issue_pair(pr + 2);
+  }
+
+  // per-head totals over the two tiles of each pair; flags of both waves of a head half
+  const float lw = xhalf_sum(l);
+  const uint32_t ow = (uint32_t)__ballot(over);
+  if (hh == 0) xsum[wave][c] = lw;
+  if (lane == 0) xover[wave] = ow;
+  __syncthreads();
+  const float lt = lw + xsum[wave ^ 2][c];
+  const uint32_t flagword = ow | xover[wave ^ 2];
+  if (par == 0 && hh == 0) hv[32 * hq + c] = lt > 0.f ? 1.f / lt : 0.f;
+  __syncthreads();
+  const int hgb = hg * 64;                         // first head of the workgroup
+  // accumulator (hb, nb) element 4j + i of lane (hh, c): head hgb + 32hb + 8j + 4hh + i,
+  // dim 128 wave + 32 nb + c
+  if (p.nsplit == 1) {
+    uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + hgb) * kSfaDv + 128 * wave + c;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 inv = *(const f32x4*)&hv[32 * hb + 8 * j + 4 * hh];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hd = 32 * hb + 8 * j + 4 * hh + i;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            out[hd * kSfaDv + 32 * nb] = __builtin_bit_cast(uint16_t, (__bf16)(o[hb][nb][4 * j + i] * inv[i]));
+        }
+      }
+    if (p.lse && par == 0 && hh == 0)
+      p.lse[(size_t)t * p.H + h0 + c] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
+  } else {
+    // O / l of this slice in fp16, records as the accumulators lie in the registers: record
+    // (hb*4 + j)*2 + np of lane (hh, c) holds heads 32hb + 8j + 4hh + i (i < 4) at dims
+    // 128 wave + 32(2np + s) + c (s < 2), value 4s + i; 16 KB per (query, head group, slice,
+    // wave)
+    uint8_t* po = (uint8_t*)p.part_o +
+                  ((((size_t)t * p.n_hg + hg) * p.nsplit + r) * NW + wave) * 16 * 1024 + 16 * lane;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 inv = *(const f32x4*)&hv[32 * hb + 8 * j + 4 * hh];
+#pragma unroll
+        for (int np = 0; np < 2; ++np) {
+          uint32_t w[4];
+#pragma unroll
+          for (int sd = 0; sd < 2; ++sd)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              const _Float16 a = (_Float16)(o[hb][2 * np + sd][4 * j + i] * inv[i]);
+              const _Float16 b = (_Float16)(o[hb][2 * np + sd][4 * j + i + 1] * inv[i + 1]);
+              w[2 * sd + i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+            }
+          *(u32x4*)(po + (size_t)((hb * 4 + j) * 2 + np) * 1024) = u32x4{w[0], w[1], w[2], w[3]};
+        }
+      }
+    if (par == 0 && hh == 0) {
+      float* pm = p.part_ml + (((size_t)t * p.H + h0 + c) * p.nsplit + r) * 2;
+      pm[0] = m2;
+      pm[1] = lt;
+    }
+  }
+  if (par == 0 && lane == 0) p.flags[((size_t)t * (p.H / 32) + hg * 2 + hq) * p.nsplit + r] = flagword;
 }
 
 // Reference computation of one (query, head), fp32 throughout, by the calling workgroup of
@@ -567,7 +860,8 @@ __global__ __launch_bounds__(kRefThreads) void sfa_reference_kernel(SfaParams p)
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSlices = 64;
 static_assert(kMaxTopK / kTileRows <= kMaxSlices, "a slice holds at least one tile");
-constexpr int kCombineBatch = 16;                    // partial loads in flight per thread
+// partial loads in flight per thread: the combine kernel is built for batches of 8 and 32
+// slices and launched with the one that covers the slices in one batch when it can
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -578,26 +872,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+template <int kCombineBatch>
 __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams p) {
   __shared__ RefSmem ws;
   __shared__ __attribute__((aligned(16))) float wgt[kMaxSlices][16];
   __shared__ uint32_t flagged, nonfinite;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int NW = p.heads_per_wg / 32;                 // waves (dim ranges) of the MFMA kernel
-  const int DW = kSfaDv / NW, NB = DW / 32;
+  const int HB = p.heads_per_wg / 32;                 // 32-head blocks of an attention workgroup
+  const int DWV = p.dim_waves;                        // its waves, each owning DW output dims
+  const int DW = kSfaDv / DWV, NB = DW / 32;
   const int half = blockIdx.x & 1;
-  const int hb = (blockIdx.x >> 1) % NW;
-  const int w = (blockIdx.x >> 1) / NW % NW;
-  const int hg = (blockIdx.x >> 1) / (NW * NW);
+  const int hb = (blockIdx.x >> 1) % HB;
+  const int w = (blockIdx.x >> 1) / HB % DWV;
+  const int hg = (blockIdx.x >> 1) / (HB * DWV);
   const int t = blockIdx.y;
-  const int hw = hg * NW + hb;                        // 32-head block
+  const int hw = hg * HB + hb;                        // 32-head block
   const int hb0 = hw * 32 + 16 * half;                // heads hb0 .. hb0 + 15
   const int S = p.nsplit;
-  // slot (record, lane): record (hb*4 + j)*(NB/2) + np with j = 2*half + jl, value 4s + i:
-  // head hb0 + 8jl + 4hh + i, dim DW*w + 32(2np + s) + c
   const int nslot = NB * 64;
-  const uint8_t* blk = (const uint8_t*)p.part_o + (((size_t)t * p.n_hg + hg) * S * NW + w) * 32 * 1024;
-  const size_t rstride = (size_t)NW * 32 * 1024;      // from one slice to the next
+  const size_t wbytes = (size_t)HB * 4 * (NB / 2) * 1024;   // records of one attention wave
+  const uint8_t* blk = (const uint8_t*)p.part_o + (((size_t)t * p.n_hg + hg) * S * DWV + w) * wbytes;
+  const size_t rstride = (size_t)DWV * wbytes;        // from one slice to the next
   if (wave == 0) {
     uint32_t f = lane < S ? p.flags[((size_t)t * (p.H / 32) + hw) * S + lane] : 0u;
     for (int off = 32; off >= 1; off >>= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
@@ -606,6 +901,18 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
       nonfinite = 0u;
     }
   }
+  // slot (record, lane) of this thread: record (hb*4 + j)*(NB/2) + np with j = 2*half + jl,
+  // value 4s + i: head hb0 + 8jl + 4hh + i, dim DW*w + 32(2np + s) + c
+  auto src_of = [&](int slot) {
+    const int ln = slot & 63, rl = slot >> 6;
+    const int rec = (hb * 4 + 2 * half + rl / (NB / 2)) * (NB / 2) + rl % (NB / 2);
+    return blk + (size_t)rec * 1024 + 16 * ln;
+  };
+  // Every load of the first batch is issued before any is used: the (m, l) pairs, then this
+  // thread's records of the first kCombineBatch slices of its first slot, so that the weights
+  // are computed while the partials are in flight and a combine of up to kCombineBatch slices
+  // costs one memory round trip.
+  u32x4 v0[kCombineBatch];
   if (S > 1) {
     // weights of heads 4*wave .. 4*wave + 3 (of the 16), lane r holding slice r
     float m[4], lv[4];
@@ -619,6 +926,10 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
         lv[k] = a.y;
       }
     }
+    const uint8_t* src = src_of(tid);
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      v0[u] = u < S ? *(const u32x4*)(src + (size_t)u * rstride) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float M = wave_max(m[k]);
@@ -632,17 +943,11 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
   __syncthreads();
   if (S > 1) {
     for (int slot = tid; slot < nslot; slot += kCombineThreads) {
-      const int ln = slot & 63, rl = slot >> 6;        // lane of the record, record of the WG
-      const int jl = rl / (NB / 2), np = rl % (NB / 2);
-      const int rec = (hb * 4 + 2 * half + jl) * (NB / 2) + np;
+      const int ln = slot & 63, jl = (slot >> 6) / (NB / 2), np = (slot >> 6) % (NB / 2);
       const int hh = ln >> 5, c = ln & 31;
-      const uint8_t* src = blk + (size_t)rec * 1024 + 16 * ln;
+      const uint8_t* src = src_of(slot);
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int r0 = 0; r0 < S; r0 += kCombineBatch) {
-        u32x4 v[kCombineBatch];
-#pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
-          v[u] = r0 + u < S ? *(const u32x4*)(src + (size_t)(r0 + u) * rstride) : u32x4{0u, 0u, 0u, 0u};
+      auto accumulate = [&](const u32x4 (&v)[kCombineBatch], int r0) {
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
           const f32x4 wr = r0 + u < S ? *(const f32x4*)&wgt[r0 + u][8 * jl + 4 * hh] : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -652,6 +957,15 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
             acc[e] += wr[e & 3] * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
           }
         }
+      };
+      for (int r0 = 0; r0 < S; r0 += kCombineBatch) {
+        // the first batch of the first slot was loaded before the weights
+        if (slot != (int)tid || r0 != 0) {
+#pragma unroll
+          for (int u = 0; u < kCombineBatch; ++u)
+            v0[u] = r0 + u < S ? *(const u32x4*)(src + (size_t)(r0 + u) * rstride) : u32x4{0u, 0u, 0u, 0u};
+        }
+        accumulate(v0, r0);
       }
       const uint32_t skip = flagged >> (8 * jl + 4 * hh);
       uint16_t* out = (uint16_t*)p.out + ((size_t)t * p.H + hb0 + 8 * jl + 4 * hh) * kSfaDv + DW * w + 64 * np + c;
@@ -706,7 +1020,7 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_flag_fixup_kernel(SfaPara
 
 }  // namespace
 
-SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path) {
+SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path, bool kv_fp8) {
   SfaPlan pl{};
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   if (!fast_path) {
@@ -720,16 +1034,29 @@ SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path) {
     // slices (at most 1024 rows each) until about one workgroup per CU runs.
     const bool wide = (int64_t)T * (H / 128) >= 256;
     pl.heads_per_wg = (H % 128 == 0) ? 128 : (H % 64 == 0) ? 64 : 32;
-    if (const int v = plan_overrides().sfa_hpw; (v == 32 || v == 64 || v == 128) && H % v == 0)
+    // Small decode batches with bf16 rows take the 64-head variant.  A workgroup of either
+    // kind reads its heads' queries plus its slice's rows: with at most 16 queries' worth of
+    // 128-head groups the 128-head slices hold at most 128 rows, fewer bytes than the 147 KB
+    // of queries, and halving the heads while doubling the rows reads the same bytes and
+    // writes half the partial outputs; with more queries the rows dominate and the 128-head
+    // workgroup reads less.
+    pl.decode64 = !wide && !kv_fp8 && H % 64 == 0 && (int64_t)T * (H / 64) <= 32;
+    if (pl.decode64) pl.heads_per_wg = 64;
+    if (const int v = plan_overrides().sfa_hpw; (v == 32 || v == 64 || v == 128) && H % v == 0) {
       pl.heads_per_wg = v;
+      pl.decode64 = v == 64 && !kv_fp8;
+    }
     pl.n_hg = H / pl.heads_per_wg;
+    pl.dim_waves = pl.decode64 ? 4 : pl.heads_per_wg / 32;
     const int64_t max_ns = (K + kTileRows - 1) / kTileRows;
     int64_t ns = 1;
     if (!wide) {
       const int64_t want = 256;
       ns = (want + (int64_t)T * pl.n_hg - 1) / ((int64_t)T * pl.n_hg);
       if (plan_overrides().sfa_splits > 0) ns = plan_overrides().sfa_splits;
-      const int64_t min_ns = (K + 1023) / 1024;
+      // slices of at most 1024 rows (kRows64 = 512 for the 64-head variant)
+      const int64_t cap = pl.decode64 ? kRows64 : 1024;
+      const int64_t min_ns = (K + cap - 1) / cap;
       if (ns < min_ns) ns = min_ns;
     }
     if (ns > max_ns) ns = max_ns;
@@ -760,7 +1087,9 @@ hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream) {
   const int pairs = (p.T * p.nsplit + 7) / 8 * 8;
   const dim3 grid(pairs * p.n_hg);
   const bool f8 = p.kv_dtype == kDtFP8;
-  switch (p.heads_per_wg) {
+  if (p.decode64) {
+    hipLaunchKernelGGL(sfa_mfma64_kernel, grid, dim3(256), 0, stream, p);
+  } else switch (p.heads_per_wg) {
     case 128:
       if (f8) hipLaunchKernelGGL((sfa_mfma_kernel<4, true>), grid, dim3(256), 0, stream, p);
       else hipLaunchKernelGGL((sfa_mfma_kernel<4, false>), grid, dim3(256), 0, stream, p);
@@ -778,9 +1107,10 @@ hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream) {
   if (e != hipSuccess) return e;
   // merges the slices, and recomputes any flagged head (with one slice it only checks flags)
   if (p.nsplit > 1) {
-    const int nw = p.heads_per_wg / 32;
-    hipLaunchKernelGGL(sfa_combine_kernel, dim3(p.n_hg * nw * nw * 2, p.T), dim3(kCombineThreads), 0,
-                       stream, p);
+    const int hb = p.heads_per_wg / 32;
+    const dim3 cg(p.n_hg * hb * p.dim_waves * 2, p.T);
+    if (p.nsplit <= 8) hipLaunchKernelGGL(sfa_combine_kernel<8>, cg, dim3(kCombineThreads), 0, stream, p);
+    else hipLaunchKernelGGL(sfa_combine_kernel<32>, cg, dim3(kCombineThreads), 0, stream, p);
   } else {
     const int words = p.T * (p.H / 32);
     hipLaunchKernelGGL(sfa_flag_fixup_kernel, dim3((words + kCombineThreads - 1) / kCombineThreads),
