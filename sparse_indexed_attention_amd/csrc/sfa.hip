@@ -448,11 +448,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
       p.lse[(size_t)t * p.H + h0 + c] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
   } else {
     // Partial of this slice: O / l in fp16, stored as the accumulators lie in the registers,
-    // one 32 KB block per (query, head group, slice, wave).  Record (hb*4 + j)*(NB/2) + np of
-    // lane (hh, c) holds heads 32hb + 8j + 4hh + i (i < 4) at dims DW*wave + 32(2np + s) + c
-    // (s < 2), value 4s + i.
+    // 32 records of 1 KB (16 bytes per lane) per (query, head group, slice, wave).  Record
+    // (hb*4 + j)*(NB/2) + np of lane (hh, c) holds heads 32hb + 8j + 4hh + i (i < 4) at dims
+    // DW*wave + 32(2np + s) + c (s < 2), value 4s + i.  Record rec of (query, head group,
+    // wave) for slice r lies at ((qhw * NREC + rec) * nsplit + r) KB: the slices of one record
+    // are adjacent, so the merge reads them 1 KB apart (with the slice outermost, 32 to 128 KB
+    // apart, the merge read measured slower)
+    constexpr int NREC = NW * 4 * (NB / 2);
     uint8_t* po = (uint8_t*)p.part_o +
-                  ((((size_t)t * p.n_hg + hg) * p.nsplit + r) * NW + wave) * 32 * 1024 + 16 * lane;
+                  ((((size_t)t * p.n_hg + hg) * NW + wave) * NREC * p.nsplit + r) * 1024 + 16 * lane;
 #pragma unroll
     for (int hb = 0; hb < NW; ++hb)
 #pragma unroll
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
               const _Float16 b = (_Float16)(o[hb * NB + 2 * np + sd][4 * j + i + 1] * inv[i + 1]);
               w[2 * sd + i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
             }
-          *(u32x4*)(po + (size_t)((hb * 4 + j) * (NB / 2) + np) * 1024) = u32x4{w[0], w[1], w[2], w[3]};
+          *(u32x4*)(po + (size_t)((hb * 4 + j) * (NB / 2) + np) * p.nsplit * 1024) = u32x4{w[0], w[1], w[2], w[3]};
         }
       }
     if (hh == 0) {
@@ -740,8 +744,9 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
     // (hb*4 + j)*2 + np of lane (hh, c) holds heads 32hb + 8j + 4hh + i (i < 4) at dims
     // 128 wave + 32(2np + s) + c (s < 2), value 4s + i; 16 KB per (query, head group, slice,
     // wave)
+    // (slices of one record adjacent, as in the 128-head kernel: 16 records per wave)
     uint8_t* po = (uint8_t*)p.part_o +
-                  ((((size_t)t * p.n_hg + hg) * p.nsplit + r) * NW + wave) * 16 * 1024 + 16 * lane;
+                  ((((size_t)t * p.n_hg + hg) * NW + wave) * 16 * p.nsplit + r) * 1024 + 16 * lane;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -758,7 +763,7 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
               const _Float16 b = (_Float16)(o[hb][2 * np + sd][4 * j + i + 1] * inv[i + 1]);
               w[2 * sd + i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
             }
-          *(u32x4*)(po + (size_t)((hb * 4 + j) * 2 + np) * 1024) = u32x4{w[0], w[1], w[2], w[3]};
+          *(u32x4*)(po + (size_t)((hb * 4 + j) * 2 + np) * p.nsplit * 1024) = u32x4{w[0], w[1], w[2], w[3]};
         }
       }
     if (par == 0 && hh == 0) {
@@ -890,9 +895,9 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
   const int hb0 = hw * 32 + 16 * half;                // heads hb0 .. hb0 + 15
   const int S = p.nsplit;
   const int nslot = NB * 64;
-  const size_t wbytes = (size_t)HB * 4 * (NB / 2) * 1024;   // records of one attention wave
-  const uint8_t* blk = (const uint8_t*)p.part_o + (((size_t)t * p.n_hg + hg) * S * DWV + w) * wbytes;
-  const size_t rstride = (size_t)DWV * wbytes;        // from one slice to the next
+  const int nrec = HB * 4 * (NB / 2);                 // records of one attention wave
+  const uint8_t* blk = (const uint8_t*)p.part_o + (((size_t)t * p.n_hg + hg) * DWV + w) * nrec * S * 1024;
+  const size_t rstride = 1024;                        // from one slice to the next
   if (wave == 0) {
     uint32_t f = lane < S ? p.flags[((size_t)t * (p.H / 32) + hw) * S + lane] : 0u;
     for (int off = 32; off >= 1; off >>= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
@@ -906,7 +911,7 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
   auto src_of = [&](int slot) {
     const int ln = slot & 63, rl = slot >> 6;
     const int rec = (hb * 4 + 2 * half + rl / (NB / 2)) * (NB / 2) + rl % (NB / 2);
-    return blk + (size_t)rec * 1024 + 16 * ln;
+    return blk + (size_t)rec * S * 1024 + 16 * ln;
   };
   // Every load of the first batch is issued before any is used: the (m, l) pairs, then this
   // thread's records of the first kCombineBatch slices of its first slot, so that the weights
