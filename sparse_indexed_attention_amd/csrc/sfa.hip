@@ -401,7 +401,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     }
   } else {
   // Tiles stream through kTileBufs LDS buffers, kTileBufs - 1 of them ahead of the one being
-  // computed.
+  // computed.  (Issuing tile i + 2 after the barrier that opens tile i, which would save the
+  // second barrier per tile, measured slower on chunked prefill: the gather needs the lead.)
   static_assert(kTileBufs == 3, "prologue below issues three tiles");
   if (ntiles > 0) issue(0, 0);
   if (ntiles > 1) issue(1, 1);
@@ -621,9 +622,13 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
 
   for (int pr = 0; pr < npairs; ++pr) {
     const int b0 = 2 * (pr & 1);
-    if (pr + 1 < npairs) wait_vmcnt<(2 * LPW_MIN < 63 ? 2 * LPW_MIN : 63)>();   // the next pair may fly
+    // Pairs 0 and 1 are issued before the loop, pair pr + 1 (pr >= 1) right after pair pr
+    // opens: so only at pair 0 is a later pair in flight while waiting.
+    if (pr == 0 && npairs > 1) wait_vmcnt<(2 * LPW_MIN < 63 ? 2 * LPW_MIN : 63)>();
     else wait_vmcnt<0>();
-    __syncthreads();                               // every wave's loads of pair pr have landed
+    __syncthreads();                               // every wave's loads of pair pr have landed,
+                                                   // and every wave is done with pair pr - 1
+    if (pr >= 1 && pr + 1 < npairs) issue_pair(pr + 1);   // into pair pr - 1's buffers
     // S^T for tile 2 pr + par, heads h0 .. h0 + 31
     const int tile = 2 * pr + par;
     const uint8_t* tb = tiles[b0 + par];
@@ -705,8 +710,6 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
         for (int kk = 0; kk < 4; ++kk)
           o[hb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb][kk], b[kk], o[hb][nb], 0, 0, 0);
     }
-    __syncthreads();                               // the pair's buffers and the P tile are free
-    if (pr + 2 < npairs) issue_pair(pr + 2);
   }
 
   // per-head totals over the two tiles of each pair; flags of both waves of a head half

@@ -49,6 +49,11 @@ CASES = {
     "tiny_fp32_sharp": (lambda: workload(1), "sharp"),
     "bf16_h128_T3": (lambda: scaled_spec(workload(2), seq_lens=[5000, 2500, 40000]), "sharp"),
     "bf16_h128_T40": (lambda: scaled_spec(workload(2), seq_lens=[3000] * 40), "sharp"),
+    # 64-head decode workgroups with 3 and 4 tile pairs per slice (12 and 16 queries)
+    "bf16_h128_T12_pairs3": (lambda: scaled_spec(workload(2), seq_lens=[2500 + 97 * i for i in range(12)]),
+                             "sharp"),
+    "bf16_h128_T16_pairs4": (lambda: scaled_spec(workload(2), seq_lens=[2100 + 31 * i for i in range(16)]),
+                             "sharp"),
     "bf16_h32_k100": (lambda: scaled_spec(workload(2), seq_lens=[500, 700], sfa_heads=32,
                                           top_k=100), "sharp"),
     "bf16_h16_k1": (lambda: scaled_spec(workload(2), seq_lens=[64, 99], sfa_heads=16, top_k=1),
