@@ -10,8 +10,8 @@ What is computed (for one query t of sequence b that sees positions [0, V)):
     Top-K   = the K_eff = min(K, V) positions with the largest S32, the lower position
               first among equal scores
 
-The three steps are the pages' "relevance scoring, head weight weighting, and Top-K
-selection" ("Day0 Adaptation and Performance Optimization for Novel Long-Sequence Reasoning
+The three steps follow the pages' description of the indexer as relevance scores, combined
+under per-head weights, then a Top-K selection ("Day0 Adaptation and Performance Optimization for Novel Long-Sequence Reasoning
 Models", section 3; "Optimizing and Deploying Ultra-Long Sequence Inference Architectures",
 section I; "Large Model Inference Acceleration: Day-0 Adaptation...", section 1.1, where the
 per-head scores are the Batch x Head x Seq intermediate of section 2.1).  The pages give no
