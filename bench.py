@@ -350,6 +350,10 @@ def main():
                          "other (each one device's share at its real shape)")
     ap.add_argument("--layout", choices=("zigzag", "contiguous"), default="zigzag",
                     help="how --shards cuts the chunk of queries")
+    ap.add_argument("--order", choices=("natural", "zigzag"), default="natural",
+                    help="query order of the unsharded launch: zigzag pairs the 4-query tiles "
+                         "head and tail (0, B-1, 1, B-2, ...), the workgroup-level pairing of short "
+                         "and long causal histories; it changes only the order (and so the timing)")
     ap.add_argument("--prolog", action="store_true",
                     help="time the indexer prolog (projections, key RMSNorm, query quantization, "
                          "key store) for the workload's new tokens instead of the step")
@@ -445,6 +449,17 @@ def main():
     if args.shards:
         shard_bench(args, dsa, torch, spec, inp, base, layouts[0])
         return
+    if args.order == "zigzag":
+        # tiles of 4 consecutive queries (one multi-query indexer workgroup each) in head-tail
+        # order; every copy of the inputs is permuted the same way
+        nb = (T + 3) // 4
+        blocks = [b for i in range((nb + 1) // 2) for b in ((i, nb - 1 - i) if i != nb - 1 - i else (i,))]
+        perm = torch.tensor([q for b in blocks for q in range(4 * b, min(T, 4 * b + 4))],
+                            dtype=torch.int64, device="cuda")
+        for d in devs:
+            for f in ("q_idx", "w", "q_sfa", "q_seq", "q_visible"):
+                setattr(d, f, getattr(d, f).index_select(0, perm).contiguous())
+        args.no_cpu_baseline = True
     ws_i = dsa.zeroed_workspace(dsa.indexer_workspace_bytes(T, base.max_visible, K), "cuda")
     ws_s = dsa.zeroed_workspace(dsa.sfa_workspace_bytes(T, spec.sfa_heads, K, spec.d_v), "cuda")
     outs = []
@@ -524,8 +539,11 @@ def main():
     # (5% allowed for run-to-run noise between the two measurements)
     consistent = idx_mean + sfa_mean <= step_ms * 1.05
     achieved = step_bytes_idx / (idx_mean * 1e-3) / 1e9
+    # counter-measured bytes only for the workload the committed counters were taken on
     traffic, prof_wl = counter_traffic("indexer")
     sfa_traffic, _ = counter_traffic("sparse_attn")
+    if prof_wl != spec.name:
+        traffic = sfa_traffic = None
     print(f"bench: step {step_ms * 1e3:.1f} us (host enqueue {t_host * 1e6 / args.steps:.1f} us); "
           f"indexer {idx_mean * 1e3:.1f} us (median {np.median(idx_us):.1f}, p10 "
           f"{np.percentile(idx_us, 10):.1f}, p90 {np.percentile(idx_us, 90):.1f}), "
@@ -587,6 +605,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": spec.name,
+            "query_order": args.order,
             "queries_per_step": T,
             "context": {"min": min(V), "max": max(V), "mean": float(np.mean(V))},
             "top_k": K,

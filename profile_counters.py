@@ -2,6 +2,7 @@
 
     python profile_counters.py hbm  [--config 4] [--out DIR]   # FETCH_SIZE / WRITE_SIZE
     python profile_counters.py mfma [--config 3] [--out DIR]   # MFMA busy cycles and ops
+    python profile_counters.py balance [--config 6] [--out DIR] # CU busy fraction, occupancy
 
 Each counter pass is its own `rocprofv3 --pmc ... -- python3 bench.py ...` child process (the
 profiler's library must start with the program, so this script never touches the GPU
@@ -18,6 +19,12 @@ mfma: SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16
 dispatch.  Utilisation = busy cycles / (GUI-active cycles x 1024 SIMDs), the profiler's own
 MfmaUtil definition; flops = MOPS x 512; the durations come from a kernel-trace pass of the
 same command.  A Markdown table is printed.
+
+balance: the profiler's derived SIMD_UTILIZATION (summed SQ_BUSY_CU_CYCLES over the clock count
+and the CU count), OccupancyPercent and MeanOccupancyPerActiveCU per dispatch, with the
+durations of a kernel-trace pass, for the natural query order and for bench.py's zigzag order
+(4-query tiles paired head and tail).  A kernel whose work is spread evenly keeps its CUs busy
+to its end; CUs left idle while a few long workgroups finish would show as a low busy fraction.
 """
 from __future__ import annotations
 
@@ -179,18 +186,43 @@ def mfma(args):
     print("commands:\n" + "\n".join("    cd /tmp && export TMPDIR=/tmp && " + c for c in (c1, c2, c3)))
 
 
+def balance(args):
+    rows, cmds = [], []
+    for order in ("natural", "zigzag"):
+        ba = ["--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--config", str(args.config),
+              "--order", order]
+        d, c1 = run_prof(args.out, f"balance_{order}",
+                         ["--pmc", "SIMD_UTILIZATION", "OccupancyPercent", "MeanOccupancyPerActiveCU"], ba, 600)
+        ctr, n = counters_per_kernel(d)
+        d, c2 = run_prof(args.out, f"balance_trace_{order}", ["--kernel-trace"], ba, 600)
+        dur = durations(d)
+        cmds += [c1, c2]
+        for k in sorted(ctr):
+            if call_of(k):
+                cs = ctr[k]
+                rows.append(f"| {order} | `{k}` | {n[k]} | {dur.get(k, (0, float('nan')))[1]:.1f} | "
+                            f"{cs.get('SIMD_UTILIZATION', float('nan')):.3f} | "
+                            f"{cs.get('OccupancyPercent', float('nan')):.1f} | "
+                            f"{cs.get('MeanOccupancyPerActiveCU', float('nan')):.2f} |")
+    print(f"workload {bench_workload(args.config)}")
+    print("| query order | kernel | dispatches | mean us | SIMD_UTILIZATION | OccupancyPercent | MeanOccupancyPerActiveCU |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    print("\n".join(rows))
+    print("commands:\n" + "\n".join("    cd /tmp && export TMPDIR=/tmp && " + c for c in cmds))
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=("hbm", "mfma"))
+    ap.add_argument("mode", choices=("hbm", "mfma", "balance"))
     ap.add_argument("--config", type=int, default=None)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "counters"))
     ap.add_argument("--write", action="store_true",
                     help="hbm: write profiles/decode_counters.json (else into --out)")
     args = ap.parse_args()
     if args.config is None:
-        args.config = 4 if args.mode == "hbm" else 3
+        args.config = {"hbm": 4, "mfma": 3, "balance": 6}[args.mode]
     os.makedirs(args.out, exist_ok=True)
-    hbm(args) if args.mode == "hbm" else mfma(args)
+    {"hbm": hbm, "mfma": mfma, "balance": balance}[args.mode](args)
 
 
 if __name__ == "__main__":

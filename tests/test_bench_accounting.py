@@ -50,3 +50,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_committed_counter_summary_matches_the_kernel_sources():
+    """The committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy
+    kernel's reading) was taken on the current kernel sources, so the bench line of its workload
+    carries counter-measured HBM traffic for both calls of the decode step."""
+    idx, wl = bench.counter_traffic("indexer")
+    sfa, wl_sfa = bench.counter_traffic("sparse_attn")
+    assert wl == wl_sfa == workload(4).name
+    assert idx is not None and sfa is not None, "counters were taken on other kernel sources"
+    spec = workload(4)
+    from synth import make_inputs
+    V = [int(v) for v in make_inputs(spec, seed=4, with_sfa=False).q_visible]
+    alg = bench.indexer_bytes(spec, V)
+    # the keys are read once: the measured traffic is the algorithmic bytes plus a few percent
+    assert alg <= idx <= 1.25 * alg
