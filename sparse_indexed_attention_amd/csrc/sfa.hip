@@ -497,7 +497,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
 //   * P.V: wave w owns output dims 128 w .. +127 of all 64 heads over the pair's 64 rows
 //     (probabilities from the shared P tile, values through the transposing LDS read).
 //   * Four tile buffers: two pairs in flight.  The sequence's block-table row is staged in the
-//     last buffer before any tile is loaded.
+//     last buffer before any tile is loaded, and the workgroup's query rows in the last two
+//     (while pair 0 lands) before pair 1 is.
 //   * Slices write O / l in fp16 in the record format of the 128-head kernel with two head
 //     blocks per wave (16 KB per wave), and (m, l) per head; the combine kernel merges them.
 constexpr int kRows64 = 512;                           // most slice entries of the decode variant
@@ -598,15 +599,31 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
     issue(2 * pr + 1, 2 * (pr & 1) + 1);
   };
   issue_pair(0);
-  if (npairs > 1) issue_pair(1);
-  // queries of this wave's 32 heads, after the first tiles (their first use waits for every
-  // load issued before them)
+  // The workgroup's 64 query rows (73.7 KB, contiguous) land in buffers 2 and 3 as one 64-row
+  // tile in the padded row layout, behind pair 0's tiles; each wave then reads its 32 heads'
+  // fragments from there.  Two waves share each head half, so loading the fragments from
+  // global memory directly would fetch every query twice.  Pair 1 goes into the same buffers
+  // once every wave has its fragments.
+  {
+    const uint8_t* qrows = (const uint8_t*)p.q + ((size_t)t * p.H + hg * 64) * kRowBytes;
+    constexpr int QLOADS = 2 * kTileSlots / 64;    // 73: 64 rows of 73 slots
+    static_assert(2 * kTileSlots % 64 == 0, "query tile");
+    for (int I = wave; I < QLOADS; I += NW) {
+      const int P = 64 * I + lane;
+      const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
+      if (ch < kRowChunks) load16_to_lds(qrows + (size_t)rr * kRowBytes + 16 * ch, lds_u32(tiles[2] + 1024 * I));
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();                                 // pair 0 and the query tile have landed
   bf16x8 qk[36];
   {
-    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)t * p.H + h0 + c) * kSfaDqk + 8 * hh;
+    const uint8_t* qr = tiles[2] + tile_off(32 * hq + c, hh);   // head 32 hq + c, dims 8 hh + 16 s
 #pragma unroll
-    for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qb + 16 * s);
+    for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qr + 32 * s);
   }
+  __syncthreads();                                 // every wave holds its fragments
+  if (npairs > 1) issue_pair(1);
 
   const float scale2 = p.scale * kLog2e;
   float m2 = -INFINITY, l = 0.f;
@@ -868,8 +885,11 @@ __global__ __launch_bounds__(kRefThreads) void sfa_reference_kernel(SfaParams p)
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSlices = 64;
 static_assert(kMaxTopK / kTileRows <= kMaxSlices, "a slice holds at least one tile");
-// partial loads in flight per thread: the combine kernel is built for batches of 8 and 32
-// slices and launched with the one that covers the slices in one batch when it can
+// partial loads in flight per thread: the combine kernel is built for batches of 8, 16 and 32
+// slices and launched with the smallest that covers the slices in one batch (a batch's
+// records take 4 VGPRs each, and a larger batch than needed costs registers: at 32 the kernel
+// runs one workgroup per SIMD and moves the first loads' results through AGPRs, which makes
+// the compiler wait for them before the rest of the batch is issued)
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -901,14 +921,13 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
   const int nrec = HB * 4 * (NB / 2);                 // records of one attention wave
   const uint8_t* blk = (const uint8_t*)p.part_o + (((size_t)t * p.n_hg + hg) * DWV + w) * nrec * S * 1024;
   const size_t rstride = 1024;                        // from one slice to the next
-  if (wave == 0) {
-    uint32_t f = lane < S ? p.flags[((size_t)t * (p.H / 32) + hw) * S + lane] : 0u;
-    for (int off = 32; off >= 1; off >>= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
-    if (lane == 0) {
-      flagged = (f >> (16 * half)) & 0xffffu;
-      nonfinite = 0u;
-    }
-  }
+  // the slices' flag words of this 32-head block (wave 0, lane r: slice r), reduced once the
+  // other loads are in flight
+  // (loads from clamped addresses, masked at use: a load under a lane condition made the
+  // compiler wait for it in place)
+  const int sl = min(lane, S - 1);
+  uint32_t fl = 0u;
+  if (wave == 0) fl = p.flags[((size_t)t * (p.H / 32) + hw) * S + sl];
   // slot (record, lane) of this thread: record (hb*4 + j)*(NB/2) + np with j = 2*half + jl,
   // value 4s + i: head hb0 + 8jl + 4hh + i, dim DW*w + 32(2np + s) + c
   auto src_of = [&](int slot) {
@@ -916,36 +935,38 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
     const int rec = (hb * 4 + 2 * half + rl / (NB / 2)) * (NB / 2) + rl % (NB / 2);
     return blk + (size_t)rec * S * 1024 + 16 * ln;
   };
-  // Every load of the first batch is issued before any is used: the (m, l) pairs, then this
-  // thread's records of the first kCombineBatch slices of its first slot, so that the weights
-  // are computed while the partials are in flight and a combine of up to kCombineBatch slices
-  // costs one memory round trip.
+  // Every load of the first batch is issued before any is used: the flags, the (m, l) pairs,
+  // then this thread's records of the first kCombineBatch slices of its first slot, so that
+  // the weights are computed while the partials are in flight and a combine of up to
+  // kCombineBatch slices costs one memory round trip.
   u32x4 v0[kCombineBatch];
   if (S > 1) {
     // weights of heads 4*wave .. 4*wave + 3 (of the 16), lane r holding slice r
-    float m[4], lv[4];
+    float2 a[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      m[k] = -INFINITY;
-      lv[k] = 0.f;
-      if (lane < S) {
-        const float2 a = *(const float2*)(p.part_ml + (((size_t)t * p.H + hb0 + 4 * wave + k) * S + lane) * 2);
-        m[k] = a.x;
-        lv[k] = a.y;
-      }
-    }
+    for (int k = 0; k < 4; ++k)
+      a[k] = *(const float2*)(p.part_ml + (((size_t)t * p.H + hb0 + 4 * wave + k) * S + sl) * 2);
     const uint8_t* src = src_of(tid);
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u)
       v0[u] = u < S ? *(const u32x4*)(src + (size_t)u * rstride) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float M = wave_max(m[k]);
-      const float e = (M == -INFINITY || lane >= S) ? 0.f : exp2f(m[k] - M) * lv[k];
+      const float mk = lane < S ? a[k].x : -INFINITY;
+      const float M = wave_max(mk);
+      const float e = (M == -INFINITY || lane >= S) ? 0.f : exp2f(mk - M) * a[k].y;
       const float Lsum = wave_sum(e);
       if (lane < S) wgt[lane][4 * wave + k] = Lsum > 0.f ? e / Lsum : 0.f;
       if (p.lse && w == 0 && lane == 0)
         p.lse[(size_t)t * p.H + hb0 + 4 * wave + k] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+    }
+  }
+  if (wave == 0) {
+    fl = lane < S ? fl : 0u;
+    for (int off = 32; off >= 1; off >>= 1) fl |= (uint32_t)__shfl_xor((int)fl, off, 64);
+    if (lane == 0) {
+      flagged = (fl >> (16 * half)) & 0xffffu;
+      nonfinite = 0u;
     }
   }
   __syncthreads();
@@ -1118,6 +1139,7 @@ hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream) {
     const int hb = p.heads_per_wg / 32;
     const dim3 cg(p.n_hg * hb * p.dim_waves * 2, p.T);
     if (p.nsplit <= 8) hipLaunchKernelGGL(sfa_combine_kernel<8>, cg, dim3(kCombineThreads), 0, stream, p);
+    else if (p.nsplit <= 16) hipLaunchKernelGGL(sfa_combine_kernel<16>, cg, dim3(kCombineThreads), 0, stream, p);
     else hipLaunchKernelGGL(sfa_combine_kernel<32>, cg, dim3(kCombineThreads), 0, stream, p);
   } else {
     const int words = p.T * (p.H / 32);
