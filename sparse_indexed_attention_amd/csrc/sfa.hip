@@ -767,6 +767,9 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
     // (slices of one record adjacent, as in the 128-head kernel: 16 records per wave)
     uint8_t* po = (uint8_t*)p.part_o +
                   ((((size_t)t * p.n_hg + hg) * NW + wave) * 16 * p.nsplit + r) * 1024 + 16 * lane;
+    // streaming stores with up to 16 slices (measured: 128K decode, 16 slices, attention 27.7
+    // -> 27.0 us; one 1M query, 64 slices of one tile, 24.7 -> 25.4 us with them)
+    const bool nt = p.nsplit <= 16;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -783,7 +786,9 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
               const _Float16 b = (_Float16)(o[hb][2 * np + sd][4 * j + i + 1] * inv[i + 1]);
               w[2 * sd + i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
             }
-          *(u32x4*)(po + (size_t)((hb * 4 + j) * 2 + np) * p.nsplit * 1024) = u32x4{w[0], w[1], w[2], w[3]};
+          u32x4* dst = (u32x4*)(po + (size_t)((hb * 4 + j) * 2 + np) * p.nsplit * 1024);
+          if (nt) __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, dst);
+          else *dst = u32x4{w[0], w[1], w[2], w[3]};
         }
       }
     if (par == 0 && hh == 0) {
