@@ -350,6 +350,9 @@ def main():
                          "other (each one device's share at its real shape)")
     ap.add_argument("--layout", choices=("zigzag", "contiguous"), default="zigzag",
                     help="how --shards cuts the chunk of queries")
+    ap.add_argument("--ctx", type=int, default=0,
+                    help="decode workloads: give every sequence this many tokens (e.g. 131072 for "
+                         "the 128K end of workload 4's range); the workload is renamed *_ctxN")
     ap.add_argument("--order", choices=("natural", "zigzag"), default="natural",
                     help="query order of the unsharded launch: zigzag pairs the 4-query tiles "
                          "head and tail (0, B-1, 1, B-2, ...), the workgroup-level pairing of short "
@@ -387,6 +390,12 @@ def main():
     dsa.load()
     torch.cuda.set_device(0)
     spec = workload(args.config)
+    if args.ctx:
+        if spec.name.startswith("prefill"):
+            raise SystemExit("bench: --ctx applies to the decode workloads")
+        from synth import scaled_spec
+        spec = scaled_spec(spec, seq_lens=[args.ctx] * spec.num_seqs,
+                           name=f"{spec.name}_ctx{args.ctx}")
     if args.prolog:
         prolog_bench(args, dsa, torch, spec)
         return
