@@ -22,16 +22,20 @@
 //     first live tile and never moved, so the output accumulators are never rescaled; a head
 //     whose scores climb more than 64 above that reference is flagged and recomputed by the
 //     reference method (fp32) after the attention kernel.
-//   * O += P . V on the same MFMA: the probabilities, in the S^T accumulator layout, are the
-//     A operand as they stand (the k order of the contraction is permuted to the rows each
-//     lane holds), and the V operand comes straight from the row-major tile through the
-//     transposing LDS read ds_read_b64_tr_b16, which gathers one dim of four rows into a lane.
+//   * O += P . V on the same MFMA, split by output dims: the head-owner waves write their
+//     probabilities (bf16, in the accumulator's k order, so the k order of the contraction is
+//     permuted to the rows each lane holds) to a small P tile in LDS; every wave then computes
+//     O for all the workgroup's heads over its own 512/NW output dims, with P as the A operand
+//     and V straight from the row-major tile through the transposing LDS read
+//     ds_read_b64_tr_b16, which gathers one dim of four rows into a lane.
 //   * Slices of the index list are merged by a log-sum-exp weighted combine kernel.
+//   * Small decode batches take a 64-head variant (sfa_mfma64_kernel, below) that halves the
+//     slices a query needs.
 //   * fp8 latent rows (656 bytes: four 128-column tiles of e4m3 codes with power-of-two
 //     scales, the rope columns in bf16): tiles of fp8 rows stream into four smaller LDS
-//     staging buffers (three or four tiles in flight instead of two), and one pass widens
-//     the landed tile into the bf16 tile with v_cvt_scalef32_pk_bf16_fp8, exactly (a code
-//     times a power of two is a bf16 value); the contractions then run as above.
+//     staging buffers (three tiles in flight instead of two), and the contractions widen their
+//     operands from the staged tile as they read them, with v_cvt_scalef32_pk_bf16_fp8,
+//     exactly (a code times a power of two is a bf16 value); see the fp8 tile loop.
 // Reference path (fp32 storage or other shapes): one workgroup per (query, head), fp32.
 
 #include <cstdlib>
@@ -40,6 +44,8 @@
 
 namespace dsa {
 namespace {
+
+typedef int32_t v2i32 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileRows = 32;
 constexpr int kRowBytes = kSfaDqk * 2;                   // 1152
@@ -56,6 +62,7 @@ constexpr int kTileLoadsF8 = (kTileSlotsF8 + 63) / 64;   // 21
 constexpr int kStageBufs = 4;                            // fp8 staging buffers
 constexpr int kBtLds = 4096;                             // block-table entries staged in LDS
 constexpr int kPStride = 80;                             // bytes per head row of the shared P tile
+constexpr int kPStride32 = 144;                          // ... in fp32 (fp8 rows: 128 bytes + 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -116,12 +123,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   constexpr int LPW = (TLOADS + NW - 1) / NW;      // loads per wave per tile (at most)
   constexpr int LPW_MIN = TLOADS / NW;              // ... and at least
   // bf16 tiles (fp8 rows: one, filled from the staging buffers)
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[F8 ? 1 : kTileBufs][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[F8 ? 1 : kTileBufs][F8 ? 16 : kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage[F8 ? kStageBufs : 1][F8 ? kTileBytesF8 : 16];
   __shared__ int32_t rows[kMaxTopK];                // pool row of each slice entry, -1 if none
   __shared__ int32_t bt_lds[kBtLds];                // the sequence's block-table row
   __shared__ __attribute__((aligned(16))) float hv[NW * 32];   // per-head values
-  __shared__ __attribute__((aligned(16))) uint8_t plds[NW * 32 * kPStride];   // P of the tile
+  __shared__ __attribute__((aligned(16))) uint8_t plds[NW * 32 * (F8 ? kPStride32 : kPStride)];   // P of the tile
 
   // workgroup -> (query, head group, slice); consecutive workgroups go to different XCDs, so
   // the head groups of one (query, slice) are placed 8 apart and share an XCD's L2
@@ -226,34 +233,6 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
       }
     }
   };
-  // fp8 rows: widens the staged tile into the bf16 tile.  Work item s = (row s / 36, 16-column
-  // group g = s % 36): groups 0..31 are codes of tile g / 8, widened with its scale; groups
-  // 32..35 are the bf16 rope columns, copied.
-  auto widen = [&](const uint8_t* sb, uint8_t* tb) {
-    for (int s = tid; s < kTileRows * 36; s += NTS) {
-      const int rr = s / 36, g = s - rr * 36;
-      const uint8_t* srow = sb + rr * kSfaRowF8;
-      u32x4 w0, w1;
-      if (g < 32) {
-        const u32x4 cd = *(const u32x4*)(srow + 16 * g);
-        const float sc = *(const float*)(srow + 640 + 4 * (g >> 3));
-        uint32_t o[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd[k], sc, false));
-          o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd[k], sc, true));
-        }
-        w0 = u32x4{o[0], o[1], o[2], o[3]};
-        w1 = u32x4{o[4], o[5], o[6], o[7]};
-      } else {
-        w0 = *(const u32x4*)(srow + 512 + 32 * (g - 32));
-        w1 = *(const u32x4*)(srow + 512 + 32 * (g - 32) + 16);
-      }
-      *(u32x4*)(tb + tile_off(rr, 2 * g)) = w0;
-      *(u32x4*)(tb + tile_off(rr, 2 * g + 1)) = w1;
-    }
-  };
-
   const float scale2 = p.scale * kLog2e;
 
   // S^T = R . Q^T for the tile in `tb`, scaled to the exp2 domain, -inf for empty rows: lane
@@ -379,9 +358,127 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
 #pragma unroll
   for (int n = 0; n < NW * NB; ++n) o[n] = f32x16{};
   if constexpr (F8) {
-    // fp8 tiles stream through kStageBufs staging buffers; a landed tile is widened into the
-    // bf16 tile, which frees its staging buffer for the tile kStageBufs later
+    // fp8 rows: the contractions read the landed staging tile directly.  S^T: the A fragment
+    // of row c and k step s < 32 is 8 codes (one 8-byte read) widened to bf16 with the row's
+    // scale of tile s / 8 by v_cvt_scalef32_pk_bf16_fp8 (exact: a code times a power of two is a
+    // bf16 value); steps 32..35 read the bf16 rope columns.  P . V: the value codes are widened
+    // with scale 1 and each row's scale of the wave's dim tile multiplies P instead (a power of
+    // two, exact in fp32), so P is exchanged in fp32 and rounded to bf16 once, per wave, after
+    // its scaling.  The B fragments come from the 8-bit transposing read ds_read_b64_tr_b8: in
+    // each 16-lane group g, lane 8h + i receives byte i of the 8-byte chunks that lanes
+    // 16g + h + 2b (b = 0..7) address, so lane s of the group addresses k slot
+    // 8(g / 2) + (s % 16) / 2 of the step at dims 16(g % 2) + 8(s % 2) of the block.
     static_assert(kStageBufs == 4 && 3 * LPW_MIN < 64, "waits below");
+    auto widen8 = [](u32x2 r, float sc) {
+      const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, false);
+      const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, true);
+      const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, false);
+      const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, true);
+      return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+    };
+    auto attend8 = [&](int tile, const uint8_t* sb) {
+      const uint32_t valid = (uint32_t)__ballot(rows[tile * kTileRows + c] >= 0);
+      float z[16];
+      {
+        const uint8_t* ra = sb + c * kSfaRowF8;
+        const f32x4 sc = *(const f32x4*)(ra + 640);
+        f32x16 sa = {};
+        u32x2 raw[2][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[0][u] = *(const u32x2*)(ra + 16 * u + 8 * hh);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          if (g + 1 < 8) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) raw[(g + 1) & 1][u] = *(const u32x2*)(ra + 16 * (4 * (g + 1) + u) + 8 * hh);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8(raw[g & 1][u], sc[g >> 1]), qk[4 * g + u], sa, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 ar[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ar[u] = *(const bf16x8*)(ra + 512 + 32 * u + 16 * hh);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[u], qk[32 + u], sa, 0, 0, 0);
+        if (valid == 0xffffffffu) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) z[e] = sa[e] * scale2;
+        } else {
+          const uint32_t mh = valid >> (4 * hh);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            z[e] = (mh >> (8 * (e >> 2) + (e & 3))) & 1u ? sa[e] * scale2 : -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, z[e]);
+      mx = xhalf_max(mx);
+      if (m2 == -INFINITY) m2 = mx;
+      over |= mx > m2 + 64.f;
+      const bool live = m2 != -INFINITY;
+      float pe[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pe[e] = live ? __builtin_amdgcn_exp2f(z[e] - m2) : 0.f;
+        l += pe[e];
+      }
+      {
+        // head row c of this wave, k step kk, k slots 8 hh .. 8 hh + 7: floats 16 kk + 8 hh
+        float* prow = (float*)(plds + (32 * wave + c) * kPStride32) + 8 * hh;
+        *(f32x4*)prow = f32x4{pe[0], pe[1], pe[2], pe[3]};
+        *(f32x4*)(prow + 4) = f32x4{pe[4], pe[5], pe[6], pe[7]};
+        *(f32x4*)(prow + 16) = f32x4{pe[8], pe[9], pe[10], pe[11]};
+        *(f32x4*)(prow + 20) = f32x4{pe[12], pe[13], pe[14], pe[15]};
+      }
+      __syncthreads();                           // every head's P is in the tile
+      // this lane's source row for the transposing reads (k slot of step kk: + 16 kk)
+      const int tg = lane >> 4, tu = (lane & 15) >> 1;
+      const int trow = 8 * (tu >> 2) + 4 * (tg >> 1) + (tu & 3);
+      const int tdim = 16 * (tg & 1) + 8 * (lane & 1);
+      bf16x8 pa[NW][2];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int dim0 = DW * wave + 32 * nb;
+        if ((nb & 3) == 0) {
+          // P times the rows' scales of dim tile dim0 / 128 (k slot 8 hh + u of step kk is row
+          // 16 kk + 8 (u / 4) + 4 hh + u % 4)
+          const int tsc = 640 + 4 * (dim0 >> 7);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            float vs[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              vs[u] = *(const float*)(sb + (16 * kk + 8 * (u >> 2) + 4 * hh + (u & 3)) * kSfaRowF8 + tsc);
+#pragma unroll
+            for (int hb = 0; hb < NW; ++hb) {
+              const float* pr = (const float*)(plds + (32 * hb + c) * kPStride32) + 16 * kk + 8 * hh;
+              const f32x4 p0 = *(const f32x4*)pr, p1 = *(const f32x4*)(pr + 4);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                pa[hb][kk][u] = (__bf16)(p0[u] * vs[u]);
+                pa[hb][kk][4 + u] = (__bf16)(p1[u] * vs[4 + u]);
+              }
+            }
+          }
+        }
+        bf16x8 b[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const v2i32 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i32*)(sb + (16 * kk + trow) * kSfaRowF8 + dim0 + tdim));
+          b[kk] = widen8(u32x2{(uint32_t)v.x, (uint32_t)v.y}, 1.f);
+        }
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            o[hb * NB + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb][kk], b[kk], o[hb * NB + nb], 0, 0, 0);
+      }
+    };
     for (int i = 0; i < kStageBufs && i < ntiles; ++i) issue(i, i);
     load_queries();
     int buf = 0;
@@ -392,11 +489,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
       else if (ahead == 1) wait_vmcnt<LPW_MIN>();
       else wait_vmcnt<0>();
       __syncthreads();                           // every wave's loads of `tile` have landed
-      widen(stage[buf], tiles[0]);
-      __syncthreads();                           // the bf16 tile is complete, the buffer free
+      attend8(tile, stage[buf]);
+      __syncthreads();                           // the staging buffer and the P tile are free
       if (tile + kStageBufs < ntiles) issue(tile + kStageBufs, buf);
-      attend(tile, tiles[0]);
-      __syncthreads();                           // the bf16 tile and the P tile are free again
       buf = buf == kStageBufs - 1 ? 0 : buf + 1;
     }
   } else {
