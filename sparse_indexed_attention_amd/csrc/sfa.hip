@@ -71,6 +71,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Byte offset in a tile of chunk c of row r.
 __device__ __forceinline__ int tile_off(int r, int c) { return 16 * (r * kLdsChunks + c); }
 
+// 8 e4m3 codes (little-endian in r) times the power-of-two scale sc, as bf16: exact.
+__device__ __forceinline__ bf16x8 widen_fp8x8(u32x2 r, float sc) {
+  const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, false);
+  const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, true);
+  const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, false);
+  const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, true);
+  return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -369,13 +378,6 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     // 16g + h + 2b (b = 0..7) address, so lane s of the group addresses k slot
     // 8(g / 2) + (s % 16) / 2 of the step at dims 16(g % 2) + 8(s % 2) of the block.
     static_assert(kStageBufs == 4 && 3 * LPW_MIN < 64, "waits below");
-    auto widen8 = [](u32x2 r, float sc) {
-      const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, false);
-      const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, true);
-      const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, false);
-      const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, true);
-      return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-    };
     auto attend8 = [&](int tile, const uint8_t* sb) {
       const uint32_t valid = (uint32_t)__ballot(rows[tile * kTileRows + c] >= 0);
       float z[16];
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8(raw[g & 1][u], sc[g >> 1]), qk[4 * g + u], sa, 0, 0, 0);
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen_fp8x8(raw[g & 1][u], sc[g >> 1]), qk[4 * g + u], sa, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         bf16x8 ar[4];
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
         for (int kk = 0; kk < 2; ++kk) {
           const v2i32 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (__attribute__((address_space(3))) v2i32*)(sb + (16 * kk + trow) * kSfaRowF8 + dim0 + tdim));
-          b[kk] = widen8(u32x2{(uint32_t)v.x, (uint32_t)v.y}, 1.f);
+          b[kk] = widen_fp8x8(u32x2{(uint32_t)v.x, (uint32_t)v.y}, 1.f);
         }
 #pragma unroll
         for (int hb = 0; hb < NW; ++hb)
@@ -598,18 +600,39 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
 //     blocks per wave (16 KB per wave), and (m, l) per head; the combine kernel merges them.
 constexpr int kRows64 = 512;                           // most slice entries of the decode variant
 constexpr int kPStride64 = 144;                        // bytes per head row of its P tile (64 rows)
+constexpr int kPStride64F = 272;                       // ... in fp32 (fp8 rows: 256 bytes + 16)
+// F8: fp8 latent rows, read and widened as in the 128-head kernel's fp8 tile loop (the rows'
+// value scales folded into an fp32 P tile, the V fragments from the 8-bit transposing read).
+// Its smaller buffers lie in one region [buffer 0 | buffer 1 | P tile | spare | buffer 2 |
+// buffer 3] whose first 74,752 bytes take the padded query rows, so there pair 0 goes into
+// buffers 2 and 3 and pair 1 into 0 and 1.
+template <bool F8>
 __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
   constexpr int NW = 4, NTS = 256;
-  constexpr int LPW = (kTileLoads + NW - 1) / NW, LPW_MIN = kTileLoads / NW;
+  constexpr int TL = F8 ? kTileLoadsF8 : kTileLoads;
+  constexpr int LPW = (TL + NW - 1) / NW, LPW_MIN = TL / NW;
   constexpr int kBufs = 4;
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[kBufs][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t plds[64 * kPStride64];
+  constexpr int TB = F8 ? kTileBytesF8 : kTileBytes;
+  constexpr int PS = F8 ? kPStride64F : kPStride64;
+  constexpr int QTILE = 2 * kTileBytes;                      // 64 padded bf16 query rows
+  constexpr int LO = 2 * TB + 64 * PS;                       // F8: buffers 0, 1 and the P tile
+  constexpr int HI = F8 ? (LO > QTILE ? LO : QTILE) : LO;    // F8: start of buffer 2
+  constexpr int REGION = F8 ? HI + 2 * TB : kBufs * TB + 64 * PS;
+  __shared__ __attribute__((aligned(16))) uint8_t region[REGION];
   __shared__ int32_t rows[kRows64];
   __shared__ float xmax[NW][32], xsum[NW][32];
   __shared__ uint32_t xover[NW];
   __shared__ __attribute__((aligned(16))) float hv[64];
-  static_assert(kBufs * kTileBytes + 64 * kPStride64 + 4 * kRows64 + 2 * NW * 32 * 4 + 16 + 256 <= 163840,
-                "LDS");
+  static_assert(REGION + 4 * kRows64 + 2 * NW * 32 * 4 + 16 + 256 <= 163840, "LDS");
+  static_assert(TB >= 4 * kBtLds, "block-table row staged in a tile buffer");
+  // tile buffer b, the P tile, the query rows' landing place, and the buffers of pair pr
+  auto tbuf = [&](int b) -> uint8_t* {
+    if constexpr (F8) return region + (b < 2 ? b * TB : HI + (b - 2) * TB);
+    else return region + b * TB;
+  };
+  uint8_t* const plds = F8 ? region + 2 * TB : region + kBufs * TB;
+  uint8_t* const qland = F8 ? region : region + 2 * TB;
+  auto pair_buf = [](int pr) { return F8 ? 2 * ((pr + 1) & 1) : 2 * (pr & 1); };
 
   // workgroup -> (query, head group, slice): the head groups of one (query, slice) are 8
   // apart, so consecutive workgroup numbers place them on one XCD, sharing its L2 for the rows
@@ -641,7 +664,7 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
       posr[u] = i < nrows ? idx[i] : -1;
     }
   }
-  int32_t* bt_lds = (int32_t*)tiles[kBufs - 1];
+  int32_t* bt_lds = (int32_t*)tbuf(kBufs - 1);
   const bool stage_bt = p.L.bt != nullptr && p.L.bt_stride <= kBtLds;
   if (stage_bt) {
     const int32_t* btrow = p.L.bt + (size_t)seq * p.L.bt_stride;
@@ -674,31 +697,40 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
   // this wave's share of tile `tile` (see the 128-head kernel): rows without a position load
   // from a zeroed chunk, so every wave issues the same number of loads per tile
   auto issue = [&](int tile, int buf) {
-    uint8_t* tb = tiles[buf];
+    uint8_t* tb = tbuf(buf);
     int z0 = 0;
     asm volatile("" : "+v"(z0));
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int I = wave + NW * u;
-      if (LPW != LPW_MIN && I >= kTileLoads) break;
+      if (LPW != LPW_MIN && I >= TL) break;
       const int P = 64 * I + lane + z0;
-      const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
-      if (P < kTileSlots && ch < kRowChunks) {
-        const int row = rows[tile * kTileRows + rr];
-        load16_to_lds(row >= 0 ? kv + (size_t)row * kRowBytes + 16 * ch : zero, lds_u32(tb + 1024 * I));
+      if constexpr (F8) {
+        const int rr = P / kRowChunksF8, ch = P - rr * kRowChunksF8;   // packed rows
+        if (P < kTileSlotsF8) {
+          const int row = rows[tile * kTileRows + rr];
+          load16_to_lds(row >= 0 ? kv + (size_t)row * kSfaRowF8 + 16 * ch : zero, lds_u32(tb + 1024 * I));
+        }
+      } else {
+        const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
+        if (P < kTileSlots && ch < kRowChunks) {
+          const int row = rows[tile * kTileRows + rr];
+          load16_to_lds(row >= 0 ? kv + (size_t)row * kRowBytes + 16 * ch : zero, lds_u32(tb + 1024 * I));
+        }
       }
     }
   };
   auto issue_pair = [&](int pr) {
-    issue(2 * pr, 2 * (pr & 1));
-    issue(2 * pr + 1, 2 * (pr & 1) + 1);
+    issue(2 * pr, pair_buf(pr));
+    issue(2 * pr + 1, pair_buf(pr) + 1);
   };
   issue_pair(0);
-  // The workgroup's 64 query rows (73.7 KB, contiguous) land in buffers 2 and 3 as one 64-row
-  // tile in the padded row layout, behind pair 0's tiles; each wave then reads its 32 heads'
-  // fragments from there.  Two waves share each head half, so loading the fragments from
-  // global memory directly would fetch every query twice.  Pair 1 goes into the same buffers
-  // once every wave has its fragments.
+  bf16x8 qk[36];
+  // The workgroup's 64 query rows (73.7 KB, contiguous) land as one 64-row tile in the padded
+  // row layout (in buffers 2 and 3; with fp8 rows in the front of the region), behind pair 0's
+  // tiles; each wave then reads its 32 heads' fragments from there.  Two waves share each head
+  // half, so loading the fragments from global memory directly would fetch every query twice.
+  // Pair 1 goes into the landing place once every wave has its fragments.
   {
     const uint8_t* qrows = (const uint8_t*)p.q + ((size_t)t * p.H + hg * 64) * kRowBytes;
     constexpr int QLOADS = 2 * kTileSlots / 64;    // 73: 64 rows of 73 slots
@@ -706,14 +738,13 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
     for (int I = wave; I < QLOADS; I += NW) {
       const int P = 64 * I + lane;
       const int rr = P / kLdsChunks, ch = P - rr * kLdsChunks;
-      if (ch < kRowChunks) load16_to_lds(qrows + (size_t)rr * kRowBytes + 16 * ch, lds_u32(tiles[2] + 1024 * I));
+      if (ch < kRowChunks) load16_to_lds(qrows + (size_t)rr * kRowBytes + 16 * ch, lds_u32(qland + 1024 * I));
     }
   }
   wait_vmcnt<0>();
   __syncthreads();                                 // pair 0 and the query tile have landed
-  bf16x8 qk[36];
   {
-    const uint8_t* qr = tiles[2] + tile_off(32 * hq + c, hh);   // head 32 hq + c, dims 8 hh + 16 s
+    const uint8_t* qr = qland + tile_off(32 * hq + c, hh);   // head 32 hq + c, dims 8 hh + 16 s
 #pragma unroll
     for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qr + 32 * s);
   }
@@ -733,7 +764,7 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
   const int vdim = 16 * (c >> 4) + 4 * (vi & 3);
 
   for (int pr = 0; pr < npairs; ++pr) {
-    const int b0 = 2 * (pr & 1);
+    const int b0 = pair_buf(pr);
     // Pairs 0 and 1 are issued before the loop, pair pr + 1 (pr >= 1) right after pair pr
     // opens: so only at pair 0 is a later pair in flight while waiting.
     if (pr == 0 && npairs > 1) wait_vmcnt<(2 * LPW_MIN < 63 ? 2 * LPW_MIN : 63)>();
@@ -743,11 +774,35 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
     if (pr >= 1 && pr + 1 < npairs) issue_pair(pr + 1);   // into pair pr - 1's buffers
     // S^T for tile 2 pr + par, heads h0 .. h0 + 31
     const int tile = 2 * pr + par;
-    const uint8_t* tb = tiles[b0 + par];
+    const uint8_t* tb = tbuf(b0 + par);
     const uint32_t valid = (uint32_t)__ballot(rows[tile * kTileRows + c] >= 0);
     float z[16];
     {
       f32x16 sa = {};
+      if constexpr (F8) {
+        const uint8_t* ra = tb + c * kSfaRowF8;
+        const f32x4 sc = *(const f32x4*)(ra + 640);
+        u32x2 raw[2][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[0][u] = *(const u32x2*)(ra + 16 * u + 8 * hh);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          if (g + 1 < 8) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) raw[(g + 1) & 1][u] = *(const u32x2*)(ra + 16 * (4 * (g + 1) + u) + 8 * hh);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen_fp8x8(raw[g & 1][u], sc[g >> 1]), qk[4 * g + u], sa, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 ar[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ar[u] = *(const bf16x8*)(ra + 512 + 32 * u + 16 * hh);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[u], qk[32 + u], sa, 0, 0, 0);
+      } else {
       const uint8_t* ra = tb + tile_off(c, hh);
       bf16x8 a[2][4];
 #pragma unroll
@@ -762,6 +817,7 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[g & 1][u], qk[4 * g + u], sa, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+      }
       }
       const uint32_t mh = valid >> (4 * hh);
 #pragma unroll
@@ -778,7 +834,20 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
     if (m2 == -INFINITY) m2 = mx;                  // first pair with a live row of this head
     over |= mx > m2 + 64.f;
     const bool live = m2 != -INFINITY;
-    {
+    if constexpr (F8) {
+      float pe[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pe[e] = live ? __builtin_amdgcn_exp2f(z[e] - m2) : 0.f;
+        l += pe[e];
+      }
+      // head row 32 hq + c, k steps 2 par and 2 par + 1: floats 16 k + 8 hh .. + 7
+      float* prow = (float*)(plds + (32 * hq + c) * PS) + 32 * par + 8 * hh;
+      *(f32x4*)prow = f32x4{pe[0], pe[1], pe[2], pe[3]};
+      *(f32x4*)(prow + 4) = f32x4{pe[4], pe[5], pe[6], pe[7]};
+      *(f32x4*)(prow + 16) = f32x4{pe[8], pe[9], pe[10], pe[11]};
+      *(f32x4*)(prow + 20) = f32x4{pe[12], pe[13], pe[14], pe[15]};
+    } else {
       bf16x8 pw[2];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -795,6 +864,47 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
     }
     __syncthreads();                               // every head's P of both tiles is in place
     bf16x8 pa[2][4];
+    if constexpr (F8) {
+      // P times the rows' value scales of this wave's dim tile (k step kk: tile kk / 2, k slot
+      // 8 hh + u is its row 16 (kk % 2) + 8 (u / 4) + 4 hh + u % 4)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint8_t* st = tbuf(b0 + (kk >> 1)) + 640 + 4 * wave;
+        float vs[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          vs[u] = *(const float*)(st + (16 * (kk & 1) + 8 * (u >> 2) + 4 * hh + (u & 3)) * kSfaRowF8);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const float* pr = (const float*)(plds + (32 * hb + c) * PS) + 16 * kk + 8 * hh;
+          const f32x4 p0 = *(const f32x4*)pr, p1 = *(const f32x4*)(pr + 4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            pa[hb][kk][u] = (__bf16)(p0[u] * vs[u]);
+            pa[hb][kk][4 + u] = (__bf16)(p1[u] * vs[4 + u]);
+          }
+        }
+      }
+      const int tg = lane >> 4, tu = (lane & 15) >> 1;
+      const int trow = 8 * (tu >> 2) + 4 * (tg >> 1) + (tu & 3);
+      const int tdim = 128 * wave + 16 * (tg & 1) + 8 * (lane & 1);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        bf16x8 b[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const v2i32 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i32*)(
+              tbuf(b0 + (kk >> 1)) + (16 * (kk & 1) + trow) * kSfaRowF8 + 32 * nb + tdim));
+          b[kk] = widen_fp8x8(u32x2{(uint32_t)v.x, (uint32_t)v.y}, 1.f);
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            o[hb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb][kk], b[kk], o[hb][nb], 0, 0, 0);
+      }
+      continue;
+    }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -811,7 +921,7 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           v[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(tiles[b0 + tt] + tile_off(8 * q + vrow, 0) + cho));
+              (__attribute__((address_space(3))) s16x4*)(tbuf(b0 + tt) + tile_off(8 * q + vrow, 0) + cho));
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
           b[2 * tt + kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[2 * kk], v[2 * kk + 1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -1163,17 +1273,17 @@ SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path, bo
     // slices (at most 1024 rows each) until about one workgroup per CU runs.
     const bool wide = (int64_t)T * (H / 128) >= 256;
     pl.heads_per_wg = (H % 128 == 0) ? 128 : (H % 64 == 0) ? 64 : 32;
-    // Small decode batches with bf16 rows take the 64-head variant.  A workgroup of either
+    // Small decode batches take the 64-head variant (bf16 or fp8 rows).  A workgroup of either
     // kind reads its heads' queries plus its slice's rows: with at most 16 queries' worth of
     // 128-head groups the 128-head slices hold at most 128 rows, fewer bytes than the 147 KB
     // of queries, and halving the heads while doubling the rows reads the same bytes and
     // writes half the partial outputs; with more queries the rows dominate and the 128-head
     // workgroup reads less.
-    pl.decode64 = !wide && !kv_fp8 && H % 64 == 0 && (int64_t)T * (H / 64) <= 32;
+    pl.decode64 = !wide && H % 64 == 0 && (int64_t)T * (H / 64) <= 32;
     if (pl.decode64) pl.heads_per_wg = 64;
     if (const int v = plan_overrides().sfa_hpw; (v == 32 || v == 64 || v == 128) && H % v == 0) {
       pl.heads_per_wg = v;
-      pl.decode64 = v == 64 && !kv_fp8;
+      pl.decode64 = v == 64;
     }
     pl.n_hg = H / pl.heads_per_wg;
     pl.dim_waves = pl.decode64 ? 4 : pl.heads_per_wg / 32;
@@ -1217,7 +1327,8 @@ hipError_t launch_sfa(const SfaParams& p, bool fast_path, hipStream_t stream) {
   const dim3 grid(pairs * p.n_hg);
   const bool f8 = p.kv_dtype == kDtFP8;
   if (p.decode64) {
-    hipLaunchKernelGGL(sfa_mfma64_kernel, grid, dim3(256), 0, stream, p);
+    if (f8) hipLaunchKernelGGL(sfa_mfma64_kernel<true>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(sfa_mfma64_kernel<false>, grid, dim3(256), 0, stream, p);
   } else switch (p.heads_per_wg) {
     case 128:
       if (f8) hipLaunchKernelGGL((sfa_mfma_kernel<4, true>), grid, dim3(256), 0, stream, p);
