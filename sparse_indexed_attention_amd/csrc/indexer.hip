@@ -1619,6 +1619,9 @@ __device__ __forceinline__ Kth lst_kth(const uint32_t* keys, int n, int k, uint3
 // s (in index order) writes pos[i] to out[s] (s < limit).  Wave w owns a contiguous range of
 // 4-entry chunks; within one step of 64 chunks a packed exclusive scan of the per-lane
 // (taken above T, equal to T) counts gives every lane its slots.
+__device__ __forceinline__ void lst_emit_range(const uint32_t* keys, const int32_t* pos, int c0,
+                                               int c1, uint32_t T, int need, int32_t* out,
+                                               float* out_score, int limit, int slot, int eq);
 __device__ __forceinline__ void lst_emit(const uint32_t* keys, const int32_t* pos, int n,
                                          uint32_t T, int need, int32_t* out, float* out_score,
                                          int limit, const Lds& L) {
@@ -1649,6 +1652,15 @@ __device__ __forceinline__ void lst_emit(const uint32_t* keys, const int32_t* po
     eq += ew;
   }
   __syncthreads();
+  lst_emit_range(keys, pos, c0, c1, T, need, out, out_score, limit, slot, eq);
+}
+
+// The emission of lst_emit over this wave's chunks [c0, c1), given the entries taken (slot)
+// and the keys equal to T (eq) before them.
+__device__ __forceinline__ void lst_emit_range(const uint32_t* keys, const int32_t* pos, int c0,
+                                               int c1, uint32_t T, int need, int32_t* out,
+                                               float* out_score, int limit, int slot, int eq) {
+  const int lane = threadIdx.x & 63;
   for (int cb = c0; cb < c1; cb += 64) {
     const int c = cb + lane;
     u32x4 k = {0u, 0u, 0u, 0u};
@@ -1700,12 +1712,76 @@ __device__ __forceinline__ int merge_fast(const IndexerParams& p, int t, int K_e
                                           bool& enough) {
   enough = mh.n_real >= K_eff;
   if (!enough) return -1;
-  const Kth kt = lst_kth(fk, mh.n, K_eff, mh.lo, mh.hi, L);
-  T = kt.T;
-  gt = kt.gt;
-  if (mh.max_tau > T) return 0;
-  lst_emit(fk, fp, mh.n, T, K_eff - gt, p.out_idx + (size_t)t * p.K,
-           p.out_score ? p.out_score + (size_t)t * p.K : nullptr, K_eff, L);
+  int32_t* out = p.out_idx + (size_t)t * p.K;
+  float* out_s = p.out_score ? p.out_score + (size_t)t * p.K : nullptr;
+  const int n = mh.n, nc = n >> 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // One radix pass finds the bin of the K_eff-th key.  When that bin holds at most 64 keys,
+  // one more pass over the list both gathers them (with their wave) and counts, per wave, the
+  // keys above the bin; the bin's keys ranked within a wave then give T and every wave's
+  // counts above and at T, so the output's count pass is not needed.  Otherwise lst_kth
+  // narrows the bin and lst_emit counts.
+  if (threadIdx.x == 0) L.bcast[3] = 0;
+  const uint32_t width = mh.hi - mh.lo;
+  const int sh = range_shift(width);
+  const BinPick bp = lst_rank_bin(fk, n, mh.lo, width, sh, K_eff, L);
+  if (sh == 0 || bp.c > 64) {
+    const Kth kt = lst_kth(fk, n, K_eff, mh.lo, mh.hi, L);
+    T = kt.T;
+    gt = kt.gt;
+    if (mh.max_tau > T) return 0;
+    lst_emit(fk, fp, n, T, K_eff - gt, out, out_s, K_eff, L);
+  } else {
+    const uint32_t blo = mh.lo + ((uint32_t)bp.d << sh), bw = (1u << sh) - 1u;
+    uint32_t* const bin_wave = L.sel_key;         // wave of each gathered key (free here)
+    const int cpw = (nc + NWAVE - 1) / NWAVE;
+    const int c0 = min(nc, wave * cpw), c1 = min(nc, c0 + cpw);
+    int above = 0;
+    for (int c = c0 + lane; c < c1; c += 64) {
+      const u32x4 k = *(const u32x4*)(fk + 4 * c);
+      int m = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        above += k[u] - blo > bw && k[u] > blo;   // above the bin (key 0 padding is below it)
+        m += k[u] - blo <= bw;
+      }
+      if (m) {
+        int at = atomicAdd(&L.bcast[3], m);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (k[u] - blo <= bw) {
+            L.small[at] = k[u];
+            bin_wave[at++] = (uint32_t)wave;
+          }
+      }
+    }
+    above = __builtin_amdgcn_readlane(wave_scan_add(above), 63);
+    if (lane == 0) L.wcnt[wave] = above;
+    __syncthreads();
+    const int cb = bp.c, r = K_eff - bp.above;
+    const uint32_t v = lane < cb ? L.small[lane] : 0u;
+    const int vw = lane < cb ? (int)bin_wave[lane] : -1;
+    int g = 0, ge = 0;
+    for (int j = 0; j < cb; ++j) {
+      const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+      g += w > v;
+      ge += w >= v;
+    }
+    const uint64_t hit = __ballot(lane < cb && g < r && r <= ge);
+    const int l = __builtin_ctzll(hit);
+    T = (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+    gt = bp.above + __builtin_amdgcn_readlane(g, l);
+    if (mh.max_tau > T) return 0;
+    const int need = K_eff - gt;
+    int slot = 0, eq = 0;   // taken entries and ties before this wave's range
+    for (int w = 0; w < wave; ++w) {
+      const int gw = L.wcnt[w] + __popcll(__ballot(vw == w && v > T));
+      const int ew = __popcll(__ballot(vw == w && v == T));
+      slot += gw + max(0, min(ew, need - eq));
+      eq += ew;
+    }
+    lst_emit_range(fk, fp, c0, c1, T, need, out, out_s, K_eff, slot, eq);
+  }
   pad_output(p, t, K_eff);
   if (threadIdx.x == 0) st_agent(p.counters + t, 0u);
   return 1;
