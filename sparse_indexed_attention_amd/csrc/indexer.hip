@@ -79,9 +79,10 @@ template <int MODE>
 constexpr int region_bytes() {
   return MODE == 0 ? 65536 : Ring<MODE>::D * NWAVE * Ring<MODE>::SLOT;
 }
-// Merge layout of the region: the selection (keys, then virtual indices turned positions),
-// the run starts of the query's splits, then the candidate runs copied in split order (keys,
-// then positions when they fit).
+// Merge layout of the region: the run starts of the query's splits at its end; the candidate
+// runs copied in split order (keys, then positions) from its start when the selection runs on
+// that list alone (merge_fast), else after a selection area (keys, then virtual indices turned
+// positions) that the general merge uses.
 constexpr int kSelCap = kMaxTopK + 64;           // the selection and one histogram bin
 constexpr int kSelBytes = kSelCap * 8;
 template <int MODE>
@@ -105,6 +106,7 @@ struct Lds {
   uint32_t* range;    // [2 * NWAVE] per-wave smallest and largest score key of the split
   int* psum;          // [NT] partial histogram sums
   uint32_t* small;    // [64] keys of one histogram bin
+  uint32_t* small_w;  // [64] merge: the wave that gathered each of them
 };
 
 struct GenericSmem {
@@ -1733,7 +1735,7 @@ __device__ __forceinline__ int merge_fast(const IndexerParams& p, int t, int K_e
     lst_emit(fk, fp, n, T, K_eff - gt, out, out_s, K_eff, L);
   } else {
     const uint32_t blo = mh.lo + ((uint32_t)bp.d << sh), bw = (1u << sh) - 1u;
-    uint32_t* const bin_wave = L.sel_key;         // wave of each gathered key (free here)
+    uint32_t* const bin_wave = L.small_w;
     const int cpw = (nc + NWAVE - 1) / NWAVE;
     const int c0 = min(nc, wave * cpw), c1 = min(nc, c0 + cpw);
     int above = 0;
@@ -1794,8 +1796,9 @@ template <int MODE>
 __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, int nsplit,
                                       const Lds& L, uint32_t& T, int& gt, bool& enough) {
   constexpr int FW = flat_words<MODE>();
-  uint32_t* pre = L.flat;
+  constexpr int RW = region_bytes<MODE>() / 4;
   const int pw = (nsplit + 4) & ~3;   // pre[0 .. nsplit], whole 16-byte words
+  uint32_t* pre = (uint32_t*)L.region + RW - pw;   // at the region's end
   const MergeHdr mh = load_headers(p, t, nsplit, pre, L);
   const int rs = p.rs;
   const size_t qb = (size_t)t * p.nsplit_max * rs;
@@ -1813,17 +1816,22 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
     for (int u = 0; u < kGatherU; ++u)
       ps[u] = v[u] >= 0 ? ld_agent(gp + r[u] * rs + v[u] - pr[u]) : 0;
   };
+  if (mh.n_real >= K_eff && 2 * n <= RW - pw) {
+    // merge_fast needs no selection area: keys and positions from the region's start
+    uint32_t* fk = (uint32_t*)L.region;
+    int32_t* fp = (int32_t*)(fk + n);
+    stage_runs(gk, gp, rs, nsplit, n, pre, fk, fp);
+    __syncthreads();
+    return merge_fast(p, t, K_eff, mh, fk, fp, L, T, gt, enough) == 1;
+  }
+  // (here merge_fast would not apply: too few candidates, or a list too long for positions)
   if (n > FW - pw) return merge_select(p, t, K_eff, mh, gkey, gpos, gpos_batch, L, T, gt, enough);
   const bool pos_in = 2 * n <= FW - pw;
-  uint32_t* fk = L.flat + pw;
+  uint32_t* fk = L.flat;
   int32_t* fp = (int32_t*)(fk + n);
   stage_runs(gk, gp, rs, nsplit, n, pre, fk, pos_in ? fp : nullptr);
   __syncthreads();
   auto lkey = [&](int v) { return fk[v]; };
-  if (pos_in) {
-    const int r = merge_fast(p, t, K_eff, mh, fk, fp, L, T, gt, enough);
-    if (r >= 0) return r == 1;
-  }
   if (pos_in) {
     auto lpos = [&](int v) { return fp[v]; };
     auto lpos_batch = [&](const int (&v)[kGatherU], int32_t (&ps)[kGatherU]) {
@@ -2115,7 +2123,7 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(Ind
   __shared__ int s_res[4], s_scan[2 * NWAVE + 2], s_wcnt[2 * NWAVE], s_bcast[4];
   __shared__ uint32_t s_range[2 * NWAVE];
   __shared__ __attribute__((aligned(16))) int s_psum[NT];
-  __shared__ uint32_t s_small[64];
+  __shared__ uint32_t s_small[64], s_small_w[64];
   Lds L;
   L.keys = s_keys;
   L.w = s_w;
@@ -2131,6 +2139,7 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(Ind
   L.range = s_range;
   L.psum = s_psum;
   L.small = s_small;
+  L.small_w = s_small_w;
   Lds Lm = L;
   Lm.hist = (int*)s_keys;
   if constexpr (QT > 1) {
