@@ -150,8 +150,9 @@ typedef struct {
  * accepted combination runs a reference path that scores in fp64.
  *
  * workspace: dsa_indexer_topk_workspace_size(...) bytes.  It MUST be zero-filled before its
- * first use; every call leaves it zero-filled again where that matters, so one buffer can be
- * reused across calls of any size up to the one it was sized for.
+ * first use; every call leaves it zero-filled again where that matters (the per-query arrival
+ * counters, kept in a block of their own at its start for up to 8192 queries), so one buffer
+ * can be reused across calls of any size up to the one it was sized for.
  * --------------------------------------------------------------------------------------- */
 size_t dsa_indexer_topk_workspace_size(int32_t num_queries, int32_t max_visible, int32_t top_k);
 

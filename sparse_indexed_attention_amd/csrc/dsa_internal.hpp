@@ -29,6 +29,11 @@ constexpr int kMaxTopK = 2048;         // largest top_k
 constexpr int kMinFastBlock = 32;      // smallest page size of the MFMA path (one page per 32-position group)
 constexpr int kMinSplit = 512;         // shortest context split
 constexpr int kCompactMaxT = 64;       // most queries of a compact indexer launch
+// The workspace starts with the queries' arrival counters, words that are zero between calls.
+// Every layout puts the rest at kCtrlBytes or later (at 4 T bytes for more queries than fit),
+// so no shape's headers or candidates land on another shape's counters, and one buffer serves
+// calls of any shape it is large enough for.
+constexpr size_t kCtrlBytes = 32768;
 constexpr int kGenericMaxHD = 8192;    // n_heads * head_dim on the reference path
 constexpr int kGenericMaxHeads = 256;
 

@@ -2238,7 +2238,9 @@ IndexerPlan plan_indexer_split(int32_t T, int32_t max_visible, int32_t top_k, in
   // one run of rs candidate slots per split
   const size_t slots = (size_t)T * pl.nsplit_max * pl.rs;
   size_t off = 0;
-  pl.off_counters = off; off = al(off + (size_t)T * 4);
+  pl.off_counters = 0;
+  off = al((size_t)T * 4);
+  if (off < kCtrlBytes) off = kCtrlBytes;
   pl.off_hdr = off;      off = al(off + (size_t)T * pl.nsplit_max * 32);
   pl.off_ckey = off;     off = al(off + slots * 4);
   pl.off_cpos = off;     off = al(off + slots * 4);

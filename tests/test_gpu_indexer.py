@@ -181,6 +181,21 @@ def test_workspace_reuse_across_sizes(dsa):
         check(inp, idx, score)
 
 
+def test_workspace_reuse_from_few_to_many_queries(dsa):
+    """A call with few queries, then one with more than 64 on the same workspace: the first
+    call's split headers must not land on the second call's arrival counters (the counters
+    keep a block of their own at the workspace's start, zero between calls)."""
+    few = scaled_spec(workload(2), seq_lens=[40000, 40000, 3000])
+    many = scaled_spec(workload(2), seq_lens=[int(x) for x in
+                                              np.random.default_rng(101).integers(2100, 9000, 100)])
+    inp_f = make_inputs(few, seed=3, with_sfa=False)
+    inp_m = make_inputs(many, seed=4, with_sfa=False)
+    ws = dsa.zeroed_workspace(dsa.indexer_workspace_bytes(100, 40000, 2048), "cuda")
+    for inp in (inp_f, inp_m, inp_f, inp_m):
+        idx, score = run_indexer(dsa, inp, workspace=ws)
+        check(inp, idx, score)
+
+
 # ---- full-size workloads (all queries, or a sample the oracle can score) ---------------------
 @pytest.mark.slow
 def test_full_decode_bf16_32k(dsa):
