@@ -337,6 +337,48 @@ def prolog_bench(args, dsa, torch, spec):
     print(json.dumps(line), flush=True)
 
 
+def record_timeline(args, dsa, torch, step, spec, V):
+    """Phase stamps (include/dsa_timeline.h) of --steps steps: for each, three steps run back to
+    back, the stamp buffer is cleared on the stream, and one more step is recorded.  Written to
+    args.timeline as JSON: per recorded step and kernel, the stamps of every workgroup that
+    started, in microseconds from that step's first indexer start (null: slot not reached);
+    the shader-clock counts and readings (slots 8-12), item words (slot 14) and merge flags (slot 15) are kept as
+    integers."""
+    words = dsa.timeline_bytes() // 8
+    buf = torch.zeros(words, dtype=torch.int64, device="cuda")
+    dsa.timeline_register(buf)
+    kernels, slots = 3, 16
+    steps_out = []
+    i = 1000
+    for _ in range(max(1, args.steps)):
+        for _ in range(3):
+            step(i)
+            i += 1
+        buf.zero_()
+        step(i)
+        i += 1
+        torch.cuda.synchronize()
+        a = buf.view(kernels, -1, slots).cpu().numpy()
+        t0 = int(a[0, :, 0][a[0, :, 0] > 0].min())
+        rec = {}
+        for k, name in enumerate(("indexer", "attention", "combine")):
+            wgs = {}
+            for wg in np.nonzero(a[k, :, 0])[0]:
+                row = a[k, wg]
+                # slots 8-12: shader-clock cycle counts and readings, kept as integers
+                wgs[int(wg)] = [int(row[s_]) if 8 <= s_ <= 12 else
+                                None if row[s_] == 0 else round((int(row[s_]) - t0) * 0.01, 2)
+                                for s_ in range(14)] + [int(row[14]), int(row[15])]
+            rec[name] = wgs
+        steps_out.append(rec)
+    dsa.timeline_register(None)
+    with open(args.timeline, "w") as f:
+        json.dump({"workload": spec.name, "queries": spec.num_queries, "visible": V,
+                   "clock": "s_memrealtime, 100 MHz", "steps": steps_out}, f)
+    print(f"bench: {len(steps_out)} recorded steps written to {args.timeline}", file=sys.stderr,
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +409,10 @@ def main():
                     help="time the indexer prolog (projections, key RMSNorm, query quantization, "
                          "key store) for the workload's new tokens instead of the step")
     ap.add_argument("--prolog-dx", type=int, default=7168, help="hidden width for --prolog")
+    ap.add_argument("--timeline", default="", metavar="PATH",
+                    help="with the measurement build (DSA_LIB_PATH=.../libdsa_timeline.so): record "
+                         "the kernels' per-workgroup phase stamps of --steps steps (each after three "
+                         "untimed ones) into PATH as JSON instead of timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel for scaling the HBM byte counters) and exit")
@@ -505,6 +551,9 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.timeline:
+        record_timeline(args, dsa, torch, step, spec, V)
+        return
 
     # The timed region: exactly --steps steps between two synchronizations, nothing else.
     t0 = time.perf_counter()

@@ -3,6 +3,8 @@
     python profile_counters.py hbm  [--config 4] [--out DIR]   # FETCH_SIZE / WRITE_SIZE
     python profile_counters.py mfma [--config 3] [--out DIR]   # MFMA busy cycles and ops
     python profile_counters.py balance [--config 6] [--out DIR] # CU busy fraction, occupancy
+    python profile_counters.py timeline [--config 4] [--out DIR] [--bench-args ...]
+                                                              # per-workgroup phase stamps
 
 Each counter pass is its own `rocprofv3 --pmc ... -- python3 bench.py ...` child process (the
 profiler's library must start with the program, so this script never touches the GPU
@@ -25,6 +27,15 @@ and the CU count), OccupancyPercent and MeanOccupancyPerActiveCU per dispatch, w
 durations of a kernel-trace pass, for the natural query order and for bench.py's zigzag order
 (4-query tiles paired head and tail).  A kernel whose work is spread evenly keeps its CUs busy
 to its end; CUs left idle while a few long workgroups finish would show as a low busy fraction.
+
+timeline: no profiler.  bench.py --timeline runs the step with the measurement build of the
+library (libdsa_timeline.so, `python -m sparse_indexed_attention_amd.build --timeline`), whose
+kernels stamp the constant 100 MHz clock at the end of each phase of every workgroup
+(include/dsa_timeline.h), for 20 recorded steps.  The summary gives, in microseconds from the
+step's first indexer workgroup start, when the phases end across workgroups (median, 90th
+percentile, latest, each the median over the recorded steps) and how long the merges' phases
+take.  The stamps add a store per phase and workgroup; the library's own timing is taken
+without them.
 """
 from __future__ import annotations
 
@@ -211,18 +222,130 @@ def balance(args):
     print("commands:\n" + "\n".join("    cd /tmp && export TMPDIR=/tmp && " + c for c in cmds))
 
 
+def _pct(xs, q):
+    import numpy as np
+    xs = [x for x in xs if x is not None]
+    return float(np.percentile(xs, q)) if xs else float("nan")
+
+
+def timeline(args):
+    lib = os.path.join(ROOT, "sparse_indexed_attention_amd", "libdsa_timeline.so")
+    if not os.path.exists(lib) and not args.from_json:
+        raise SystemExit("profile_counters: build libdsa_timeline.so first "
+                         "(python -m sparse_indexed_attention_amd.build --timeline)")
+    path = args.from_json or os.path.join(args.out, f"timeline_config{args.config}.json")
+    if args.from_json:
+        with open(path) as f:
+            return timeline_summary(json.load(f))
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--config", str(args.config),
+           "--steps", "20", "--warmup", "5", "--no-cpu-baseline", "--timeline", path,
+           *args.bench_args]
+    print("profile_counters: DSA_LIB_PATH=$ROOT/sparse_indexed_attention_amd/libdsa_timeline.so "
+          + " ".join(cmd).replace(ROOT, "$ROOT"), flush=True)
+    r = subprocess.run(["timeout", "-k", "10", "240", *cmd], env=dict(os.environ, DSA_LIB_PATH=lib))
+    if r.returncode != 0:
+        raise SystemExit(f"profile_counters: bench.py --timeline exited {r.returncode}")
+    with open(path) as f:
+        timeline_summary(json.load(f))
+
+
+def timeline_summary(data):
+    import numpy as np
+    steps = data["steps"]
+
+    def per_step(fn):
+        """median over the recorded steps of fn(step) (a number)"""
+        return float(np.median([fn(s) for s in steps]))
+
+    def col(s, kern, slot, only=None):
+        return [v[slot] for v in s[kern].values() if v[slot] is not None and (only is None or only(v))]
+
+    print(f"\n### Phase ends, {data['workload']} ({data['queries']} queries; {len(steps)} recorded "
+          f"steps; µs from the first indexer workgroup's start)\n")
+    print("| kernel | phase end | workgroups | median | p90 | latest |")
+    print("|---|---|---|---|---|---|")
+    rows = [("indexer", 0, "start", None), ("indexer", 1, "split scored", None),
+            ("indexer", 2, "candidates stored", None), ("indexer", 3, "arrival counted", None),
+            ("indexer", 4, "merge: headers read", None), ("indexer", 5, "merge: list staged", None),
+            ("indexer", 6, "merge: K-th key found", None), ("indexer", 7, "merge: output written", None),
+            ("attention", 0, "start", None), ("attention", 1, "pool rows resolved", None),
+            ("attention", 2, "first tiles and query rows landed", None),
+            ("attention", 3, "query fragments in registers", None),
+            ("attention", 4, "last tile done", None), ("attention", 5, "outputs/partials written", None),
+            ("combine", 0, "start", None), ("combine", 5, "written", None)]
+    for kern, slot, name, only in rows:
+        if not any(col(s, kern, slot) for s in steps):
+            continue
+        n = int(per_step(lambda s: len(col(s, kern, slot))))
+        print(f"| {kern} | {name} | {n} | {per_step(lambda s: _pct(col(s, kern, slot), 50)):.2f} | "
+              f"{per_step(lambda s: _pct(col(s, kern, slot), 90)):.2f} | "
+              f"{per_step(lambda s: _pct(col(s, kern, slot), 100)):.2f} |")
+    # the merges: phase durations of the merging workgroups (one per query)
+    merging = lambda v: v[15] == 1 and v[7] is not None
+    if any(any(merging(v) for v in s["indexer"].values()) for s in steps):
+        print("\n### Merges (the last-arriving split of each query)\n")
+        print("| phase | median µs | max µs |")
+        print("|---|---|---|")
+        for name, a, b in (("arrival to headers read", 3, 4), ("staging the list", 4, 5),
+                           ("finding the K-th key", 5, 6), ("writing the output", 6, 7),
+                           ("whole merge", 3, 7)):
+            ds = lambda s: [v[b] - v[a] for v in s["indexer"].values()
+                            if merging(v) and v[a] is not None and v[b] is not None]
+            print(f"| {name} | {per_step(lambda s: _pct(ds(s), 50)):.2f} | "
+                  f"{per_step(lambda s: _pct(ds(s), 100)):.2f} |")
+    print("\n### Main loops: wave 0's shader-clock cycles per step (s_memtime)\n")
+    print("| kernel | loop | steps | waiting for loads | computing (with barriers) | wait share |")
+    print("|---|---|---|---|---|---|")
+    for kern, loop in (("indexer", "key groups (scoring)"), ("attention", "tile pairs")):
+        def cyc(s, slot):
+            return [v[slot] / v[10] for v in s[kern].values() if v[10]]
+        if not any(cyc(s, 8) for s in steps):
+            continue
+        w = per_step(lambda s: _pct(cyc(s, 8), 50))
+        c = per_step(lambda s: _pct(cyc(s, 9), 50))
+        n = per_step(lambda s: _pct([v[10] for v in s[kern].values() if v[10]], 50))
+        print(f"| {kern} | {loop} | {n:.0f} | {w:.0f} | {c:.0f} | {w / (w + c):.2f} |")
+    # shader clock rate: s_memtime ticks over wall-clock µs between the two readings
+    for kern, a, b in (("indexer", 0, 1), ("attention", 0, 4)):
+        def mhz(s):
+            return [(v[12] - v[11]) / (v[b] - v[a]) for v in s[kern].values()
+                    if v[11] and v[12] and v[a] is not None and v[b] is not None and v[b] > v[a]]
+        if any(mhz(s) for s in steps):
+            print(f"\n{kern}: shader clock {per_step(lambda s: _pct(mhz(s), 50)):.0f} MHz (median over "
+                  f"workgroups of s_memtime ticks per wall-clock µs)")
+    loop0 = lambda s: [v[13] for v in s["indexer"].values() if v[13] is not None]
+    if any(loop0(s) for s in steps):
+        print(f"indexer: scoring loops start at {per_step(lambda s: _pct(loop0(s), 50)):.2f} µs (median), "
+              f"{per_step(lambda s: _pct(loop0(s), 100)):.2f} µs (latest)")
+    if any(s["attention"] for s in steps):
+        print("\n### Attention workgroups: phase durations\n")
+        print("| phase | median µs | p90 µs |")
+        print("|---|---|---|")
+        for name, a, b in (("start to rows resolved", 0, 1), ("rows resolved to first tiles landed", 1, 2),
+                           ("query fragments to registers", 2, 3), ("tile loop", 3, 4),
+                           ("writing", 4, 5), ("whole workgroup", 0, 5)):
+            ds = lambda s: [v[b] - v[a] for v in s["attention"].values()
+                            if v[a] is not None and v[b] is not None]
+            if any(ds(s) for s in steps):
+                print(f"| {name} | {per_step(lambda s: _pct(ds(s), 50)):.2f} | "
+                      f"{per_step(lambda s: _pct(ds(s), 90)):.2f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=("hbm", "mfma", "balance"))
+    ap.add_argument("mode", choices=("hbm", "mfma", "balance", "timeline"))
     ap.add_argument("--config", type=int, default=None)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "counters"))
     ap.add_argument("--write", action="store_true",
                     help="hbm: write profiles/decode_counters.json (else into --out)")
+    ap.add_argument("--from-json", default="", help="timeline: summarize a recorded file only")
+    ap.add_argument("--bench-args", nargs=argparse.REMAINDER, default=[],
+                    help="timeline: further bench.py arguments (e.g. --sfa-kv fp8)")
     args = ap.parse_args()
     if args.config is None:
-        args.config = {"hbm": 4, "mfma": 3, "balance": 6}[args.mode]
+        args.config = {"hbm": 4, "mfma": 3, "balance": 6, "timeline": 4}[args.mode]
     os.makedirs(args.out, exist_ok=True)
-    {"hbm": hbm, "mfma": mfma, "balance": balance}[args.mode](args)
+    {"hbm": hbm, "mfma": mfma, "balance": balance, "timeline": timeline}[args.mode](args)
 
 
 if __name__ == "__main__":

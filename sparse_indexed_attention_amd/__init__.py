@@ -91,8 +91,34 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dsa_indexer_prolog.argtypes = [_P, _I32, _I32, _P, _P, ctypes.c_float, _I32, _I32,
                                        _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]
     lib.dsa_indexer_prolog.restype = _I32
+    if hasattr(lib, "dsa_timeline_register"):     # the measurement build only
+        lib.dsa_timeline_bytes.argtypes = []
+        lib.dsa_timeline_bytes.restype = _SZ
+        lib.dsa_timeline_register.argtypes = [_P, _SZ]
+        lib.dsa_timeline_register.restype = _I32
     _lib = lib
     return lib
+
+
+def timeline_bytes() -> int:
+    """Size of the phase-stamp buffer (include/dsa_timeline.h); the measurement build
+    libdsa_timeline.so only (load it with DSA_LIB_PATH)."""
+    lib = load()
+    if not hasattr(lib, "dsa_timeline_bytes"):
+        raise RuntimeError("this libdsa has no phase stamps: load libdsa_timeline.so")
+    return int(lib.dsa_timeline_bytes())
+
+
+def timeline_register(buf) -> None:
+    """Registers a device buffer of timeline_bytes() for the kernels' phase stamps
+    (None stops recording); the measurement build only."""
+    lib = load()
+    if not hasattr(lib, "dsa_timeline_register"):
+        raise RuntimeError("this libdsa has no phase stamps: load libdsa_timeline.so")
+    nbytes = 0 if buf is None else buf.numel() * buf.element_size()
+    st = lib.dsa_timeline_register(_ptr(buf), nbytes)
+    if st != 0:
+        raise DsaError("dsa_timeline_register", st)
 
 
 # ------------------------------------------------------------------------------------------

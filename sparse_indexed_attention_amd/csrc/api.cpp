@@ -7,6 +7,7 @@
 #include <cstdlib>
 
 #include "../../include/dsa.h"
+#include "../../include/dsa_timeline.h"
 #include "dsa_internal.hpp"
 
 namespace {
@@ -86,9 +87,27 @@ const PlanOverrides& plan_overrides() {
   }();
   return o;
 }
+// The registered stamp buffer of the measurement build; libdsa.so has none.
+#ifdef DSA_TIMELINE
+static uint64_t* g_timeline = nullptr;
+uint64_t* timeline_buffer() { return g_timeline; }
+#else
+uint64_t* timeline_buffer() { return nullptr; }
+#endif
 }  // namespace dsa
 
 extern "C" {
+
+#ifdef DSA_TIMELINE
+size_t dsa_timeline_bytes(void) { return (size_t)kTlKernels * kTlMaxWg * kTlSlots * sizeof(uint64_t); }
+
+dsa_status dsa_timeline_register(void* buf, size_t bytes) {
+  if (buf && bytes < dsa_timeline_bytes()) return DSA_ERR_WORKSPACE;
+  if (misaligned(buf)) return DSA_ERR_ALIGN;
+  g_timeline = static_cast<uint64_t*>(buf);
+  return DSA_OK;
+}
+#endif
 
 size_t dsa_indexer_topk_workspace_size(int32_t num_queries, int32_t max_visible, int32_t top_k) {
   if (num_queries < 1 || max_visible < 1 || max_visible > DSA_MAX_CONTEXT || top_k < 1) return 0;
@@ -150,6 +169,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
   p.hdr = reinterpret_cast<uint32_t*>(ws + pl.off_hdr);
   p.cand_key = reinterpret_cast<uint32_t*>(ws + pl.off_ckey);
   p.cand_pos = reinterpret_cast<int32_t*>(ws + pl.off_cpos);
+  p.tl = timeline_buffer();
   const hipError_t e = launch_indexer(p, indexer_fast(q_dtype, k_dtype, n_heads, head_dim, layout),
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
@@ -218,6 +238,7 @@ dsa_status dsa_sparse_attn(const void* q, dsa_dtype dtype, const void* kv_pool,
   p.flags = reinterpret_cast<uint32_t*>(ws + pl.off_flags);
   p.part_o = ws + pl.off_part;
   p.part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
+  p.tl = timeline_buffer();
   const hipError_t e = launch_sfa(p, fast, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

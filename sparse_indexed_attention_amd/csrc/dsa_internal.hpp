@@ -21,6 +21,74 @@ struct PlanOverrides {
 };
 const PlanOverrides& plan_overrides();
 
+// ------------------------------------------------------------------ phase stamps
+// The measurement build of the library (-DDSA_TIMELINE, libdsa_timeline.so; never libdsa.so)
+// records when each workgroup ends each phase of its work: thread 0 writes the 100 MHz
+// constant clock (s_memrealtime) into a device buffer the caller registers
+// (dsa_timeline_register), laid out as u64 [kernel][workgroup][slot]; a slot a workgroup
+// never reaches keeps the caller's zero.  Without the macro the stamps compile to nothing and
+// the parameter blocks' `tl` pointer stays null.
+constexpr int kTlMaxWg = 4096, kTlSlots = 16;
+enum { kTlIndexer = 0, kTlSfa = 1, kTlCombine = 2, kTlKernels = 3 };
+// slots of the indexer (single-query items): start, scored, candidates stored, arrived, and
+// for the merging workgroup headers read, list staged, K-th key found, output written; the
+// item (t << 16 | j) and whether it merged go to kTlItem and kTlLast
+enum { kTlStart = 0, kTlScored = 1, kTlEmitted = 2, kTlArrived = 3, kTlHeaders = 4,
+       kTlStaged = 5, kTlKth = 6, kTlMerged = 7, kTlItem = 14, kTlLast = 15 };
+// slots of the attention kernels: start, rows resolved, first tiles and query rows landed,
+// query fragments in registers, last tile done, outputs or partials written
+enum { kTlRows = 1, kTlFirstTile = 2, kTlQueries = 3, kTlLoopDone = 4, kTlWritten = 5 };
+// both: wave 0's shader-clock cycles waiting for loads and computing in the main loop, and its
+// steps (key groups or tile pairs)
+enum { kTlWaitCycles = 8, kTlComputeCycles = 9, kTlSteps = 10 };
+// both: the shader clock (s_memtime) at the start and at the end of the main loop's phase
+// (indexer: split scored; attention: last tile done), for the clock rate; indexer: the wall
+// clock when the scoring loop starts
+enum { kTlClockStart = 11, kTlClockEnd = 12, kTlLoopStart = 13 };
+uint64_t* timeline_buffer();   // the registered buffer (measurement build), else nullptr
+#ifdef DSA_TIMELINE
+__device__ __forceinline__ void tl_put(uint64_t* tl, int kernel, int slot, uint64_t v) {
+  const int wg = blockIdx.x + blockIdx.y * gridDim.x;
+  if (tl != nullptr && threadIdx.x == 0 && wg < kTlMaxWg)
+    tl[((size_t)kernel * kTlMaxWg + wg) * kTlSlots + slot] = v;
+}
+__device__ __forceinline__ void tl_stamp(uint64_t* tl, int kernel, int slot) {
+  tl_put(tl, kernel, slot, __builtin_amdgcn_s_memrealtime());
+}
+__device__ __forceinline__ void tl_clock(uint64_t* tl, int kernel, int slot) {
+  tl_put(tl, kernel, slot, __builtin_amdgcn_s_memtime());
+}
+// Shader-clock cycles (s_memtime) wave 0 spends waiting for a loop's loads and computing, over
+// the loop's steps: slots kTlWaitCycles, kTlComputeCycles and kTlSteps.
+struct TlCycles {
+  uint64_t w = 0, c = 0, t = 0;
+  __device__ __forceinline__ void mark() { t = __builtin_amdgcn_s_memtime(); }
+  __device__ __forceinline__ void waited() {
+    const uint64_t n = __builtin_amdgcn_s_memtime();
+    w += n - t;
+    t = n;
+  }
+  __device__ __forceinline__ void computed() { c += __builtin_amdgcn_s_memtime() - t; }
+  __device__ __forceinline__ void put(uint64_t* tl, int kernel, int steps) {
+    if (threadIdx.x < 64) {
+      tl_put(tl, kernel, kTlWaitCycles, w);
+      tl_put(tl, kernel, kTlComputeCycles, c);
+      tl_put(tl, kernel, kTlSteps, (uint64_t)steps);
+    }
+  }
+};
+#else
+__device__ __forceinline__ void tl_put(uint64_t*, int, int, uint64_t) {}
+__device__ __forceinline__ void tl_stamp(uint64_t*, int, int) {}
+__device__ __forceinline__ void tl_clock(uint64_t*, int, int) {}
+struct TlCycles {
+  __device__ __forceinline__ void mark() {}
+  __device__ __forceinline__ void waited() {}
+  __device__ __forceinline__ void computed() {}
+  __device__ __forceinline__ void put(uint64_t*, int, int) {}
+};
+#endif
+
 // ------------------------------------------------------------------ indexer + Top-K
 constexpr int kIdxThreads = 256;
 constexpr int kSplitMax = 2048;        // context positions scored by one workgroup
@@ -67,6 +135,7 @@ struct IndexerParams {
   uint32_t* hdr;        // [T][nsplit_max][8]   emitted count, threshold key, key range
   uint32_t* cand_key;   // [T][nsplit_max][rs] one run of candidates per split: keys
   int32_t* cand_pos;    // [T][nsplit_max][rs] ... and positions
+  uint64_t* tl;         // phase stamps (measurement build only), else nullptr
 };
 
 IndexerPlan plan_indexer_split(int32_t T, int32_t max_visible, int32_t top_k, int32_t split);
@@ -107,6 +176,7 @@ struct SfaParams {
   uint32_t* flags;        // [T][H/32][nsplit] bit c: head 32g + c to recompute by the reference method
   void* part_o;           // [T][H/32][nsplit] 32 KB blocks of fp16 partial outputs
   float* part_ml;         // [T][H][nsplit][2] exponent reference (exp2 domain), sum
+  uint64_t* tl;           // phase stamps (measurement build only), else nullptr
 };
 
 SfaPlan plan_sfa(int32_t T, int32_t H, int32_t K, int32_t dv, bool fast_path, bool kv_fp8);

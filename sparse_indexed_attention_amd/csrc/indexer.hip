@@ -288,26 +288,53 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
     }
     __syncthreads();
   }
-  if (g0 >= g1) {
-    if constexpr (MX) __syncthreads();
-    return;
-  }
   static_assert(kSplitMax / 32 / NWAVE <= 64, "one lane per group of a wave's run");
-  // One round trip brings the query (registers), this wave's copy of the head weights (LDS)
-  // and the pages of its groups (lane l: the block id of group g0 + l).
-  const uint16_t* qsrc = MX ? (const uint16_t*)L.region : qb;
-  bf16x8 a0[8], a1[8];
+  // The query's 64 x 128 bf16 values (16 KB): with MXFP8 keys the workgroup has just left
+  // their dequantized values at the region's start; otherwise they land once per workgroup
+  // in the ring's last slots (slot D - 1 of every wave, at least 16 KB, first filled by the
+  // loop's first step), with the 16-byte chunk c of head row r at chunk c ^ (r & 15), so
+  // that the fragment reads below (32 heads at one chunk) fall in distinct banks.  Four
+  // waves loading their fragments straight from global memory would fetch each query four
+  // times per workgroup, about 32 MB across a decode launch at its start.
+  static_assert(NWAVE * SLOT >= 64 * 128 * 2, "the query fits in the ring's last slots");
+  uint8_t* const qland = L.region + (D - 1) * (NWAVE * SLOT);
+  if constexpr (!MX) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    a0[s] = *(const bf16x8*)(qsrc + col * 128 + half * 64 + 8 * s);
-    a1[s] = *(const bf16x8*)(qsrc + (32 + col) * 128 + half * 64 + 8 * s);
+    for (int u = 0; u < 16 / NWAVE; ++u) {
+      const int P = 64 * (wave + NWAVE * u) + lane;    // landing chunk: row P / 16, slot P % 16
+      const int r = P >> 4;
+      load_to_lds<16>(qb, (uint32_t)(r * 256 + 16 * ((P & 15) ^ (r & 15))),
+                      lds_addr(qland + 1024 * (wave + NWAVE * u)));
+    }
   }
-  if constexpr (MX) __syncthreads();
+  // One round trip brings the query, this wave's copy of the head weights (LDS) and the
+  // pages of its groups (lane l: the block id of group g0 + l).
   const float* lw = L.w + wave * 64;
   load_to_lds<4>(p.w + (size_t)t * 64, 4u * lane, lds_addr(lw));
   int gblk = 0;
   if constexpr (PAGED)
-    gblk = p.L.bt[(int64_t)seq * p.L.bt_stride + ((start + 32 * min(g0 + lane, g1 - 1)) >> p.L.bs_log2)];
+    gblk = p.L.bt[(int64_t)seq * p.L.bt_stride + ((start + 32 * max(0, min(g0 + lane, g1 - 1))) >> p.L.bs_log2)];
+  wait_vmcnt<0>();
+  __syncthreads();                            // every wave's share of the query has landed
+  bf16x8 a0[8], a1[8];
+  if constexpr (MX) {
+    const uint16_t* qsrc = (const uint16_t*)L.region;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      a0[s] = *(const bf16x8*)(qsrc + col * 128 + half * 64 + 8 * s);
+      a1[s] = *(const bf16x8*)(qsrc + (32 + col) * 128 + half * 64 + 8 * s);
+    }
+  } else {
+    // head col and 32 + col share the swizzle (32 is a multiple of 16)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int ch = (8 * half + s) ^ (col & 15);
+      a0[s] = *(const bf16x8*)(qland + col * 256 + 16 * ch);
+      a1[s] = *(const bf16x8*)(qland + (32 + col) * 256 + 16 * ch);
+    }
+  }
+  __syncthreads();                            // every wave holds its fragments: the ring may start
+  if (g0 >= g1) return;
   uint32_t& kmin = kr_lo;
   uint32_t& kmax = kr_hi;
   const int bsl = PAGED ? p.L.bs_log2 : 0;
@@ -397,24 +424,39 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
     }
   };
 
-  // The query must be in registers before the ring starts: left pending, the compiler's wait
-  // for it would sit inside the loop and drain the ring on every step.
-  wait_vmcnt<0>();
-  for (int k = 0; k < D - 1; ++k) issue(g0 + k, slot_of(k));
+  // The query is in registers (the fragment reads above completed before the barrier), so
+  // the only loads in flight in the loop are the ring's, and the loop's waits count them
+  // exactly.  Only the split's own groups are loaded: at step g the groups g + 1 .. up to
+  // g + D - 1 that exist are in flight, so nothing is left to drain after the last step.
+  tl_stamp(p.tl, kTlIndexer, kTlLoopStart);
+  for (int k = 0; k < D - 1 && g0 + k < g1; ++k) issue(g0 + k, slot_of(k));
+  TlCycles tc;
 #pragma unroll 1
   for (int g = g0; g < g1; ++g) {
     const int k = (g - g0) & (D - 1);
-    // refill the slot consumed in the previous step (its LDS reads have completed)
-    issue(g + D - 1, slot_of((k + D - 1) & (D - 1)));
-    wait_vmcnt<LPG * (D - 1)>();              // group g has landed in LDS
+    const int ahead = g1 - 1 - g;              // groups after g
+    tc.mark();
+    if (ahead >= D - 1) {
+      // refill the slot consumed in the previous step (its LDS reads have completed)
+      issue(g + D - 1, slot_of((k + D - 1) & (D - 1)));
+      wait_vmcnt<LPG * (D - 1)>();            // group g has landed in LDS
+    } else if (D > 3 && ahead == 2) {
+      wait_vmcnt<LPG * 2>();
+    } else if (D > 2 && ahead == 1) {
+      wait_vmcnt<LPG>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    tc.waited();
     const uint8_t* sb = slot_of(k);
     f32x16 acc0, acc1;
     products(sb, acc0, acc1);
     // both chains are issued before any accumulator is read, so they interleave
     __builtin_amdgcn_sched_barrier(0);
     finish(g, acc0, acc1, FP8 && !MX ? *(const float*)(sb + GB + 4 * col) : 1.f);
+    tc.computed();
   }
-  wait_vmcnt<0>();                            // no load may still target the ring afterwards
+  tc.put(p.tl, kTlIndexer, g1 - g0);
 }
 
 // Multi-query scoring (bf16, fp8 or MXFP8 keys, kMqQ queries of one sequence over one split, as in a
@@ -1731,6 +1773,7 @@ __device__ __forceinline__ int merge_fast(const IndexerParams& p, int t, int K_e
     const Kth kt = lst_kth(fk, n, K_eff, mh.lo, mh.hi, L);
     T = kt.T;
     gt = kt.gt;
+    tl_stamp(p.tl, kTlIndexer, kTlKth);
     if (mh.max_tau > T) return 0;
     lst_emit(fk, fp, n, T, K_eff - gt, out, out_s, K_eff, L);
   } else {
@@ -1773,6 +1816,7 @@ __device__ __forceinline__ int merge_fast(const IndexerParams& p, int t, int K_e
     const int l = __builtin_ctzll(hit);
     T = (uint32_t)__builtin_amdgcn_readlane((int)v, l);
     gt = bp.above + __builtin_amdgcn_readlane(g, l);
+    tl_stamp(p.tl, kTlIndexer, kTlKth);
     if (mh.max_tau > T) return 0;
     const int need = K_eff - gt;
     int slot = 0, eq = 0;   // taken entries and ties before this wave's range
@@ -1786,6 +1830,7 @@ __device__ __forceinline__ int merge_fast(const IndexerParams& p, int t, int K_e
   }
   pad_output(p, t, K_eff);
   if (threadIdx.x == 0) st_agent(p.counters + t, 0u);
+  tl_stamp(p.tl, kTlIndexer, kTlMerged);
   return 1;
 }
 
@@ -1800,6 +1845,7 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
   const int pw = (nsplit + 4) & ~3;   // pre[0 .. nsplit], whole 16-byte words
   uint32_t* pre = (uint32_t*)L.region + RW - pw;   // at the region's end
   const MergeHdr mh = load_headers(p, t, nsplit, pre, L);
+  tl_stamp(p.tl, kTlIndexer, kTlHeaders);
   const int rs = p.rs;
   const size_t qb = (size_t)t * p.nsplit_max * rs;
   const uint32_t* gk = p.cand_key + qb;
@@ -1822,6 +1868,7 @@ __device__ __forceinline__ bool merge(const IndexerParams& p, int t, int K_eff, 
     int32_t* fp = (int32_t*)(fk + n);
     stage_runs(gk, gp, rs, nsplit, n, pre, fk, fp);
     __syncthreads();
+    tl_stamp(p.tl, kTlIndexer, kTlStaged);
     return merge_fast(p, t, K_eff, mh, fk, fp, L, T, gt, enough) == 1;
   }
   // (here merge_fast would not apply: too few candidates, or a list too long for positions)
@@ -1869,6 +1916,7 @@ __device__ __forceinline__ bool run_item(const IndexerParams& p, int t, int j, c
   if (j >= nsplit) return false;
   const int seq = p.q_seq[t];
   const int K_eff = min(p.K, V);
+  tl_put(p.tl, kTlIndexer, kTlItem, ((uint64_t)t << 16) | (uint32_t)j);
 
   const GenericSmem* gsp = nullptr;
   if constexpr (MODE == 0) {
@@ -1925,6 +1973,10 @@ __device__ __forceinline__ bool run_item(const IndexerParams& p, int t, int j, c
     const int start = cur * split, len = min(split, V - start);
     uint32_t klo = klo0, khi = khi0;
     if (!prescored || refill) score_split<MODE>(p, t, seq, start, len, L, gsp, klo, khi);
+    if (!refill) {
+      tl_stamp(p.tl, kTlIndexer, kTlScored);
+      tl_clock(p.tl, kTlIndexer, kTlClockEnd);
+    }
 
     if (!refill) {
       if (nsplit == 1) {
@@ -1995,9 +2047,12 @@ __device__ __forceinline__ bool run_item(const IndexerParams& p, int t, int j, c
       if (phase == 3) return false;
       wait_all_memory();
       __syncthreads();
+      tl_stamp(p.tl, kTlIndexer, kTlEmitted);
       if (threadIdx.x == 0)
         L.bcast[0] = add_agent(p.counters + t, 1u) == (uint32_t)(nsplit - 1);
       __syncthreads();
+      tl_stamp(p.tl, kTlIndexer, kTlArrived);
+      tl_put(p.tl, kTlIndexer, kTlLast, L.bcast[0] ? 1u : 0u);
       if (!L.bcast[0]) return false;
       if (phase == 1) return true;
       if (merge<MODE>(p, t, K_eff, nsplit, Lm, T, gt, enough)) return false;
@@ -2163,6 +2218,8 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(Ind
   // workgroups spread over all the CUs, and within a block of T workgroups the queries are
   // rotated by j so that each query's splits spread over the XCDs.
   __shared__ int s_pre[kCompactMaxT + 1];
+  tl_stamp(p.tl, kTlIndexer, kTlStart);
+  tl_clock(p.tl, kTlIndexer, kTlClockStart);
   int n_items = gridDim.x;
   if (p.compact) {
     if ((int)threadIdx.x < p.T) {

@@ -147,6 +147,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   const int cc = (qq / p.n_hg) * 8 + xcd;
   if (cc >= p.T * p.nsplit) return;
   const int t = cc / p.nsplit, r = cc - t * p.nsplit;
+  tl_stamp(p.tl, kTlSfa, kTlStart);
+  tl_clock(p.tl, kTlSfa, kTlClockStart);
+  tl_put(p.tl, kTlSfa, kTlItem, ((uint64_t)t << 16) | ((uint32_t)hg << 8) | (uint32_t)r);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -580,6 +583,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
       pm[1] = lt;
     }
   }
+  tl_stamp(p.tl, kTlSfa, kTlWritten);
   if (lane == 0) p.flags[((size_t)t * (p.H / 32) + hw) * p.nsplit + r] = flagword;
 }
 
@@ -642,6 +646,9 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
   const int cc = (qq / p.n_hg) * 8 + xcd;
   if (cc >= p.T * p.nsplit) return;
   const int t = cc / p.nsplit, r = cc - t * p.nsplit;
+  tl_stamp(p.tl, kTlSfa, kTlStart);
+  tl_clock(p.tl, kTlSfa, kTlClockStart);
+  tl_put(p.tl, kTlSfa, kTlItem, ((uint64_t)t << 16) | ((uint32_t)hg << 8) | (uint32_t)r);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -691,6 +698,7 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
     }
   }
   __syncthreads();                                 // rows ready; the staged block table is free
+  tl_stamp(p.tl, kTlSfa, kTlRows);
 
   const uint8_t* kv = (const uint8_t*)p.kv;
   const uint8_t* zero = (const uint8_t*)p.zero;
@@ -730,7 +738,9 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
   // row layout (in buffers 2 and 3; with fp8 rows in the front of the region), behind pair 0's
   // tiles; each wave then reads its 32 heads' fragments from there.  Two waves share each head
   // half, so loading the fragments from global memory directly would fetch every query twice.
-  // Pair 1 goes into the landing place once every wave has its fragments.
+  // Pair 1 goes into the landing place once every wave has its fragments.  (Requesting the
+  // query rows first, so that pair 1 could follow sooner, measured the same: a workgroup's
+  // time is set by the bytes it brings in, not their order.)
   {
     const uint8_t* qrows = (const uint8_t*)p.q + ((size_t)t * p.H + hg * 64) * kRowBytes;
     constexpr int QLOADS = 2 * kTileSlots / 64;    // 73: 64 rows of 73 slots
@@ -743,12 +753,14 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
   }
   wait_vmcnt<0>();
   __syncthreads();                                 // pair 0 and the query tile have landed
+  tl_stamp(p.tl, kTlSfa, kTlFirstTile);
   {
     const uint8_t* qr = qland + tile_off(32 * hq + c, hh);   // head 32 hq + c, dims 8 hh + 16 s
 #pragma unroll
     for (int s = 0; s < 36; ++s) qk[s] = *(const bf16x8*)(qr + 32 * s);
   }
   __syncthreads();                                 // every wave holds its fragments
+  tl_stamp(p.tl, kTlSfa, kTlQueries);
   if (npairs > 1) issue_pair(1);
 
   const float scale2 = p.scale * kLog2e;
@@ -763,14 +775,17 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
   const int vrow = 4 * hh + (vi >> 2);
   const int vdim = 16 * (c >> 4) + 4 * (vi & 3);
 
+  TlCycles tc;
   for (int pr = 0; pr < npairs; ++pr) {
     const int b0 = pair_buf(pr);
     // Pairs 0 and 1 are issued before the loop, pair pr + 1 (pr >= 1) right after pair pr
     // opens: so only at pair 0 is a later pair in flight while waiting.
+    tc.mark();
     if (pr == 0 && npairs > 1) wait_vmcnt<(2 * LPW_MIN < 63 ? 2 * LPW_MIN : 63)>();
     else wait_vmcnt<0>();
     __syncthreads();                               // every wave's loads of pair pr have landed,
                                                    // and every wave is done with pair pr - 1
+    tc.waited();
     if (pr >= 1 && pr + 1 < npairs) issue_pair(pr + 1);   // into pair pr - 1's buffers
     // S^T for tile 2 pr + par, heads h0 .. h0 + 31
     const int tile = 2 * pr + par;
@@ -903,6 +918,7 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
           for (int kk = 0; kk < 4; ++kk)
             o[hb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb][kk], b[kk], o[hb][nb], 0, 0, 0);
       }
+      tc.computed();
       continue;
     }
 #pragma unroll
@@ -932,8 +948,12 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
         for (int kk = 0; kk < 4; ++kk)
           o[hb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb][kk], b[kk], o[hb][nb], 0, 0, 0);
     }
+    tc.computed();
   }
 
+  tl_stamp(p.tl, kTlSfa, kTlLoopDone);
+  tl_clock(p.tl, kTlSfa, kTlClockEnd);
+  tc.put(p.tl, kTlSfa, npairs);
   // per-head totals over the two tiles of each pair; flags of both waves of a head half
   const float lw = xhalf_sum(l);
   const uint32_t ow = (uint32_t)__ballot(over);
@@ -1002,6 +1022,7 @@ __global__ __launch_bounds__(256, 1) void sfa_mfma64_kernel(SfaParams p) {
       pm[1] = lt;
     }
   }
+  tl_stamp(p.tl, kTlSfa, kTlWritten);
   if (par == 0 && lane == 0) p.flags[((size_t)t * (p.H / 32) + hg * 2 + hq) * p.nsplit + r] = flagword;
 }
 
@@ -1127,6 +1148,7 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
   const int hw = hg * HB + hb;                        // 32-head block
   const int hb0 = hw * 32 + 16 * half;                // heads hb0 .. hb0 + 15
   const int S = p.nsplit;
+  tl_stamp(p.tl, kTlCombine, kTlStart);
   const int nslot = NB * 64;
   const int nrec = HB * 4 * (NB / 2);                 // records of one attention wave
   const uint8_t* blk = (const uint8_t*)p.part_o + (((size_t)t * p.n_hg + hg) * DWV + w) * nrec * S * 1024;
@@ -1218,6 +1240,7 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(SfaParams 
     }
   }
   __syncthreads();
+  tl_stamp(p.tl, kTlCombine, kTlWritten);
   uint32_t mm = (w == 0 ? flagged : 0u) | nonfinite;
   while (mm) {
     const int k = __builtin_ctz(mm);
