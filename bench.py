@@ -347,7 +347,8 @@ def record_timeline(args, dsa, torch, step, spec, V):
     words = dsa.timeline_bytes() // 8
     buf = torch.zeros(words, dtype=torch.int64, device="cuda")
     dsa.timeline_register(buf)
-    kernels, slots = 3, 16
+    kernels = 3
+    slots = words // (kernels * 4096)
     steps_out = []
     i = 1000
     for _ in range(max(1, args.steps)):
@@ -365,10 +366,11 @@ def record_timeline(args, dsa, torch, step, spec, V):
             wgs = {}
             for wg in np.nonzero(a[k, :, 0])[0]:
                 row = a[k, wg]
-                # slots 8-12: shader-clock cycle counts and readings, kept as integers
-                wgs[int(wg)] = [int(row[s_]) if 8 <= s_ <= 12 else
+                # slots 8-12: shader-clock cycle counts and readings, 14-15: item word and
+                # merge flag, kept as integers; the others are stamps
+                wgs[int(wg)] = [int(row[s_]) if (8 <= s_ <= 12 or s_ in (14, 15)) else
                                 None if row[s_] == 0 else round((int(row[s_]) - t0) * 0.01, 2)
-                                for s_ in range(14)] + [int(row[14]), int(row[15])]
+                                for s_ in range(slots)]
             rec[name] = wgs
         steps_out.append(rec)
     dsa.timeline_register(None)

@@ -11,14 +11,20 @@
  *
  *   uint64 stamps[kernel][workgroup][slot],  kernel 0 = indexer, 1 = attention, 2 = combine,
  *                                            workgroup < 4096 (flattened grid index),
- *                                            slot < 16.
+ *                                            slot < 32.
  *
  * Indexer slots: 0 start, 1 split scored, 2 candidates stored, 3 arrival counted, and for the
  * workgroup that merges its query: 4 headers read, 5 list staged, 6 K-th key found, 7 output
- * written; slot 14 holds (query << 16 | split) and slot 15 is 1 for the merging workgroup.
+ * written; slot 14 holds (query << 16 | split) and slot 15 is 1 for the merging workgroup;
+ * slot 16 the split's candidate cut chosen, 17 its candidate and header stores issued (slot 2
+ * ends their drain), 18 the merge's bin of the K-th key found.  Slots 8-10 hold wave 0's
+ * shader-clock cycles waiting for loads and computing in the scoring loop and its steps, 11 and
+ * 12 the shader clock (s_memtime) at the start and after scoring, 13 the scoring loop's start.
  * Attention slots: 0 start, 1 pool rows resolved, 2 first tile pair and query rows landed, 3 query
  * fragments in registers, 4 last tile done, 5 outputs or partials written; slot 14 holds
- * (query << 16 | head group << 8 | slice).  Combine slots: 0 start, 5 written.
+ * (query << 16 | head group << 8 | slice), slots 8-10 the tile loop's wait and compute cycles
+ * and steps, 11 and 12 the shader clock at the start and after the last tile.  Combine slots:
+ * 0 start, 5 written.
  *
  * A slot a workgroup never reaches keeps whatever the caller left there: clear the buffer
  * before the call whose stamps you want.  Stamps are plain stores, visible once the stream
@@ -35,7 +41,7 @@
 extern "C" {
 #endif
 
-/* Bytes the stamp buffer must hold: 3 kernels x 4096 workgroups x 16 slots x 8. */
+/* Bytes the stamp buffer must hold: 3 kernels x 4096 workgroups x 32 slots x 8. */
 size_t dsa_timeline_bytes(void);
 
 /* Registers `buf` (device memory of at least dsa_timeline_bytes(), 16-byte aligned; owned by

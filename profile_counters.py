@@ -280,6 +280,24 @@ def timeline_summary(data):
         print(f"| {kern} | {name} | {n} | {per_step(lambda s: _pct(col(s, kern, slot), 50)):.2f} | "
               f"{per_step(lambda s: _pct(col(s, kern, slot), 90)):.2f} | "
               f"{per_step(lambda s: _pct(col(s, kern, slot), 100)):.2f} |")
+    # a split's steps from scoring to arrival (finer stamps; absent in older records)
+    def steps_of(pairs, kern, only=None):
+        rows_ = []
+        for name, a, b in pairs:
+            ds = lambda s: [v[b] - v[a] for v in s[kern].values()
+                            if len(v) > max(a, b) and v[a] is not None and v[b] is not None
+                            and (only is None or only(v))]
+            if any(ds(s) for s in steps):
+                rows_.append(f"| {name} | {per_step(lambda s: _pct(ds(s), 50)):.2f} | "
+                             f"{per_step(lambda s: _pct(ds(s), 90)):.2f} |")
+        return rows_
+    r_ = steps_of((("choosing the cut", 1, 16), ("issuing candidate and header stores", 16, 17),
+                   ("draining the stores", 17, 2), ("counting the arrival", 2, 3)), "indexer")
+    if r_:
+        print("\n### A split from scored to arrived\n")
+        print("| step | median µs | p90 µs |")
+        print("|---|---|---|")
+        print("\n".join(r_))
     # the merges: phase durations of the merging workgroups (one per query)
     merging = lambda v: v[15] == 1 and v[7] is not None
     if any(any(merging(v) for v in s["indexer"].values()) for s in steps):
@@ -287,10 +305,13 @@ def timeline_summary(data):
         print("| phase | median µs | max µs |")
         print("|---|---|---|")
         for name, a, b in (("arrival to headers read", 3, 4), ("staging the list", 4, 5),
+                           ("finding the K-th key's bin", 5, 18), ("from the bin to the K-th key", 18, 6),
                            ("finding the K-th key", 5, 6), ("writing the output", 6, 7),
                            ("whole merge", 3, 7)):
             ds = lambda s: [v[b] - v[a] for v in s["indexer"].values()
-                            if merging(v) and v[a] is not None and v[b] is not None]
+                            if merging(v) and len(v) > max(a, b) and v[a] is not None and v[b] is not None]
+            if not any(ds(s) for s in steps):
+                continue
             print(f"| {name} | {per_step(lambda s: _pct(ds(s), 50)):.2f} | "
                   f"{per_step(lambda s: _pct(ds(s), 100)):.2f} |")
     print("\n### Main loops: wave 0's shader-clock cycles per step (s_memtime)\n")

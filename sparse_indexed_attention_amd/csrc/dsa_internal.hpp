@@ -28,13 +28,16 @@ const PlanOverrides& plan_overrides();
 // (dsa_timeline_register), laid out as u64 [kernel][workgroup][slot]; a slot a workgroup
 // never reaches keeps the caller's zero.  Without the macro the stamps compile to nothing and
 // the parameter blocks' `tl` pointer stays null.
-constexpr int kTlMaxWg = 4096, kTlSlots = 16;
+constexpr int kTlMaxWg = 4096, kTlSlots = 32;
 enum { kTlIndexer = 0, kTlSfa = 1, kTlCombine = 2, kTlKernels = 3 };
 // slots of the indexer (single-query items): start, scored, candidates stored, arrived, and
 // for the merging workgroup headers read, list staged, K-th key found, output written; the
 // item (t << 16 | j) and whether it merged go to kTlItem and kTlLast
 enum { kTlStart = 0, kTlScored = 1, kTlEmitted = 2, kTlArrived = 3, kTlHeaders = 4,
        kTlStaged = 5, kTlKth = 6, kTlMerged = 7, kTlItem = 14, kTlLast = 15 };
+// finer indexer slots: the split's cut chosen, its candidate and header stores issued (before
+// the drain that kTlEmitted ends), and in the merge the bin of the K-th key found
+enum { kTlCut = 16, kTlStoresIssued = 17, kTlKthBin = 18 };
 // slots of the attention kernels: start, rows resolved, first tiles and query rows landed,
 // query fragments in registers, last tile done, outputs or partials written
 enum { kTlRows = 1, kTlFirstTile = 2, kTlQueries = 3, kTlLoopDone = 4, kTlWritten = 5 };

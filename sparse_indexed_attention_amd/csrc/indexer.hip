@@ -1769,6 +1769,7 @@ __device__ __forceinline__ int merge_fast(const IndexerParams& p, int t, int K_e
   const uint32_t width = mh.hi - mh.lo;
   const int sh = range_shift(width);
   const BinPick bp = lst_rank_bin(fk, n, mh.lo, width, sh, K_eff, L);
+  tl_stamp(p.tl, kTlIndexer, kTlKthBin);
   if (sh == 0 || bp.c > 64) {
     const Kth kt = lst_kth(fk, n, K_eff, mh.lo, mh.hi, L);
     T = kt.T;
@@ -2025,6 +2026,7 @@ __device__ __forceinline__ bool run_item(const IndexerParams& p, int t, int j, c
         }
         // this split's run of the candidate area
         cnt = min(cnt, cap);
+        tl_stamp(p.tl, kTlIndexer, kTlCut);
         const size_t cb = ((size_t)t * p.nsplit_max + cur) * p.rs;
         block_emit(kb, tau, 0x7fffffff,
                    [&](int slot, int i, uint32_t k) {
@@ -2044,6 +2046,7 @@ __device__ __forceinline__ bool run_item(const IndexerParams& p, int t, int j, c
         }
       }
       // arrival: the last split of this query to arrive merges
+      tl_stamp(p.tl, kTlIndexer, kTlStoresIssued);
       if (phase == 3) return false;
       wait_all_memory();
       __syncthreads();

@@ -47,7 +47,7 @@ def tl_lib():
 
 def test_timeline_build_exports_and_validates(tl_lib):
     nbytes = tl_lib.dsa_timeline_bytes()
-    assert nbytes == 3 * 4096 * 16 * 8
+    assert nbytes == 3 * 4096 * 32 * 8
     # the pointer is only recorded, never dereferenced on the host
     assert tl_lib.dsa_timeline_register(0x1000, nbytes - 8) == 5      # DSA_ERR_WORKSPACE
     assert tl_lib.dsa_timeline_register(0x1008, nbytes) == 6          # DSA_ERR_ALIGN
