@@ -137,14 +137,19 @@ def indexer_flops(spec, V):
 
 
 def source_digest():
-    """Digest of the kernel sources' code: comments and blank space are dropped first, so that a
-    comment edit does not detach the committed counter figures from the code they were taken on."""
+    """Digest of the kernel sources' code: comments, blank space and the phase-stamp statements
+    (empty in libdsa.so) are dropped first, so that neither detaches the committed counter
+    figures from the code they were taken on."""
     h = hashlib.sha256()
     for f in ("indexer.hip", "sfa.hip", "dsa_common.hpp", "dsa_internal.hpp"):
         with open(os.path.join(ROOT, "sparse_indexed_attention_amd", "csrc", f)) as fh:
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
+        # phase-stamp statements compile to nothing outside the measurement build
+        src = re.sub(r"\btl_(stamp|put|clock)\([^;]*\);", " ", src)
+        src = re.sub(r"\btc\.(mark|waited|computed|put)\([^;]*\);", " ", src)
+        src = re.sub(r"\bTlCycles tc;", " ", src)
         h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 

@@ -365,6 +365,7 @@ def main():
     args = ap.parse_args()
     if args.config is None:
         args.config = {"hbm": 4, "mfma": 3, "balance": 6, "timeline": 4}[args.mode]
+    args.out = os.path.abspath(args.out)        # the profiler runs from /tmp
     os.makedirs(args.out, exist_ok=True)
     {"hbm": hbm, "mfma": mfma, "balance": balance, "timeline": timeline}[args.mode](args)
 
