@@ -169,6 +169,7 @@ dsa_status dsa_indexer_topk(const void* q, dsa_dtype q_dtype, const float* head_
   p.hdr = reinterpret_cast<uint32_t*>(ws + pl.off_hdr);
   p.cand_key = reinterpret_cast<uint32_t*>(ws + pl.off_ckey);
   p.cand_pos = reinterpret_cast<int32_t*>(ws + pl.off_cpos);
+  p.q_mx = reinterpret_cast<uint16_t*>(ws + pl.off_qmx);
   p.tl = timeline_buffer();
   const hipError_t e = launch_indexer(p, indexer_fast(q_dtype, k_dtype, n_heads, head_dim, layout),
                                       static_cast<hipStream_t>(stream));

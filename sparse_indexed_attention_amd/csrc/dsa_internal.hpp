@@ -117,7 +117,7 @@ struct IndexerPlan {
   int32_t cap;          // candidates per split at most = min(split, top_k)
   int32_t rs;           // candidate slots per split: cap rounded up to 4
   int32_t compact;      // 1: the grid numbers only live splits (IndexerParams::compact)
-  size_t off_counters, off_hdr, off_ckey, off_cpos, bytes;
+  size_t off_counters, off_hdr, off_ckey, off_cpos, off_qmx, bytes;
 };
 
 struct IndexerParams {
@@ -138,6 +138,8 @@ struct IndexerParams {
   uint32_t* hdr;        // [T][nsplit_max][8]   emitted count, threshold key, key range
   uint32_t* cand_key;   // [T][nsplit_max][rs] one run of candidates per split: keys
   int32_t* cand_pos;    // [T][nsplit_max][rs] ... and positions
+  uint16_t* q_mx;       // [T][64][128] MXFP8 keys: the queries quantized once per call (their
+                        // dequantized values, exact in bf16), written before the main kernel
   uint64_t* tl;         // phase stamps (measurement build only), else nullptr
 };
 

@@ -257,55 +257,24 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
   const int per = (ngroups + NWAVE - 1) / NWAVE;
   const int g0 = min(ngroups, wave * per), g1 = min(ngroups, g0 + per);
   constexpr bool MX = MODE == 3;
-  const uint16_t* qb = (const uint16_t*)p.q + (size_t)t * (64 * 128);
-  if constexpr (MX) {
-    // MXFP8: the workgroup quantizes the query, thread i the group of 32 dims 32 (i % 4) ..
-    // of head i / 4, and leaves the dequantized values (exact in bf16: an e4m3 value times a
-    // power of two) in the ring's LDS, where every wave reads its operands.  All waves pass
-    // the same barriers: before the writes (the region may still be read by the previous
-    // phase) and after every wave has its copy (before any ring load or early return).
-    static_assert(NT == 64 * 4, "one thread per group of the query");
-    __syncthreads();
-    uint16_t* qs = (uint16_t*)L.region + (threadIdx.x >> 2) * 128 + 32 * (threadIdx.x & 3);
-    const uint16_t* src = qb + (threadIdx.x >> 2) * 128 + 32 * (threadIdx.x & 3);
-    bf16x8 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *(const bf16x8*)(src + 8 * u);
-    float amax = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[u][e]));
-    const uint32_t sbyte = mx_scale_byte(amax);
-    const float inv = mx_inv_scale(sbyte), sc = mx_scale_f32(sbyte);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      bf16x8 r;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        r[e] = (__bf16)(fp8_e4m3_to_f32(f32_to_fp8_e4m3_nb((float)v[u][e] * inv)) * sc);
-      *(bf16x8*)(qs + 8 * u) = r;
-    }
-    __syncthreads();
-  }
+  // MXFP8 keys: the query was quantized once for the call (mx_query_kernel) and is read like
+  // a bf16 query from its dequantized values
+  const uint16_t* qb = (MX ? (const uint16_t*)p.q_mx : (const uint16_t*)p.q) + (size_t)t * (64 * 128);
   static_assert(kSplitMax / 32 / NWAVE <= 64, "one lane per group of a wave's run");
-  // The query's 64 x 128 bf16 values (16 KB): with MXFP8 keys the workgroup has just left
-  // their dequantized values at the region's start; otherwise they land once per workgroup
-  // in the ring's last slots (slot D - 1 of every wave, at least 16 KB, first filled by the
-  // loop's first step), with the 16-byte chunk c of head row r at chunk c ^ (r & 15), so
-  // that the fragment reads below (32 heads at one chunk) fall in distinct banks.  Four
-  // waves loading their fragments straight from global memory would fetch each query four
-  // times per workgroup, about 32 MB across a decode launch at its start.
+  // The query's 64 x 128 bf16 values (16 KB) land once per workgroup in the ring's last slots
+  // (slot D - 1 of every wave, at least 16 KB, first filled by the loop's first step), with
+  // the 16-byte chunk c of head row r at chunk c ^ (r & 15), so that the fragment reads below
+  // (32 heads at one chunk) fall in distinct banks.  Four waves loading their fragments
+  // straight from global memory would fetch each query four times per workgroup, about 32 MB
+  // across a decode launch at its start.
   static_assert(NWAVE * SLOT >= 64 * 128 * 2, "the query fits in the ring's last slots");
   uint8_t* const qland = L.region + (D - 1) * (NWAVE * SLOT);
-  if constexpr (!MX) {
 #pragma unroll
-    for (int u = 0; u < 16 / NWAVE; ++u) {
-      const int P = 64 * (wave + NWAVE * u) + lane;    // landing chunk: row P / 16, slot P % 16
-      const int r = P >> 4;
-      load_to_lds<16>(qb, (uint32_t)(r * 256 + 16 * ((P & 15) ^ (r & 15))),
-                      lds_addr(qland + 1024 * (wave + NWAVE * u)));
-    }
+  for (int u = 0; u < 16 / NWAVE; ++u) {
+    const int P = 64 * (wave + NWAVE * u) + lane;    // landing chunk: row P / 16, slot P % 16
+    const int r = P >> 4;
+    load_to_lds<16>(qb, (uint32_t)(r * 256 + 16 * ((P & 15) ^ (r & 15))),
+                    lds_addr(qland + 1024 * (wave + NWAVE * u)));
   }
   // One round trip brings the query, this wave's copy of the head weights (LDS) and the
   // pages of its groups (lane l: the block id of group g0 + l).
@@ -317,21 +286,12 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
   wait_vmcnt<0>();
   __syncthreads();                            // every wave's share of the query has landed
   bf16x8 a0[8], a1[8];
-  if constexpr (MX) {
-    const uint16_t* qsrc = (const uint16_t*)L.region;
+  // head col and 32 + col share the swizzle (32 is a multiple of 16)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      a0[s] = *(const bf16x8*)(qsrc + col * 128 + half * 64 + 8 * s);
-      a1[s] = *(const bf16x8*)(qsrc + (32 + col) * 128 + half * 64 + 8 * s);
-    }
-  } else {
-    // head col and 32 + col share the swizzle (32 is a multiple of 16)
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int ch = (8 * half + s) ^ (col & 15);
-      a0[s] = *(const bf16x8*)(qland + col * 256 + 16 * ch);
-      a1[s] = *(const bf16x8*)(qland + (32 + col) * 256 + 16 * ch);
-    }
+  for (int s = 0; s < 8; ++s) {
+    const int ch = (8 * half + s) ^ (col & 15);
+    a0[s] = *(const bf16x8*)(qland + col * 256 + 16 * ch);
+    a1[s] = *(const bf16x8*)(qland + (32 + col) * 256 + 16 * ch);
   }
   __syncthreads();                            // every wave holds its fragments: the ring may start
   if (g0 >= g1) return;
@@ -470,9 +430,8 @@ __device__ __forceinline__ void score_mfma(const IndexerParams& p, int t, int se
 // MFMA steps as score_mfma, into its own key array.  Waves without a query (nq < kMqQ) still
 // load and pass the barriers.  Group indices past the split are clamped onto its last group,
 // so that every step issues the same loads and the waits stay exact.  MXFP8 keys (MX) move
-// like fp8 keys with their rows' scale bytes, are widened with their group's power-of-two
-// scale, and the workgroup first quantizes all the tile's queries to MXFP8 into the free
-// region, from which each wave loads its own dequantized query.
+// like fp8 keys with their rows' scale bytes and are widened with their group's power-of-two
+// scale; the queries were quantized to MXFP8 once for the call (mx_query_kernel).
 template <bool FP8, bool PAGED, bool MX = false>
 __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)[kMqQ], int nq,
                                          int seq, int start, int lenmax, const int (&lens)[kMqQ],
@@ -493,7 +452,6 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
   static_assert(kMqRingOff + D * SLOT <= region_bytes<1>() &&
                 kMqRingOff + D * SLOT <= region_bytes<2>() &&
                 kMqRingOff + D * SLOT <= region_bytes<3>(), "ring size");
-  static_assert(kMqQ * 64 * 128 * 2 <= region_bytes<3>(), "the tile's MXFP8 queries fit the region");
   static_assert(kMqKeysOff + (kMqQ - 1) * kSplitMax * 4 <= kMqRingOff, "scores below the ring");
   static_assert(kSplitMax / 32 <= 64, "one lane per group of the split");
   seq = __builtin_amdgcn_readfirstlane(seq);
@@ -505,46 +463,15 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
   const int len = __builtin_amdgcn_readfirstlane(act ? lens[wave] : 0);
   uint32_t* const kout = keys[act ? wave : 0];
 
-  const uint16_t* qb = (const uint16_t*)p.q + (size_t)t * (64 * 128);
-  if constexpr (MX) {
-    // query i's group g (head g / 4, dims 32 (g % 4) ..) is quantized by thread g of round i
-    // and stored dequantized (exact in bf16 for scale bytes >= 3) at region + 16 KB i
-    static_assert(NT == 64 * 4, "one thread per group of a query");
-    for (int i = 0; i < kMqQ; ++i) {
-      const int ti = i < nq ? tq[i] : tq[0];
-      const uint16_t* src = (const uint16_t*)p.q + (size_t)ti * (64 * 128) +
-                            (threadIdx.x >> 2) * 128 + 32 * (threadIdx.x & 3);
-      uint16_t* dst = (uint16_t*)(L.region + 16384 * i) + (threadIdx.x >> 2) * 128 +
-                      32 * (threadIdx.x & 3);
-      bf16x8 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *(const bf16x8*)(src + 8 * u);
-      float amax = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[u][e]));
-      const uint32_t sbyte = mx_scale_byte(amax);
-      const float inv = mx_inv_scale(sbyte), sc = mx_scale_f32(sbyte);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        bf16x8 r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          r[e] = (__bf16)(fp8_e4m3_to_f32(f32_to_fp8_e4m3_nb((float)v[u][e] * inv)) * sc);
-        *(bf16x8*)(dst + 8 * u) = r;
-      }
-    }
-    __syncthreads();
-  }
-  const uint16_t* qsrc = MX ? (const uint16_t*)(L.region + 16384 * (act ? wave : 0)) : qb;
+  // MXFP8 keys: the queries were quantized once for the call (mx_query_kernel) and are read
+  // like bf16 queries from their dequantized values
+  const uint16_t* qsrc = (MX ? (const uint16_t*)p.q_mx : (const uint16_t*)p.q) + (size_t)t * (64 * 128);
   bf16x8 a0[8], a1[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     a0[s] = *(const bf16x8*)(qsrc + col * 128 + half * 64 + 8 * s);
     a1[s] = *(const bf16x8*)(qsrc + (32 + col) * 128 + half * 64 + 8 * s);
   }
-  if constexpr (MX) __syncthreads();          // every wave holds its query; the ring may start
   const float* lw = L.w + wave * 64;
   load_to_lds<4>(p.w + (size_t)t * 64, 4u * lane, lds_addr(lw));
   int gblk = 0;
@@ -2171,6 +2098,31 @@ __device__ __forceinline__ void run_tile(const IndexerParams& p, int b, int j, c
 
 // The reference path (MODE 0) keeps its fp32 query in LDS and fits one workgroup per CU; the
 // MFMA paths fit two.
+// MXFP8 keys (MFMA path): the queries are quantized the same way, per head and group of 32
+// dims, once per call, and their dequantized values (an e4m3 value times a power of two, exact
+// in bf16 for scale bytes >= 3) go to p.q_mx, from which the scorers read them like a bf16
+// query.  Four workgroups per query, each a quarter (16 heads x 128 dims): thread i takes dims
+// 8 (i % 16) .. + 7 of head 16 b + i / 16 of quarter b, so a group of 32 dims is four
+// consecutive lanes, which share its largest magnitude by lane exchange.
+__global__ __launch_bounds__(NT) void mx_query_kernel(IndexerParams p) {
+  static_assert(NT == 256, "a quarter of a query (16 heads x 128 dims) per workgroup");
+  const int t = blockIdx.x >> 2;
+  const size_t off = (size_t)t * (64 * 128) + (size_t)(blockIdx.x & 3) * (16 * 128) + 8 * threadIdx.x;
+  const bf16x8 v = *(const bf16x8*)((const uint16_t*)p.q + off);
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+  // the group's 32 values are lanes 4k .. 4k + 3 of the wave
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const uint32_t sbyte = mx_scale_byte(amax);
+  const float inv = mx_inv_scale(sbyte), sc = mx_scale_f32(sbyte);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)(fp8_e4m3_to_f32(f32_to_fp8_e4m3_nb((float)v[e] * inv)) * sc);
+  *(bf16x8*)(p.q_mx + off) = r;
+}
+
 template <int MODE, int QT = 1>
 __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(IndexerParams p) {
   constexpr int RB = region_bytes<MODE>();
@@ -2304,6 +2256,8 @@ IndexerPlan plan_indexer_split(int32_t T, int32_t max_visible, int32_t top_k, in
   pl.off_hdr = off;      off = al(off + (size_t)T * pl.nsplit_max * 32);
   pl.off_ckey = off;     off = al(off + slots * 4);
   pl.off_cpos = off;     off = al(off + slots * 4);
+  // MXFP8 keys on the MFMA path: every query quantized once per call (64 x 128 bf16 values)
+  pl.off_qmx = off;      off = al(off + (size_t)T * 64 * 128 * 2);
   pl.bytes = off;
   return pl;
 }
@@ -2356,6 +2310,12 @@ hipError_t launch_indexer(const IndexerParams& p, bool fast_path, hipStream_t st
   const dim3 grid(p.grid);
   const bool mq = fast_path && indexer_multi_query(p);
   const dim3 gmq(p.nsplit_max * ((p.T + kMqQ - 1) / kMqQ));
+  if (fast_path && p.k_dtype == kDtMX) {
+    // the queries' MXFP8 quantization, once per call, ahead of the scoring
+    hipLaunchKernelGGL(mx_query_kernel, dim3(4 * p.T), dim3(NT), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (!fast_path) launch_instance<0, 1>(grid, stream, p);
   else if (p.k_dtype == kDtFP8) mq ? launch_instance<2, kMqQ>(gmq, stream, p) : launch_instance<2, 1>(grid, stream, p);
   else if (p.k_dtype == kDtMX) mq ? launch_instance<3, kMqQ>(gmq, stream, p) : launch_instance<3, 1>(grid, stream, p);
