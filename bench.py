@@ -365,7 +365,11 @@ def record_timeline(args, dsa, torch, step, spec, V):
         i += 1
         torch.cuda.synchronize()
         a = buf.view(kernels, -1, slots).cpu().numpy()
-        t0 = int(a[0, :, 0][a[0, :, 0] > 0].min())
+        starts = a[:, :, 0][a[:, :, 0] > 0]
+        if starts.size == 0:
+            raise SystemExit("bench: no phase stamps recorded (is DSA_LIB_PATH the timeline build?)")
+        first_idx = a[0, :, 0][a[0, :, 0] > 0]
+        t0 = int(first_idx.min() if first_idx.size else starts.min())
         rec = {}
         for k, name in enumerate(("indexer", "attention", "combine")):
             wgs = {}

@@ -506,63 +506,133 @@ __device__ __forceinline__ void score_mq(const IndexerParams& p, const int (&tq)
     if constexpr (FP8) load_to_lds<4>(p.k_scale + row0, 4u * (uint32_t)min(col, last), lb + GB);
   };
   wait_vmcnt<0>();                            // query and head weights
-  for (int g = 0; g < D - 1; ++g) issue(g);
-#pragma unroll 1
-  for (int g = 0; g < ng; ++g) {
-    wait_vmcnt<LPW * (D - 2)>();              // this wave's loads of group g have landed
-    __syncthreads();                          // ... and every wave's; group g - 1 is consumed
-    issue(g + D - 1);                         // into group g - 1's slot
-    if (act) {
-      const uint8_t* sb = slot_of(g);
-      const uint8_t* rb = sb + col * ROWB;
-      // MXFP8: this lane's two groups 2 half, 2 half + 1 (k steps 0..3, 4..7)
-      const uint32_t sw = MX ? *(const uint32_t*)(sb + GB + 4 * col) >> (16 * half) : 0u;
-      const float xs0 = MX ? mx_scale_f32(sw & 255u) : 1.0f;
-      const float xs1 = MX ? mx_scale_f32((sw >> 8) & 255u) : 1.0f;
-      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  // The loop is software-pipelined: the MFMAs of group g + 1 are issued before the epilogue of
+  // group g (ReLU, head weights, head sum, key), so that the matrix cores work on the next
+  // group while the vector unit finishes this one (in order, a wave would otherwise idle
+  // behind each dependent MFMA chain and then run its epilogue with the matrix cores idle).
+  // The head weights stay in registers for the whole loop.  Only the split's own groups are
+  // loaded: the waits count the groups still in flight behind the one awaited.
+  static_assert(D == 4, "the waits below count up to two groups in flight");
+  f32x4 wv[2][4];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        bf16x8 kb;
-        if constexpr (FP8) {
-          const float xs = s < 4 ? xs0 : xs1;
-          const u32x4 v = *(const u32x4*)(rb + 16 * ((4 * half + (s >> 1)) ^ (col & (CPR - 1))));
-          const uint32_t lo = (s & 1) ? v.z : v.x;
-          const uint32_t hi = (s & 1) ? v.w : v.y;
-          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, xs, false);
-          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, xs, true);
-          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, xs, false);
-          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, xs, true);
-          kb = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        } else {
-          kb = *(const bf16x8*)(rb + 16 * ((8 * half + s) ^ (col & (CPR - 1))));
-        }
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], kb, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], kb, acc1, 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 w0 = *(const f32x4*)(lw + 8 * rg + 4 * half);
-        const f32x4 w1 = *(const f32x4*)(lw + 32 + 8 * rg + 4 * half);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          part[u] = fmaf(w0[u], relu(acc0[4 * rg + u]), part[u]);
-          part[u] = fmaf(w1[u], relu(acc1[4 * rg + u]), part[u]);
-        }
-      }
-      const float psum = (part[0] + part[1]) + (part[2] + part[3]);
-      float tot = psum + __shfl_xor(psum, 32, 64);
-      if constexpr (FP8 && !MX) tot *= *(const float*)(sb + GB + 4 * col);
-      const int off = g * 32 + col;
-      if (half == 0 && off < len) {
-        const uint32_t key = float_to_key(tot);
-        kout[off] = key;
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-      }
-    }
+  for (int rg = 0; rg < 4; ++rg) {
+    wv[0][rg] = *(const f32x4*)(lw + 8 * rg + 4 * half);
+    wv[1][rg] = *(const f32x4*)(lw + 32 + 8 * rg + 4 * half);
   }
+  auto wait_behind = [&](int n) {             // n of this wave's later groups may be in flight
+    if (n >= 2) wait_vmcnt<2 * LPW>();
+    else if (n == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+  };
+  // group g's MFMAs into (acc0, acc1), and its fp8 token scale (read now: the slot is refilled
+  // before the epilogue)
+  auto products = [&](int g, f32x16& acc0, f32x16& acc1, float& tscale) {
+    const uint8_t* sb = slot_of(g);
+    const uint8_t* rb = sb + col * ROWB;
+    // MXFP8: this lane's two groups 2 half, 2 half + 1 (k steps 0..3, 4..7)
+    const uint32_t sw = MX ? *(const uint32_t*)(sb + GB + 4 * col) >> (16 * half) : 0u;
+    const float xs0 = MX ? mx_scale_f32(sw & 255u) : 1.0f;
+    const float xs1 = MX ? mx_scale_f32((sw >> 8) & 255u) : 1.0f;
+    tscale = FP8 && !MX ? *(const float*)(sb + GB + 4 * col) : 1.f;
+    acc0 = f32x16{};
+    acc1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 kb;
+      if constexpr (FP8) {
+        const float xs = s < 4 ? xs0 : xs1;
+        const u32x4 v = *(const u32x4*)(rb + 16 * ((4 * half + (s >> 1)) ^ (col & (CPR - 1))));
+        const uint32_t lo = (s & 1) ? v.z : v.x;
+        const uint32_t hi = (s & 1) ? v.w : v.y;
+        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, xs, false);
+        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, xs, true);
+        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, xs, false);
+        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, xs, true);
+        kb = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      } else {
+        kb = *(const bf16x8*)(rb + 16 * ((8 * half + s) ^ (col & (CPR - 1))));
+      }
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], kb, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], kb, acc1, 0, 0, 0);
+    }
+  };
+  // the epilogue's arithmetic (no branch, so that it can interleave with the next group's
+  // MFMAs) ...
+  auto epi_value = [&](const f32x16& acc0, const f32x16& acc1, float tscale) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        part[u] = fmaf(wv[0][rg][u], relu(acc0[4 * rg + u]), part[u]);
+        part[u] = fmaf(wv[1][rg][u], relu(acc1[4 * rg + u]), part[u]);
+      }
+    const float psum = (part[0] + part[1]) + (part[2] + part[3]);
+    float tot = psum + __shfl_xor(psum, 32, 64);
+    if constexpr (FP8 && !MX) tot *= tscale;
+    return tot;
+  };
+  // ... and its key store
+  auto epi_store = [&](int g, float tot) {
+    const int off = g * 32 + col;
+    const uint32_t key = float_to_key(tot);
+    const bool in = half == 0 && off < len;
+    kmin = in ? min(kmin, key) : kmin;
+    kmax = in ? max(kmax, key) : kmax;
+    if (in) kout[off] = key;
+  };
+  // One step: group g + 1's operand reads and MFMAs (past the last group they read a stale
+  // slot; those results are never used) interleaved with group g's epilogue arithmetic: per
+  // k step one LDS read, two MFMAs and a share of the vector work.
+  auto step = [&](int g, f32x16& n0, f32x16& n1, float& nts, const f32x16& c0, const f32x16& c1,
+                  float cts) {
+    products(g + 1, n0, n1, nts);
+    const float tot = epi_value(c0, c1, cts);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    epi_store(g, tot);
+  };
+  for (int g = 0; g < D - 1 && g < ng; ++g) issue(g);
+  TlCycles tc;
+  f32x16 accA0, accA1, accB0, accB1;
+  float tsA = 1.f, tsB = 1.f;
+  wait_behind(min(D - 2, ng - 1));            // group 0
+  __syncthreads();
+  if (D - 1 < ng) issue(D - 1);
+  if (act) products(0, accA0, accA1, tsA);
+  // two steps per trip, so that the accumulator pairs alternate without copies
+#pragma unroll 1
+  for (int g = 0; g < ng; g += 2) {
+    // step g: group g's MFMAs are in (accA); issue group g + 1's into (accB), then finish g
+    tc.mark();
+    const bool next1 = g + 1 < ng;
+    if (next1) {
+      wait_behind(min(D - 2, ng - 2 - g));    // group g + 1
+      __syncthreads();                        // every wave's loads of g + 1 are in, g's slot is free
+      if (g + D < ng) issue(g + D);
+    }
+    tc.waited();
+    if (act) step(g, accB0, accB1, tsB, accA0, accA1, tsA);
+    tc.computed();
+    if (!next1) break;
+    // step g + 1: group g + 1's MFMAs are in (accB); issue group g + 2's into (accA)
+    tc.mark();
+    const bool next2 = g + 2 < ng;
+    if (next2) {
+      wait_behind(min(D - 2, ng - 3 - g));    // group g + 2
+      __syncthreads();
+      if (g + 1 + D < ng) issue(g + 1 + D);
+    }
+    tc.waited();
+    if (act) step(g + 1, accA0, accA1, tsA, accB0, accB1, tsB);
+    tc.computed();
+  }
+  tc.put(p.tl, kTlIndexer, ng);
   wait_vmcnt<0>();                            // no load may still target the ring afterwards
   kmin = wave_min(kmin);
   kmax = wave_max(kmax);
@@ -2152,6 +2222,8 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(Ind
   L.small_w = s_small_w;
   Lds Lm = L;
   Lm.hist = (int*)s_keys;
+  tl_stamp(p.tl, kTlIndexer, kTlStart);
+  tl_clock(p.tl, kTlIndexer, kTlClockStart);
   if constexpr (QT > 1) {
     // one item (tile of QT queries, split j) per workgroup, j-major with the tiles rotated
     // by j as the queries are below
@@ -2173,8 +2245,6 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 1 : 2) void indexer_topk_kernel(Ind
   // workgroups spread over all the CUs, and within a block of T workgroups the queries are
   // rotated by j so that each query's splits spread over the XCDs.
   __shared__ int s_pre[kCompactMaxT + 1];
-  tl_stamp(p.tl, kTlIndexer, kTlStart);
-  tl_clock(p.tl, kTlIndexer, kTlClockStart);
   int n_items = gridDim.x;
   if (p.compact) {
     if ((int)threadIdx.x < p.T) {
