@@ -146,9 +146,11 @@ def source_digest():
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
-        # phase-stamp statements compile to nothing outside the measurement build
+        # phase-stamp statements compile to nothing outside the measurement build, and its
+        # helpers (the DSA_TIMELINE branch) are not compiled at all
+        src = re.sub(r"#ifdef DSA_TIMELINE\b.*?#else\b", " ", src, flags=re.S)
         src = re.sub(r"\btl_(stamp|put|clock)\([^;]*\);", " ", src)
-        src = re.sub(r"\btc\.(mark|waited|computed|put)\([^;]*\);", " ", src)
+        src = re.sub(r"\btc\.(mark|waited|computed|issued|put)\([^;]*\);", " ", src)
         src = re.sub(r"\bTlCycles tc;", " ", src)
         h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
@@ -347,7 +349,7 @@ def record_timeline(args, dsa, torch, step, spec, V):
     back, the stamp buffer is cleared on the stream, and one more step is recorded.  Written to
     args.timeline as JSON: per recorded step and kernel, the stamps of every workgroup that
     started, in microseconds from that step's first indexer start (null: slot not reached);
-    the shader-clock counts and readings (slots 8-12), item words (slot 14) and merge flags (slot 15) are kept as
+    the shader-clock counts and readings (slots 8-12, 19), item words (slot 14) and merge flags (slot 15) are kept as
     integers."""
     words = dsa.timeline_bytes() // 8
     buf = torch.zeros(words, dtype=torch.int64, device="cuda")
@@ -375,9 +377,9 @@ def record_timeline(args, dsa, torch, step, spec, V):
             wgs = {}
             for wg in np.nonzero(a[k, :, 0])[0]:
                 row = a[k, wg]
-                # slots 8-12: shader-clock cycle counts and readings, 14-15: item word and
-                # merge flag, kept as integers; the others are stamps
-                wgs[int(wg)] = [int(row[s_]) if (8 <= s_ <= 12 or s_ in (14, 15)) else
+                # slots 8-12 and 19: shader-clock cycle counts and readings, 14-15: item
+                # word and merge flag, kept as integers; the others are stamps
+                wgs[int(wg)] = [int(row[s_]) if (8 <= s_ <= 12 or s_ in (14, 15, 19)) else
                                 None if row[s_] == 0 else round((int(row[s_]) - t0) * 0.01, 2)
                                 for s_ in range(slots)]
             rec[name] = wgs

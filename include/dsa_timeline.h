@@ -23,7 +23,8 @@
  * Attention slots: 0 start, 1 pool rows resolved, 2 first tile pair and query rows landed, 3 query
  * fragments in registers, 4 last tile done, 5 outputs or partials written; slot 14 holds
  * (query << 16 | head group << 8 | slice), slots 8-10 the tile loop's wait and compute cycles
- * and steps, 11 and 12 the shader clock at the start and after the last tile.  Combine slots:
+ * and steps, 11 and 12 the shader clock at the start and after the last tile, 19 (the 128-head
+ * kernel) the loop's cycles issuing later tiles' loads.  Combine slots:
  * 0 start, 5 written.
  *
  * A slot a workgroup never reaches keeps whatever the caller left there: clear the buffer

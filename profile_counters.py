@@ -315,9 +315,11 @@ def timeline_summary(data):
             print(f"| {name} | {per_step(lambda s: _pct(ds(s), 50)):.2f} | "
                   f"{per_step(lambda s: _pct(ds(s), 100)):.2f} |")
     print("\n### Main loops: wave 0's shader-clock cycles per step (s_memtime)\n")
-    print("| kernel | loop | steps | waiting for loads | computing (with barriers) | wait share |")
-    print("|---|---|---|---|---|---|")
-    for kern, loop in (("indexer", "key groups (scoring)"), ("attention", "tile pairs")):
+    print("| kernel | loop | steps | waiting for loads | computing (with barriers) | issuing loads "
+          "| wait share |")
+    print("|---|---|---|---|---|---|---|")
+    for kern, loop in (("indexer", "key groups (scoring)"),
+                       ("attention", "tile pairs (64-head decode kernel) or tiles")):
         def cyc(s, slot):
             return [v[slot] / v[10] for v in s[kern].values() if v[10]]
         if not any(cyc(s, 8) for s in steps):
@@ -325,7 +327,10 @@ def timeline_summary(data):
         w = per_step(lambda s: _pct(cyc(s, 8), 50))
         c = per_step(lambda s: _pct(cyc(s, 9), 50))
         n = per_step(lambda s: _pct([v[10] for v in s[kern].values() if v[10]], 50))
-        print(f"| {kern} | {loop} | {n:.0f} | {w:.0f} | {c:.0f} | {w / (w + c):.2f} |")
+        has_i = any(len(v) > 19 and v[19] for s in steps for v in s[kern].values())
+        i_ = per_step(lambda s: _pct([v[19] / v[10] for v in s[kern].values() if v[10]], 50)) if has_i else 0.0
+        print(f"| {kern} | {loop} | {n:.0f} | {w:.0f} | {c:.0f} | "
+              f"{f'{i_:.0f}' if has_i else '-'} | {w / (w + c + i_):.2f} |")
     # shader clock rate: s_memtime ticks over wall-clock µs between the two readings
     for kern, a, b in (("indexer", 0, 1), ("attention", 0, 4)):
         def mhz(s):
@@ -344,6 +349,7 @@ def timeline_summary(data):
         print("|---|---|---|")
         for name, a, b in (("start to rows resolved", 0, 1), ("rows resolved to first tiles landed", 1, 2),
                            ("query fragments to registers", 2, 3), ("tile loop", 3, 4),
+                           ("start to last tile done", 0, 4),
                            ("writing", 4, 5), ("whole workgroup", 0, 5)):
             ds = lambda s: [v[b] - v[a] for v in s["attention"].values()
                             if v[a] is not None and v[b] is not None]

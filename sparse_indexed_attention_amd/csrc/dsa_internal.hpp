@@ -48,6 +48,8 @@ enum { kTlWaitCycles = 8, kTlComputeCycles = 9, kTlSteps = 10 };
 // (indexer: split scored; attention: last tile done), for the clock rate; indexer: the wall
 // clock when the scoring loop starts
 enum { kTlClockStart = 11, kTlClockEnd = 12, kTlLoopStart = 13 };
+// attention (128-head kernel): wave 0's shader-clock cycles issuing the next tile's loads
+enum { kTlIssueCycles = 19 };
 uint64_t* timeline_buffer();   // the registered buffer (measurement build), else nullptr
 #ifdef DSA_TIMELINE
 __device__ __forceinline__ void tl_put(uint64_t* tl, int kernel, int slot, uint64_t v) {
@@ -61,21 +63,26 @@ __device__ __forceinline__ void tl_stamp(uint64_t* tl, int kernel, int slot) {
 __device__ __forceinline__ void tl_clock(uint64_t* tl, int kernel, int slot) {
   tl_put(tl, kernel, slot, __builtin_amdgcn_s_memtime());
 }
-// Shader-clock cycles (s_memtime) wave 0 spends waiting for a loop's loads and computing, over
-// the loop's steps: slots kTlWaitCycles, kTlComputeCycles and kTlSteps.
+// Shader-clock cycles (s_memtime) wave 0 spends waiting for a loop's loads, computing and
+// issuing loads, over the loop's steps: slots kTlWaitCycles, kTlComputeCycles, kTlIssueCycles
+// and kTlSteps.  Each of waited(), computed() and issued() counts the cycles since the last
+// mark or count.
 struct TlCycles {
-  uint64_t w = 0, c = 0, t = 0;
+  uint64_t w = 0, c = 0, s = 0, t = 0;
   __device__ __forceinline__ void mark() { t = __builtin_amdgcn_s_memtime(); }
-  __device__ __forceinline__ void waited() {
-    const uint64_t n = __builtin_amdgcn_s_memtime();
-    w += n - t;
+  __device__ __forceinline__ uint64_t lap() {
+    const uint64_t n = __builtin_amdgcn_s_memtime(), d = n - t;
     t = n;
+    return d;
   }
-  __device__ __forceinline__ void computed() { c += __builtin_amdgcn_s_memtime() - t; }
+  __device__ __forceinline__ void waited() { w += lap(); }
+  __device__ __forceinline__ void computed() { c += lap(); }
+  __device__ __forceinline__ void issued() { s += lap(); }
   __device__ __forceinline__ void put(uint64_t* tl, int kernel, int steps) {
     if (threadIdx.x < 64) {
       tl_put(tl, kernel, kTlWaitCycles, w);
       tl_put(tl, kernel, kTlComputeCycles, c);
+      if (s != 0) tl_put(tl, kernel, kTlIssueCycles, s);
       tl_put(tl, kernel, kTlSteps, (uint64_t)steps);
     }
   }
@@ -88,6 +95,7 @@ struct TlCycles {
   __device__ __forceinline__ void mark() {}
   __device__ __forceinline__ void waited() {}
   __device__ __forceinline__ void computed() {}
+  __device__ __forceinline__ void issued() {}
   __device__ __forceinline__ void put(uint64_t*, int, int) {}
 };
 #endif

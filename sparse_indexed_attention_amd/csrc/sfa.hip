@@ -369,6 +369,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
 
 #pragma unroll
   for (int n = 0; n < NW * NB; ++n) o[n] = f32x16{};
+  TlCycles tc;
   if constexpr (F8) {
     // fp8 rows: the contractions read the landed staging tile directly.  S^T: the A fragment
     // of row c and k step s < 32 is 8 codes (one 8-byte read) widened to bf16 with the row's
@@ -488,15 +489,19 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
     load_queries();
     int buf = 0;
     for (int tile = 0; tile < ntiles; ++tile) {
+      tc.mark();
       const int ahead = min(ntiles - 1 - tile, kStageBufs - 1);   // later tiles in flight
       if (ahead >= 3) wait_vmcnt<3 * LPW_MIN>();
       else if (ahead == 2) wait_vmcnt<2 * LPW_MIN>();
       else if (ahead == 1) wait_vmcnt<LPW_MIN>();
       else wait_vmcnt<0>();
       __syncthreads();                           // every wave's loads of `tile` have landed
+      tc.waited();
       attend8(tile, stage[buf]);
       __syncthreads();                           // the staging buffer and the P tile are free
+      tc.computed();
       if (tile + kStageBufs < ntiles) issue(tile + kStageBufs, buf);
+      tc.issued();
       buf = buf == kStageBufs - 1 ? 0 : buf + 1;
     }
   } else {
@@ -510,17 +515,24 @@ __global__ __launch_bounds__(NW * 64, 1) void sfa_mfma_kernel(SfaParams p) {
   load_queries();
   int buf = 0;
   for (int tile = 0; tile < ntiles; ++tile) {
+    tc.mark();
     const int ahead = min(ntiles - 1 - tile, kTileBufs - 1);   // later tiles in flight
     if (ahead >= 2) wait_vmcnt<(2 * LPW_MIN < 63 ? 2 * LPW_MIN : 63)>();   // capped: waits longer
     else if (ahead == 1) wait_vmcnt<LPW_MIN>();
     else wait_vmcnt<0>();                        // this wave's loads of `tile` have landed
     __syncthreads();                             // ... and every other wave's
+    tc.waited();
     attend(tile, tiles[buf]);
     __syncthreads();                             // the buffer and the P tile are free again
+    tc.computed();
     if (tile + kTileBufs < ntiles) issue(tile + kTileBufs, buf);
+    tc.issued();
     buf = buf == kTileBufs - 1 ? 0 : buf + 1;
   }
   }
+  tl_stamp(p.tl, kTlSfa, kTlLoopDone);
+  tl_clock(p.tl, kTlSfa, kTlClockEnd);
+  tc.put(p.tl, kTlSfa, ntiles);
 
   // per-head totals: the two lane halves of a column hold disjoint rows of its head
   const float lt = xhalf_sum(l);

@@ -58,13 +58,14 @@ def test_timeline_build_exports_and_validates(tl_lib):
 def test_summary_of_a_known_record(capsys):
     import profile_counters as pc
     # two indexer workgroups of one query (the second merges), one attention and one combine
-    # workgroup; slots 8-12 are cycle counts and clock readings, 13 the scoring loop's start
+    # workgroup; slots 8-12 (and 19) are cycle counts and clock readings, 13 the scoring loop's start
     def idx(scored, merged, last):
         v = [0.0, scored, scored + 1, scored + 2] + ([scored + 3, scored + 4, scored + 5, scored + 6]
                                                      if merged else [None] * 4)
         v += [100, 400, 5, 0, int(2000 * scored), 1.0, 0, 1 if last else 0]
         return v
-    att = [30.0, 31.0, 35.0, 35.5, 39.0, 40.0, None, None, 50, 950, 2, 60000, 60000 + 2000 * 9, None, 0, 0]
+    att = [30.0, 31.0, 35.0, 35.5, 39.0, 40.0, None, None, 50, 950, 2, 60000, 60000 + 2000 * 9, None, 0, 0,
+           None, None, None, 300]
     comb = [42.0, None, None, None, None, 47.0] + [None] * 2 + [0, 0, 0, 0, 0, None, 0, 0]
     rec = {"indexer": {"0": idx(10.0, False, False), "1": idx(12.0, True, True)},
            "attention": {"0": att}, "combine": {"0": comb}}
@@ -74,5 +75,7 @@ def test_summary_of_a_known_record(capsys):
     assert "| indexer | merge: output written | 1 | 18.00 | 18.00 | 18.00 |" in out
     assert "| whole merge | 4.00 | 4.00 |" in out
     assert "| combine | written | 1 | 47.00 |" in out
-    assert "| indexer | key groups (scoring) | 5 | 20 | 80 | 0.20 |" in out
+    assert "| indexer | key groups (scoring) | 5 | 20 | 80 | - | 0.20 |" in out
+    # attention: 25 cycles waiting, 475 computing and 150 issuing per step (slot 19)
+    assert "| attention | tile pairs (64-head decode kernel) or tiles | 2 | 25 | 475 | 150 | 0.04 |" in out
     assert "attention: shader clock 2000 MHz" in out
